@@ -1,1 +1,8 @@
-"""head_chunked_context_amd: head-chunked, KV-trunked causal GQA attention for MI355X."""
+"""head_chunked_context_amd: head-chunked, KV-trunked causal GQA attention for MI355X.
+
+``attn_fwd`` / ``attn_bwd`` call the C ABI of ``libhcattn.so`` (built in-tree by
+``python -m head_chunked_context_amd.build``); the library is loaded on first
+use, so importing this package does not need a GPU.
+"""
+from .hcattn import (HcAttnError, attn_bwd, attn_fwd, bwd_workspace_bytes,  # noqa: F401
+                     fwd_workspace_bytes, last_error, set_single_stream, version)

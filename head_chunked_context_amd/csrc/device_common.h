@@ -1,0 +1,117 @@
+// device_common.h - gfx950 building blocks shared by the attention kernels.
+//
+// MFMA v_mfma_f32_32x32x16_bf16 (one wave64):
+//   A operand, lane l: A[m = l % 32][k = (l / 32) * 8 + 0..7]  (8 bf16)
+//   B operand, lane l: B[k = (l / 32) * 8 + 0..7][n = l % 32]  (8 bf16)
+//   C/D, lane l, register r: C[m = (r / 4) * 8 + (l / 32) * 4 + r % 4][n = l % 32]
+// ds_read_b64_tr_b16, within each group of 16 lanes: lane j points at 4
+// consecutive bf16 X[j][0..3]; lane i receives X[4t + i / 4][i % 4], t = 0..3.
+// Pointing lane j at tile[row0 + j / 4][col0 + 4 * (j % 4)] therefore gives
+// lane i the column tile[row0 + 0..3][col0 + i]: a transposed operand read
+// straight from a row-major tile.
+//
+// LDS tiles are row-major [rows][HD] bf16 with the 16-byte chunks of each row
+// XOR-swizzled by swz(row) = 2 * (row % 4) + (row / 4) % 2, which keeps both
+// access patterns free of bank conflicts: 16-byte reads of one chunk column
+// from 8 consecutive rows hit 8 different chunk slots, and the transposed
+// reads (4 rows x 32 bytes per 16 lanes) hit 8 different chunk slots too.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hc {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.693147180559945309f;
+
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// byte offset of element (row, col) in a swizzled [rows][HD] bf16 LDS tile
+template <int HD>
+__device__ __forceinline__ int lds_off(int row, int col) {
+    return row * (HD * 2) + ((((col >> 3) ^ swz(row))) << 4) + ((col & 7) << 1);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const char* base, int off) {
+    return *reinterpret_cast<const bf16x8*>(base + off);
+}
+
+__device__ __forceinline__ s16x4 lds_read_tr(const char* p) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+// Transposed A/B operand for 16 reduction indices k0 + {c*4 + 0..3, 8 + c*4 +
+// 0..3} (c = lane / 32) of the 32 columns col0..col0+31 of a row-major tile
+// (reduction index = tile row).  Lane l receives column col0 + l % 32.
+template <int HD>
+__device__ __forceinline__ bf16x8 lds_read_tr_operand(const char* tile, int k0, int col0, int lane) {
+    const int j = lane & 15;
+    const int row = k0 + ((lane >> 5) << 2) + (j >> 2);
+    const int col = col0 + (((lane >> 4) & 1) << 4) + ((j & 3) << 2);
+    s16x4 a = lds_read_tr(tile + lds_off<HD>(row, col));
+    s16x4 b = lds_read_tr(tile + lds_off<HD>(row + 8, col));
+    s16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, ab);
+}
+
+// max / sum of x over lanes l and l ^ 32; the same bits land in both lanes
+// (the sum always adds the lower lane's value first).
+__device__ __forceinline__ float pair_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x2 to_bf16x2(float a, float b) {
+    f32x2 f = {a, b};
+    return __builtin_convertvector(f, bf16x2);
+}
+
+// 64-row x HD-column bf16 tile: global -> registers -> swizzled LDS, 256 threads.
+template <int HD>
+struct Tile64 {
+    static constexpr int CPR = HD / 8;       // 16-byte chunks per row
+    static constexpr int RPI = 256 / CPR;    // rows per pass
+    static constexpr int NI = 64 / RPI;      // passes
+    uint4 r[NI];
+
+    // rows at or beyond nvalid read as zero
+    __device__ __forceinline__ void load(const uint16_t* base, int64_t rs, int64_t nvalid, int tid) {
+        const int c = tid % CPR, r0 = tid / CPR;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int row = r0 + i * RPI;
+            if (row < nvalid)
+                r[i] = *reinterpret_cast<const uint4*>(base + (int64_t)row * rs + c * 8);
+            else
+                r[i] = make_uint4(0, 0, 0, 0);
+        }
+    }
+    __device__ __forceinline__ void store(char* lds, int tid) const {
+        const int c = tid % CPR, r0 = tid / CPR;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            *reinterpret_cast<uint4*>(lds + lds_off<HD>(r0 + i * RPI, c * 8)) = r[i];
+    }
+};
+
+}  // namespace hc

@@ -1,0 +1,570 @@
+// hcattn.cpp - the C ABI (include/hcattn.h) and the host pipeline behind it.
+//
+// Forward, per head chunk (Road to 5 Million Tokens talk, U-Pipe paragraph:
+// one group of heads at a time, partial result stored, buffers reused):
+//   untrunked: pack the chunk's Q, K, V head-major -> flash kernel -> bf16 O, LSE
+//   trunked  : for query trunk m: pack Q_m; for key trunk t = 0..m (causal) the
+//              copy stream fills ring slot t%2 with K_t, V_t (pinned host or
+//              device) while the previous trunk computes; flash kernel gives
+//              the trunk partial; log-sum-exp merge into the running output
+//              (FPDT summary, "Technical Deep Dive": trunking, host offload,
+//              double buffer, separate compute and offload streams).
+// Backward, per head chunk: pack Q, dO (+ Delta), then per key range (the
+// whole sequence, or key trunk t with the same ring) the dK/dV kernel and the
+// dQ kernel; dQ is carried in fp32 across trunks, dK/dV in fp32 across chunks
+// when a GQA group spans chunks.  Finished dK/dV of host-resident k/v leave
+// through a staging slot and a device-to-host copy on the copy stream.
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/hcattn.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace {
+
+thread_local char g_err[512];
+std::atomic<int> g_single_stream{0};
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+#define HIPCHK(expr)                                                                   \
+    do {                                                                               \
+        hipError_t e_ = (expr);                                                        \
+        if (e_ != hipSuccess) {                                                        \
+            return fail(ATTN_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));     \
+        }                                                                              \
+    } while (0)
+
+// Events used by one call, per device.
+enum Ev {
+    EV_ENTRY,
+    EV_LOADED0, EV_LOADED1,     // ring slot filled (copy stream)
+    EV_FREE0, EV_FREE1,         // ring slot no longer read (compute stream)
+    EV_STAGED0, EV_STAGED1,     // staging slot written (compute stream)
+    EV_SFREE0, EV_SFREE1,       // staging slot copied out (copy stream)
+    EV_EXIT,
+    EV_COUNT
+};
+
+struct Device {
+    std::mutex mu;
+    bool ready = false;
+    hipStream_t copy = nullptr;
+    hipEvent_t ev[EV_COUNT] = {};
+};
+constexpr int kMaxDevices = 64;
+Device g_dev[kMaxDevices];
+std::mutex g_init;
+
+int device_resources(Device** out) {
+    int dev = 0;
+    HIPCHK(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_EHIP, "device index %d out of range", dev);
+    Device& d = g_dev[dev];
+    std::lock_guard<std::mutex> lk(g_init);
+    if (!d.ready) {
+        // default priority on purpose: every stream here runs at one priority
+        HIPCHK(hipStreamCreateWithFlags(&d.copy, hipStreamNonBlocking));
+        for (int i = 0; i < EV_COUNT; ++i)
+            HIPCHK(hipEventCreateWithFlags(&d.ev[i], hipEventDisableTiming));
+        d.ready = true;
+    }
+    *out = &d;
+    return ATTN_OK;
+}
+
+enum Loc { kLocDevice, kLocHost, kLocBad };
+
+Loc where(const void* ptr) {
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, ptr) != hipSuccess) {
+        (void)hipGetLastError();
+        return kLocBad;
+    }
+    if (a.type == hipMemoryTypeDevice) return kLocDevice;
+    if (a.type == hipMemoryTypeHost) return kLocHost;
+    return kLocBad;
+}
+
+
+struct Common {
+    hc::Plan pl;
+    char* ws;
+    hipStream_t st;    // caller's stream = compute stream
+    hipStream_t cp;    // copy stream (== st in single-stream mode)
+    Device* dev;
+    float scale, scale_log2;
+};
+
+int plan_or_fail(bool bwd, int64_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t causal,
+                 int32_t head_chunk, int64_t kv_trunk, hc::Plan* pl) {
+    char msg[256];
+    const int r = hc::make_plan(bwd, S, Hq, Hkv, D, causal, head_chunk, kv_trunk, pl, msg, sizeof msg);
+    if (r == -1) return fail(ATTN_EINVAL, "%s", msg);
+    if (r == -2) return fail(ATTN_EUNSUPPORTED, "%s", msg);
+    return ATTN_OK;
+}
+
+int check_workspace(const hc::Plan& pl, void* ws, size_t bytes) {
+    if (ws == nullptr) return fail(ATTN_EWORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(ws) % hc::kAlign != 0)
+        return fail(ATTN_EWORKSPACE, "workspace must be %zu-byte aligned", hc::kAlign);
+    if (bytes < pl.total)
+        return fail(ATTN_EWORKSPACE, "workspace has %zu bytes, needs %zu", bytes, pl.total);
+    return ATTN_OK;
+}
+
+// Copy rows [r0, r0 + rows) of heads [kv0, kv0 + nkv) of a token-major
+// [S][H][D] bf16 tensor into a token-major [rows][nkv][D] slot (or back).
+int copy_rows_in(void* dst, const void* src, int64_t r0, int64_t rows, int H, int kv0, int nkv,
+                 int D, hipStream_t s) {
+    const size_t row_b = (size_t)nkv * D * 2, pitch = (size_t)H * D * 2;
+    const char* from = static_cast<const char*>(src) + ((size_t)r0 * H + kv0) * D * 2;
+    HIPCHK(hipMemcpy2DAsync(dst, row_b, from, pitch, row_b, (size_t)rows, hipMemcpyDefault, s));
+    return ATTN_OK;
+}
+int copy_rows_out(void* dst, const void* src, int64_t r0, int64_t rows, int H, int kv0, int nkv,
+                  int src_nkv, int D, hipStream_t s) {
+    const size_t row_b = (size_t)nkv * D * 2, pitch = (size_t)H * D * 2;
+    char* to = static_cast<char*>(dst) + ((size_t)r0 * H + kv0) * D * 2;
+    HIPCHK(hipMemcpy2DAsync(to, pitch, src, (size_t)src_nkv * D * 2, row_b, (size_t)rows,
+                            hipMemcpyDefault, s));
+    return ATTN_OK;
+}
+
+// Two-slot ring for key/value trunks: the copy stream fills slot n % 2 with
+// the n-th trunk of the call while the compute stream reads slot (n-1) % 2.
+struct Ring {
+    Common* c;
+    int uses[2] = {0, 0};
+    int n = 0;
+    // enqueue the copy of key trunk t (heads kv0..kv0+nkv) into the next slot
+    int fill(const void* k, const void* v, int64_t t, int kv0, int nkv, int* slot) {
+        const hc::Plan& p = c->pl;
+        const int s = n & 1;
+        Device* d = c->dev;
+        HIPCHK(hipStreamWaitEvent(c->cp, d->ev[uses[s] == 0 ? EV_ENTRY : EV_FREE0 + s], 0));
+        int r = copy_rows_in(c->ws + p.ring_k[s], k, p.trunk_begin(t), p.trunk_rows(t), p.Hkv, kv0,
+                             nkv, p.D, c->cp);
+        if (r) return r;
+        r = copy_rows_in(c->ws + p.ring_v[s], v, p.trunk_begin(t), p.trunk_rows(t), p.Hkv, kv0, nkv,
+                         p.D, c->cp);
+        if (r) return r;
+        HIPCHK(hipEventRecord(d->ev[EV_LOADED0 + s], c->cp));
+        HIPCHK(hipStreamWaitEvent(c->st, d->ev[EV_LOADED0 + s], 0));
+        ++uses[s];
+        ++n;
+        *slot = s;
+        return ATTN_OK;
+    }
+    // the compute stream is done reading slot s
+    int release(int s) {
+        HIPCHK(hipEventRecord(c->dev->ev[EV_FREE0 + s], c->st));
+        return ATTN_OK;
+    }
+};
+
+// Called with the device's mutex held: orders the copy stream after all work
+// the caller enqueued on st before this call.
+int enter(Common& c, hipStream_t st) {
+    c.st = st;
+    c.cp = g_single_stream.load() ? st : c.dev->copy;
+    HIPCHK(hipEventRecord(c.dev->ev[EV_ENTRY], st));
+    return ATTN_OK;
+}
+
+int leave(Common& c) {
+    HIPCHK(hipEventRecord(c.dev->ev[EV_EXIT], c.cp));
+    HIPCHK(hipStreamWaitEvent(c.st, c.dev->ev[EV_EXIT], 0));
+    return ATTN_OK;
+}
+
+#define KCHK(expr)                                                                         \
+    do {                                                                                   \
+        hipError_t e_ = (expr);                                                            \
+        if (e_ != hipSuccess) return fail(ATTN_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+// ------------------------------------------------------------------ forward
+
+int fwd_untrunked(Common& c, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                  float* lse) {
+    const hc::Plan& p = c.pl;
+    const int64_t S = p.S;
+    const int D = p.D;
+    uint16_t* Qc = reinterpret_cast<uint16_t*>(c.ws + p.q_c);
+    uint16_t* Kc = reinterpret_cast<uint16_t*>(c.ws + p.k_c);
+    uint16_t* Vc = reinterpret_cast<uint16_t*>(c.ws + p.v_c);
+    for (int ci = 0; ci < p.nchunks; ++ci) {
+        const hc::Chunk ch = p.chunk(ci);
+        hc::PackParams pk{q + (size_t)ch.h0 * D, (int64_t)p.Hq * D, D, Qc, D, S * D, ch.nh, S, D};
+        KCHK(hc::launch_pack(pk, c.st));
+        pk = {k + (size_t)ch.kv0 * D, (int64_t)p.Hkv * D, D, Kc, D, S * D, ch.nkv, S, D};
+        KCHK(hc::launch_pack(pk, c.st));
+        pk = {v + (size_t)ch.kv0 * D, (int64_t)p.Hkv * D, D, Vc, D, S * D, ch.nkv, S, D};
+        KCHK(hc::launch_pack(pk, c.st));
+        hc::FwdParams f{};
+        f.q = Qc; f.q_rs = D; f.q_hs = S * D;
+        f.k = Kc; f.k_rs = D; f.k_hs = S * D;
+        f.v = Vc; f.v_rs = D; f.v_hs = S * D;
+        f.o = o + (size_t)ch.h0 * D; f.o_rs = (int64_t)p.Hq * D; f.o_hs = D;
+        f.lse = lse + (size_t)ch.h0 * S; f.lse_hs = S;
+        f.nh = ch.nh; f.group = p.g; f.h0 = ch.h0; f.kv_base = ch.kv0;
+        f.nq = S; f.q_pos0 = 0; f.nk = S; f.k_pos0 = 0;
+        f.causal = p.causal; f.mode = hc::kFwdFinal; f.scale_log2 = c.scale_log2;
+        KCHK(hc::launch_fwd(f, D, c.st));
+    }
+    return ATTN_OK;
+}
+
+int fwd_trunked(Common& c, const uint16_t* q, const void* k, const void* v, uint16_t* o, float* lse) {
+    const hc::Plan& p = c.pl;
+    const int D = p.D;
+    const int64_t T = p.T;
+    uint16_t* Qm = reinterpret_cast<uint16_t*>(c.ws + p.q_c);
+    float* Orun = reinterpret_cast<float*>(c.ws + p.o_run);
+    float* Ot = reinterpret_cast<float*>(c.ws + p.o_t);
+    float* Lrun = reinterpret_cast<float*>(c.ws + p.l_run);
+    float* Lt = reinterpret_cast<float*>(c.ws + p.l_t);
+    Ring ring{&c};
+    for (int ci = 0; ci < p.nchunks; ++ci) {
+        const hc::Chunk ch = p.chunk(ci);
+        for (int64_t m = 0; m < p.N; ++m) {
+            const int64_t qr0 = p.trunk_begin(m), nq = p.trunk_rows(m);
+            hc::PackParams pk{q + ((size_t)qr0 * p.Hq + ch.h0) * D, (int64_t)p.Hq * D, D, Qm, D,
+                              T * D, ch.nh, nq, D};
+            KCHK(hc::launch_pack(pk, c.st));
+            const int64_t tlast = p.causal ? m : p.N - 1;
+            for (int64_t t = 0; t <= tlast; ++t) {
+                int slot = 0;
+                int r = ring.fill(k, v, t, ch.kv0, ch.nkv, &slot);
+                if (r) return r;
+                hc::FwdParams f{};
+                f.q = Qm; f.q_rs = D; f.q_hs = T * D;
+                f.k = reinterpret_cast<const uint16_t*>(c.ws + p.ring_k[slot]);
+                f.k_rs = (int64_t)ch.nkv * D; f.k_hs = D;
+                f.v = reinterpret_cast<const uint16_t*>(c.ws + p.ring_v[slot]);
+                f.v_rs = (int64_t)ch.nkv * D; f.v_hs = D;
+                f.nh = ch.nh; f.group = p.g; f.h0 = ch.h0; f.kv_base = ch.kv0;
+                f.nq = nq; f.q_pos0 = qr0; f.nk = p.trunk_rows(t); f.k_pos0 = p.trunk_begin(t);
+                f.causal = p.causal; f.scale_log2 = c.scale_log2;
+                if (tlast == 0) {
+                    f.mode = hc::kFwdFinal;
+                    f.o = o + ((size_t)qr0 * p.Hq + ch.h0) * D; f.o_rs = (int64_t)p.Hq * D; f.o_hs = D;
+                    f.lse = lse + (size_t)ch.h0 * p.S + qr0; f.lse_hs = p.S;
+                } else {
+                    f.mode = hc::kFwdPartial;
+                    f.o = t == 0 ? Orun : Ot; f.o_rs = D; f.o_hs = nq * D;
+                    f.lse = t == 0 ? Lrun : Lt; f.lse_hs = nq;
+                }
+                KCHK(hc::launch_fwd(f, D, c.st));
+                r = ring.release(slot);
+                if (r) return r;
+                if (t > 0) {
+                    hc::MergeParams mg{};
+                    mg.o_r = Orun; mg.l_r = Lrun; mg.o_t = Ot; mg.l_t = Lt;
+                    mg.nh = ch.nh; mg.rows = nq; mg.D = D;
+                    mg.final_out = t == tlast;
+                    mg.out = o + ((size_t)qr0 * p.Hq + ch.h0) * D; mg.out_rs = (int64_t)p.Hq * D;
+                    mg.out_hs = D;
+                    mg.lse_out = lse + (size_t)ch.h0 * p.S + qr0; mg.lse_hs = p.S;
+                    KCHK(hc::launch_merge(mg, c.st));
+                }
+            }
+        }
+    }
+    return ATTN_OK;
+}
+
+// ----------------------------------------------------------------- backward
+
+struct BwdIO {
+    const uint16_t *q, *o, *dout;
+    const void *k, *v;
+    const float* lse;
+    uint16_t* dq;
+    void *dk, *dv;
+    bool kv_host;
+};
+
+// dK/dV kernel parameters for chunk ch over keys [kr0, kr0 + nk) held in (kk, vv)
+hc::DkdvParams dkdv_params(const Common& c, const hc::Chunk& ch, int ci, const BwdIO& io,
+                           const uint16_t* kk, const uint16_t* vv, int64_t k_rs, int64_t k_hs,
+                           int64_t kr0, int64_t nk) {
+    const hc::Plan& p = c.pl;
+    const int D = p.D;
+    hc::DkdvParams d{};
+    d.q = reinterpret_cast<const uint16_t*>(c.ws + p.q_c); d.q_rs = D; d.q_hs = p.S * D;
+    d.dO = reinterpret_cast<const uint16_t*>(c.ws + p.do_c); d.do_rs = D; d.do_hs = p.S * D;
+    d.lse = io.lse; d.lse_hs = p.S;
+    d.delta = reinterpret_cast<const float*>(c.ws + p.delta_c); d.delta_hs = p.S;
+    d.k = kk; d.v = vv; d.k_rs = d.v_rs = k_rs; d.k_hs = d.v_hs = k_hs;
+    d.nh = ch.nh; d.group = p.g; d.h0 = ch.h0; d.kv_base = ch.kv0; d.nkv = ch.nkv;
+    d.nq = p.S; d.nk = nk; d.k_pos0 = kr0; d.causal = p.causal;
+    d.scale = c.scale; d.scale_log2 = c.scale_log2;
+    const int in_s = p.carry_in_slot(ci), out_s = p.carry_out_slot(ci);
+    d.carry_kv_in = -1;
+    d.carry_kv_out = -1;
+    if (in_s >= 0) {
+        d.acc_in_k = reinterpret_cast<const float*>(c.ws + p.carry_k[in_s]) + (size_t)kr0 * D;
+        d.acc_in_v = reinterpret_cast<const float*>(c.ws + p.carry_v[in_s]) + (size_t)kr0 * D;
+        d.ain_rs = D; d.ain_hs = 0;  // one kv head per slot
+        d.carry_kv_in = 0;
+    }
+    if (out_s >= 0) {
+        d.acc_out_k = reinterpret_cast<float*>(c.ws + p.carry_k[out_s]) + (size_t)kr0 * D;
+        d.acc_out_v = reinterpret_cast<float*>(c.ws + p.carry_v[out_s]) + (size_t)kr0 * D;
+        d.aout_rs = D; d.aout_hs = 0;
+        d.carry_kv_out = ch.nkv - 1;
+    }
+    return d;
+}
+
+int bwd_chunk_prep(Common& c, const hc::Chunk& ch, const BwdIO& io) {
+    const hc::Plan& p = c.pl;
+    const int D = p.D;
+    const int64_t S = p.S;
+    uint16_t* Qc = reinterpret_cast<uint16_t*>(c.ws + p.q_c);
+    hc::PackParams pk{io.q + (size_t)ch.h0 * D, (int64_t)p.Hq * D, D, Qc, D, S * D, ch.nh, S, D};
+    KCHK(hc::launch_pack(pk, c.st));
+    hc::PrepParams pr{};
+    pr.o = io.o + (size_t)ch.h0 * D; pr.o_rs = (int64_t)p.Hq * D; pr.o_hs = D;
+    pr.dO = io.dout + (size_t)ch.h0 * D; pr.do_rs = (int64_t)p.Hq * D; pr.do_hs = D;
+    pr.dO_c = reinterpret_cast<uint16_t*>(c.ws + p.do_c); pr.c_rs = D; pr.c_hs = S * D;
+    pr.delta = reinterpret_cast<float*>(c.ws + p.delta_c); pr.delta_hs = S;
+    pr.nh = ch.nh; pr.rows = S; pr.D = D;
+    KCHK(hc::launch_prep(pr, c.st));
+    return ATTN_OK;
+}
+
+hc::DqParams dq_params(const Common& c, const hc::Chunk& ch, const BwdIO& io, const uint16_t* kk,
+                       const uint16_t* vv, int64_t k_rs, int64_t k_hs, int64_t kr0, int64_t nk) {
+    const hc::Plan& p = c.pl;
+    const int D = p.D;
+    hc::DqParams d{};
+    d.q = reinterpret_cast<const uint16_t*>(c.ws + p.q_c); d.q_rs = D; d.q_hs = p.S * D;
+    d.dO = reinterpret_cast<const uint16_t*>(c.ws + p.do_c); d.do_rs = D; d.do_hs = p.S * D;
+    d.lse = io.lse; d.lse_hs = p.S;
+    d.delta = reinterpret_cast<const float*>(c.ws + p.delta_c); d.delta_hs = p.S;
+    d.k = kk; d.v = vv; d.k_rs = d.v_rs = k_rs; d.k_hs = d.v_hs = k_hs;
+    d.nh = ch.nh; d.group = p.g; d.h0 = ch.h0; d.kv_base = ch.kv0;
+    d.nq = p.S; d.nk = nk; d.k_pos0 = kr0; d.causal = p.causal;
+    d.scale = c.scale; d.scale_log2 = c.scale_log2;
+    d.dq = io.dq + (size_t)ch.h0 * D; d.dq_rs = (int64_t)p.Hq * D; d.dq_hs = D;
+    d.q_begin = 0;
+    d.final_before = p.S;
+    return d;
+}
+
+int bwd_untrunked(Common& c, const BwdIO& io) {
+    const hc::Plan& p = c.pl;
+    const int D = p.D;
+    const int64_t S = p.S;
+    uint16_t* Kc = reinterpret_cast<uint16_t*>(c.ws + p.k_c);
+    uint16_t* Vc = reinterpret_cast<uint16_t*>(c.ws + p.v_c);
+    for (int ci = 0; ci < p.nchunks; ++ci) {
+        const hc::Chunk ch = p.chunk(ci);
+        int r = bwd_chunk_prep(c, ch, io);
+        if (r) return r;
+        const uint16_t* k = static_cast<const uint16_t*>(io.k);
+        const uint16_t* v = static_cast<const uint16_t*>(io.v);
+        hc::PackParams pk{k + (size_t)ch.kv0 * D, (int64_t)p.Hkv * D, D, Kc, D, S * D, ch.nkv, S, D};
+        KCHK(hc::launch_pack(pk, c.st));
+        pk = {v + (size_t)ch.kv0 * D, (int64_t)p.Hkv * D, D, Vc, D, S * D, ch.nkv, S, D};
+        KCHK(hc::launch_pack(pk, c.st));
+        hc::DkdvParams dk = dkdv_params(c, ch, ci, io, Kc, Vc, D, S * D, 0, S);
+        dk.dk = static_cast<uint16_t*>(io.dk) + (size_t)ch.kv0 * D;
+        dk.dv = static_cast<uint16_t*>(io.dv) + (size_t)ch.kv0 * D;
+        dk.dk_rs = (int64_t)p.Hkv * D; dk.dk_hs = D;
+        KCHK(hc::launch_dkdv(dk, D, c.st));
+        hc::DqParams dq = dq_params(c, ch, io, Kc, Vc, D, S * D, 0, S);
+        KCHK(hc::launch_dq(dq, D, c.st));
+    }
+    return ATTN_OK;
+}
+
+int bwd_trunked(Common& c, const BwdIO& io) {
+    const hc::Plan& p = c.pl;
+    const int D = p.D;
+    const int64_t S = p.S;
+    float* dQacc = reinterpret_cast<float*>(c.ws + p.dq_acc);
+    Ring ring{&c};
+    int stage_uses[2] = {0, 0}, nstage = 0;
+    for (int ci = 0; ci < p.nchunks; ++ci) {
+        const hc::Chunk ch = p.chunk(ci);
+        int r = bwd_chunk_prep(c, ch, io);
+        if (r) return r;
+        const bool carry_out = p.carry_out_slot(ci) >= 0;
+        const int nfin = ch.nkv - (carry_out ? 1 : 0);  // kv heads finished in this chunk
+        for (int64_t t = 0; t < p.N; ++t) {
+            const int64_t kr0 = p.trunk_begin(t), nk = p.trunk_rows(t);
+            int slot = 0;
+            r = ring.fill(io.k, io.v, t, ch.kv0, ch.nkv, &slot);
+            if (r) return r;
+            const uint16_t* kk = reinterpret_cast<const uint16_t*>(c.ws + p.ring_k[slot]);
+            const uint16_t* vv = reinterpret_cast<const uint16_t*>(c.ws + p.ring_v[slot]);
+            hc::DkdvParams dk = dkdv_params(c, ch, ci, io, kk, vv, (int64_t)ch.nkv * D, D, kr0, nk);
+            int ss = -1;
+            if (io.kv_host) {
+                ss = nstage & 1;
+                Device* d = c.dev;
+                if (stage_uses[ss] > 0) HIPCHK(hipStreamWaitEvent(c.st, d->ev[EV_SFREE0 + ss], 0));
+                dk.dk = reinterpret_cast<uint16_t*>(c.ws + p.stage_k[ss]);
+                dk.dv = reinterpret_cast<uint16_t*>(c.ws + p.stage_v[ss]);
+                dk.dk_rs = (int64_t)ch.nkv * D; dk.dk_hs = D;
+            } else {
+                dk.dk = static_cast<uint16_t*>(io.dk) + ((size_t)kr0 * p.Hkv + ch.kv0) * D;
+                dk.dv = static_cast<uint16_t*>(io.dv) + ((size_t)kr0 * p.Hkv + ch.kv0) * D;
+                dk.dk_rs = (int64_t)p.Hkv * D; dk.dk_hs = D;
+            }
+            KCHK(hc::launch_dkdv(dk, D, c.st));
+            hc::DqParams dq = dq_params(c, ch, io, kk, vv, (int64_t)ch.nkv * D, D, kr0, nk);
+            dq.q_begin = p.causal ? kr0 : 0;
+            dq.acc_in = t == 0 ? nullptr : dQacc;
+            dq.ain_rs = D; dq.ain_hs = S * D;
+            dq.acc_out = dQacc; dq.aout_rs = D; dq.aout_hs = S * D;
+            dq.final_before = p.causal ? kr0 + nk : (t == p.N - 1 ? S : 0);
+            KCHK(hc::launch_dq(dq, D, c.st));
+            r = ring.release(slot);
+            if (r) return r;
+            if (io.kv_host && nfin > 0) {
+                Device* d = c.dev;
+                HIPCHK(hipEventRecord(d->ev[EV_STAGED0 + ss], c.st));
+                HIPCHK(hipStreamWaitEvent(c.cp, d->ev[EV_STAGED0 + ss], 0));
+                r = copy_rows_out(io.dk, c.ws + p.stage_k[ss], kr0, nk, p.Hkv, ch.kv0, nfin, ch.nkv,
+                                  D, c.cp);
+                if (r) return r;
+                r = copy_rows_out(io.dv, c.ws + p.stage_v[ss], kr0, nk, p.Hkv, ch.kv0, nfin, ch.nkv,
+                                  D, c.cp);
+                if (r) return r;
+                HIPCHK(hipEventRecord(d->ev[EV_SFREE0 + ss], c.cp));
+                ++stage_uses[ss];
+                ++nstage;
+            } else if (io.kv_host) {
+                ++nstage;
+            }
+        }
+    }
+    return ATTN_OK;
+}
+
+int check_ptr(const void* p, const char* name, bool host_ok, bool* is_host) {
+    if (p == nullptr) return fail(ATTN_EPOINTER, "%s is NULL", name);
+    const Loc l = where(p);
+    if (l == kLocDevice) {
+        if (is_host) *is_host = false;
+        return ATTN_OK;
+    }
+    if (l == kLocHost && host_ok) {
+        if (is_host) *is_host = true;
+        return ATTN_OK;
+    }
+    if (l == kLocHost)
+        return fail(ATTN_EPOINTER, "%s is host memory; only k/v/dk/dv of the trunked path may be", name);
+    return fail(ATTN_EPOINTER, "%s is neither device nor pinned host memory", name);
+}
+
+void init_common(Common& c, const hc::Plan& pl, void* ws) {
+    c.pl = pl;
+    c.ws = static_cast<char*>(ws);
+    c.scale = (float)(1.0 / std::sqrt((double)pl.D));
+    c.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pl.D));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_fwd_workspace_bytes(int64_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t causal,
+                                int32_t head_chunk, int64_t kv_trunk) {
+    hc::Plan pl;
+    if (plan_or_fail(false, S, Hq, Hkv, D, causal, head_chunk, kv_trunk, &pl)) return 0;
+    return pl.total;
+}
+
+size_t attn_bwd_workspace_bytes(int64_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t causal,
+                                int32_t head_chunk, int64_t kv_trunk) {
+    hc::Plan pl;
+    if (plan_or_fail(true, S, Hq, Hkv, D, causal, head_chunk, kv_trunk, &pl)) return 0;
+    return pl.total;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t S,
+             int32_t Hq, int32_t Hkv, int32_t D, int32_t causal, int32_t head_chunk,
+             int64_t kv_trunk, void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    hc::Plan pl;
+    int r = plan_or_fail(false, S, Hq, Hkv, D, causal, head_chunk, kv_trunk, &pl);
+    if (r) return r;
+    if ((r = check_workspace(pl, workspace, workspace_bytes))) return r;
+    bool kh = false, vh = false;
+    if ((r = check_ptr(q, "q", false, nullptr)) || (r = check_ptr(k, "k", pl.trunked, &kh)) ||
+        (r = check_ptr(v, "v", pl.trunked, &vh)) || (r = check_ptr(o, "o", false, nullptr)) ||
+        (r = check_ptr(lse, "lse", false, nullptr)) ||
+        (r = check_ptr(workspace, "workspace", false, nullptr)))
+        return r;
+    Common c;
+    init_common(c, pl, workspace);
+    if ((r = device_resources(&c.dev))) return r;
+    std::lock_guard<std::mutex> lk(c.dev->mu);
+    if ((r = enter(c, static_cast<hipStream_t>(stream)))) return r;
+    if (!pl.trunked)
+        r = fwd_untrunked(c, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                          static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse);
+    else
+        r = fwd_trunked(c, static_cast<const uint16_t*>(q), k, v, static_cast<uint16_t*>(o), lse);
+    const int r2 = leave(c);
+    return r ? r : r2;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int64_t S, int32_t Hq, int32_t Hkv,
+             int32_t D, int32_t causal, int32_t head_chunk, int64_t kv_trunk, void* workspace,
+             size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    hc::Plan pl;
+    int r = plan_or_fail(true, S, Hq, Hkv, D, causal, head_chunk, kv_trunk, &pl);
+    if (r) return r;
+    if ((r = check_workspace(pl, workspace, workspace_bytes))) return r;
+    bool kh = false, vh = false, dkh = false, dvh = false;
+    if ((r = check_ptr(q, "q", false, nullptr)) || (r = check_ptr(k, "k", pl.trunked, &kh)) ||
+        (r = check_ptr(v, "v", pl.trunked, &vh)) || (r = check_ptr(o, "o", false, nullptr)) ||
+        (r = check_ptr(dout, "dout", false, nullptr)) ||
+        (r = check_ptr(lse, "lse", false, nullptr)) || (r = check_ptr(dq, "dq", false, nullptr)) ||
+        (r = check_ptr(dk, "dk", pl.trunked, &dkh)) || (r = check_ptr(dv, "dv", pl.trunked, &dvh)) ||
+        (r = check_ptr(workspace, "workspace", false, nullptr)))
+        return r;
+    if (dkh != dvh)
+        return fail(ATTN_EPOINTER, "dk and dv must both be device or both be pinned host memory");
+    Common c;
+    init_common(c, pl, workspace);
+    if ((r = device_resources(&c.dev))) return r;
+    std::lock_guard<std::mutex> lk(c.dev->mu);
+    if ((r = enter(c, static_cast<hipStream_t>(stream)))) return r;
+    BwdIO io{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(o),
+             static_cast<const uint16_t*>(dout), k, v, lse, static_cast<uint16_t*>(dq), dk, dv, dkh};
+    r = pl.trunked ? bwd_trunked(c, io) : bwd_untrunked(c, io);
+    const int r2 = leave(c);
+    return r ? r : r2;
+}
+
+const char* attn_last_error(void) { return g_err; }
+
+int attn_set_single_stream(int on) { return g_single_stream.exchange(on ? 1 : 0); }
+
+const char* attn_version(void) { return "0.1.0"; }
+
+}  // extern "C"

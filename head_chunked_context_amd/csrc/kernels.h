@@ -1,0 +1,131 @@
+// kernels.h - launch parameters and host-side launchers of the gfx950 kernels.
+//
+// Every tensor is addressed as base + head * head_stride + row * row_stride +
+// column, in elements, so one kernel reads the token-major user layout
+// ([S][H][D]: row_stride = H*D, head_stride = D), the head-major chunk
+// buffers ([H][S][D]: row_stride = D, head_stride = S*D) and trunk ring slots
+// alike.  bf16 values travel as uint16_t bit patterns on the host side.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace hc {
+
+// Forward flash kernel output modes.
+enum FwdMode : int {
+    kFwdFinal = 0,    // bf16 O (strided) + natural-log LSE, normalised
+    kFwdPartial = 1,  // fp32 O normalised over this key range + LSE (-inf if empty)
+};
+
+struct FwdParams {
+    const uint16_t* q;  int64_t q_rs, q_hs;   // nh query heads, nq rows
+    const uint16_t* k;  int64_t k_rs, k_hs;   // key heads, nk rows
+    const uint16_t* v;  int64_t v_rs, v_hs;
+    void* o;            int64_t o_rs, o_hs;   // bf16 (final) or fp32 (partial)
+    float* lse;         int64_t lse_hs;       // lse[head * lse_hs + row]
+    int nh;             // query heads in this launch
+    int group;          // query heads per key/value head
+    int h0;             // global index of query head 0 of this launch
+    int kv_base;        // global index of key/value head 0 of k/v
+    int64_t nq, q_pos0; // query rows and the sequence position of row 0
+    int64_t nk, k_pos0; // keys and the sequence position of key 0
+    int causal;
+    int mode;
+    float scale_log2;   // softmax scale * log2(e)
+};
+
+// Copy nh heads x rows x D bf16 between strided layouts (16-byte vectors).
+struct PackParams {
+    const uint16_t* src; int64_t s_rs, s_hs;
+    uint16_t* dst;       int64_t d_rs, d_hs;
+    int nh;
+    int64_t rows;
+    int D;
+};
+
+// Log-sum-exp merge of a trunk partial (o_t, l_t) into the running (o_r, l_r).
+// final != 0 writes bf16 O into out (strided) and natural LSE into lse_out.
+struct MergeParams {
+    float* o_r; float* l_r;              // [nh][rows][D], [nh][rows]
+    const float* o_t; const float* l_t;  // same shapes
+    int nh;
+    int64_t rows;
+    int D;
+    int final_out;
+    uint16_t* out; int64_t out_rs, out_hs;
+    float* lse_out; int64_t lse_hs;
+};
+
+// Backward preprocessing: Delta[h][i] = sum_d dO[i,h,d] * O[i,h,d] (fp32,
+// fixed order) and the packed copy of dO.
+struct PrepParams {
+    const uint16_t* o;  int64_t o_rs, o_hs;
+    const uint16_t* dO; int64_t do_rs, do_hs;
+    uint16_t* dO_c;     int64_t c_rs, c_hs;
+    float* delta;       int64_t delta_hs;
+    int nh;
+    int64_t rows;
+    int D;
+};
+
+// dK/dV of one chunk over a key range: one workgroup per (key tile, kv head).
+// For each kv head the chunk's query heads of its group are walked in
+// ascending order, each over its query tiles in ascending order.
+struct DkdvParams {
+    const uint16_t* q;  int64_t q_rs, q_hs;    // chunk query heads (local 0..nh)
+    const uint16_t* dO; int64_t do_rs, do_hs;
+    const float* lse;   int64_t lse_hs;        // natural LSE, [head][row]
+    const float* delta; int64_t delta_hs;
+    const uint16_t* k;  int64_t k_rs, k_hs;    // kv heads (local 0..nkv)
+    const uint16_t* v;  int64_t v_rs, v_hs;
+    int nh, group, h0, kv_base, nkv;
+    int64_t nq;                                // query rows (positions 0..nq)
+    int64_t nk, k_pos0;                        // keys of this launch, position of key 0
+    int causal;
+    float scale;                               // softmax scale
+    float scale_log2;
+    // accumulator in/out: fp32 carry [kv][row][D] (row = key index in launch)
+    const float* acc_in_k; const float* acc_in_v; int64_t ain_rs, ain_hs;  // null = start at 0
+    int carry_kv_in;    // local kv index whose accumulator comes from acc_in (-1 none)
+    float* acc_out_k; float* acc_out_v; int64_t aout_rs, aout_hs;
+    int carry_kv_out;   // local kv index that writes fp32 to acc_out (-1 none)
+    uint16_t* dk; uint16_t* dv; int64_t dk_rs, dk_hs;   // final bf16 output for the others
+};
+// acc_in/acc_out rows are indexed by key within this launch (0..nk); dk/dv
+// rows likewise.
+
+// dQ of one chunk over a key range: one workgroup per (query tile, head).
+struct DqParams {
+    const uint16_t* q;  int64_t q_rs, q_hs;
+    const uint16_t* dO; int64_t do_rs, do_hs;
+    const float* lse;   int64_t lse_hs;
+    const float* delta; int64_t delta_hs;
+    const uint16_t* k;  int64_t k_rs, k_hs;
+    const uint16_t* v;  int64_t v_rs, v_hs;
+    int nh, group, h0, kv_base;
+    int64_t nq;                  // query rows (positions 0..nq)
+    int64_t nk, k_pos0;          // keys of this launch
+    int causal;
+    float scale, scale_log2;
+    const float* acc_in;  int64_t ain_rs, ain_hs;   // fp32 dQ carry in (null = 0)
+    float* acc_out;       int64_t aout_rs, aout_hs; // fp32 carry out (null = final)
+    uint16_t* dq;         int64_t dq_rs, dq_hs;     // final bf16 output
+    int64_t q_begin;      // first query row processed (earlier rows untouched)
+    int64_t final_before; // rows < final_before write bf16 dq, the rest fp32 acc_out
+};
+
+hipError_t launch_fwd(const FwdParams& p, int D, hipStream_t st);
+hipError_t launch_pack(const PackParams& p, hipStream_t st);
+hipError_t launch_merge(const MergeParams& p, hipStream_t st);
+hipError_t launch_prep(const PrepParams& p, hipStream_t st);
+hipError_t launch_dkdv(const DkdvParams& p, int D, hipStream_t st);
+hipError_t launch_dq(const DqParams& p, int D, hipStream_t st);
+
+// Tile sizes the host planner relies on (query rows per forward/dQ workgroup,
+// keys per dK/dV workgroup).
+constexpr int kFwdBlockM = 128;
+constexpr int kDqBlockM = 128;
+constexpr int kDkdvBlockN = 128;
+
+}  // namespace hc

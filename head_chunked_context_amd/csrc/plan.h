@@ -1,0 +1,164 @@
+// plan.h - host-side planning: argument checks, head chunks, key/value
+// trunks and the workspace carve.  Pure integer arithmetic, no HIP calls.
+//
+// Head chunks: query heads [c*hc, min((c+1)*hc, Hq)), ascending, walked one
+// after another through one workspace that every chunk reuses (Road to 5
+// Million Tokens talk, U-Pipe paragraph: compute a group of heads, store the
+// partial result, move on reusing the buffers).  The chunk's key/value heads
+// are kv = h / g for its query heads.
+// Trunks: sequence slices of T tokens, N = ceil(S / T) (FPDT summary, "Key
+// Findings" item 1 and "Technical Deep Dive", the S/N trunk paragraph).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+#include <stdio.h>
+
+namespace hc {
+
+constexpr int64_t kTrunkGranule = 256;  // trunk length must be a multiple
+constexpr size_t kAlign = 256;
+
+struct Chunk {
+    int h0, nh;    // query heads [h0, h0 + nh)
+    int kv0, nkv;  // key/value heads [kv0, kv0 + nkv)
+};
+
+struct Plan {
+    bool bwd;
+    int64_t S;
+    int Hq, Hkv, D, causal, hc, g;
+    int64_t T, N;  // trunk length (S when untrunked), number of trunks
+    bool trunked;
+    int nchunks, kvc;   // chunks, max kv heads in a chunk
+    int carry_slots;    // fp32 dK/dV carries (bwd, group spanning chunks)
+
+    // workspace regions, byte offsets
+    size_t q_c = 0, k_c = 0, v_c = 0;                   // packed chunk buffers
+    size_t o_run = 0, o_t = 0, l_run = 0, l_t = 0;      // fwd trunk partials
+    size_t ring_k[2] = {0, 0}, ring_v[2] = {0, 0};      // trunk ring slots
+    size_t do_c = 0, delta_c = 0, dq_acc = 0;           // bwd chunk buffers
+    size_t carry_k[2] = {0, 0}, carry_v[2] = {0, 0};    // bwd fp32 carries
+    size_t stage_k[2] = {0, 0}, stage_v[2] = {0, 0};    // bwd dK/dV staging
+    size_t total = 0;
+
+    Chunk chunk(int c) const {
+        Chunk ch;
+        ch.h0 = c * hc;
+        ch.nh = (ch.h0 + hc <= Hq) ? hc : Hq - ch.h0;
+        ch.kv0 = ch.h0 / g;
+        ch.nkv = (ch.h0 + ch.nh - 1) / g - ch.kv0 + 1;
+        return ch;
+    }
+    int64_t trunk_begin(int64_t t) const { return t * T; }
+    int64_t trunk_rows(int64_t t) const { return (t + 1) * T <= S ? T : S - t * T; }
+    // carry slot a chunk reads its first kv head's fp32 dK/dV from, or -1
+    int carry_in_slot(int c) const {
+        if (carry_slots == 0) return -1;
+        const Chunk ch = chunk(c);
+        if (ch.h0 % g == 0) return -1;  // first kv head starts in this chunk
+        return carry_slots == 1 ? 0 : (c - 1) & 1;
+    }
+    // carry slot a chunk writes its last kv head's fp32 dK/dV to, or -1
+    int carry_out_slot(int c) const {
+        if (carry_slots == 0) return -1;
+        const Chunk ch = chunk(c);
+        if ((ch.h0 + ch.nh) % g == 0) return -1;  // last kv head ends here
+        return carry_slots == 1 ? 0 : c & 1;
+    }
+};
+
+static inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Returns 0 and fills *pl, or -1 (invalid) / -2 (unsupported) with a message.
+static inline int make_plan(bool bwd, int64_t S, int Hq, int Hkv, int D, int causal,
+                            int head_chunk, int64_t kv_trunk, Plan* pl, char* err, size_t errlen) {
+    if (S < 1) { snprintf(err, errlen, "S must be >= 1 (got %lld)", (long long)S); return -1; }
+    if (Hq < 1 || Hkv < 1) { snprintf(err, errlen, "Hq and Hkv must be >= 1"); return -1; }
+    if (Hq % Hkv != 0) {
+        snprintf(err, errlen, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+        return -1;
+    }
+    if (causal != 0 && causal != 1) { snprintf(err, errlen, "causal must be 0 or 1"); return -1; }
+    if (head_chunk < 0 || head_chunk > Hq) {
+        snprintf(err, errlen, "head_chunk must be in [0, Hq=%d] (got %d)", Hq, head_chunk);
+        return -1;
+    }
+    if (kv_trunk < 0) { snprintf(err, errlen, "kv_trunk must be >= 0"); return -1; }
+    if (D != 64 && D != 128) {
+        snprintf(err, errlen, "head dimension %d not supported (64 or 128)", D);
+        return -2;
+    }
+    if (S > (int64_t(1) << 31)) {
+        snprintf(err, errlen, "S = %lld exceeds 2^31 rows", (long long)S);
+        return -2;
+    }
+    Plan p;
+    p.bwd = bwd;
+    p.S = S; p.Hq = Hq; p.Hkv = Hkv; p.D = D; p.causal = causal;
+    p.hc = head_chunk == 0 ? Hq : head_chunk;
+    p.g = Hq / Hkv;
+    p.trunked = kv_trunk > 0 && kv_trunk < S;
+    if (p.trunked && kv_trunk % kTrunkGranule != 0) {
+        snprintf(err, errlen, "kv_trunk (%lld) must be a multiple of %lld", (long long)kv_trunk,
+                 (long long)kTrunkGranule);
+        return -1;
+    }
+    p.T = p.trunked ? kv_trunk : S;
+    p.N = (S + p.T - 1) / p.T;
+    p.nchunks = (Hq + p.hc - 1) / p.hc;
+    p.kvc = 0;
+    for (int c = 0; c < p.nchunks; ++c) {
+        const Chunk ch = p.chunk(c);
+        if (ch.nkv > p.kvc) p.kvc = ch.nkv;
+    }
+    p.carry_slots = 0;
+    if (bwd && p.hc % p.g != 0) p.carry_slots = (p.g % p.hc == 0) ? 1 : 2;
+
+    const size_t E = (size_t)S * D * 2;         // one bf16 head slice
+    const size_t Et = (size_t)p.T * D * 2;      // one bf16 trunk slice
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+    if (!bwd) {
+        if (!p.trunked) {
+            p.q_c = take(p.hc * E);
+            p.k_c = take(p.kvc * E);
+            p.v_c = take(p.kvc * E);
+        } else {
+            p.q_c = take(p.hc * Et);                          // query trunk
+            p.o_run = take(p.hc * Et * 2);                    // fp32 running O
+            p.o_t = take(p.hc * Et * 2);                      // fp32 trunk partial
+            p.l_run = take((size_t)p.hc * p.T * 4);
+            p.l_t = take((size_t)p.hc * p.T * 4);
+            for (int s = 0; s < 2; ++s) {
+                p.ring_k[s] = take(p.kvc * Et);
+                p.ring_v[s] = take(p.kvc * Et);
+            }
+        }
+    } else {
+        p.q_c = take(p.hc * E);
+        p.do_c = take(p.hc * E);
+        p.delta_c = take((size_t)p.hc * S * 4);
+        if (!p.trunked) {
+            p.k_c = take(p.kvc * E);
+            p.v_c = take(p.kvc * E);
+        } else {
+            p.dq_acc = take(p.hc * E * 2);                    // fp32 dQ carried over trunks
+            for (int s = 0; s < 2; ++s) {
+                p.ring_k[s] = take(p.kvc * Et);
+                p.ring_v[s] = take(p.kvc * Et);
+                p.stage_k[s] = take(p.kvc * Et);
+                p.stage_v[s] = take(p.kvc * Et);
+            }
+        }
+        for (int s = 0; s < p.carry_slots; ++s) {
+            p.carry_k[s] = take(E * 2);                       // fp32 [S][D]
+            p.carry_v[s] = take(E * 2);
+        }
+    }
+    p.total = off;
+    *pl = p;
+    return 0;
+}
+
+}  // namespace hc

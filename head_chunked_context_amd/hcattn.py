@@ -1,0 +1,162 @@
+"""Thin ctypes binding of libhcattn.so (include/hcattn.h).
+
+Argument marshalling only: every step of attention runs in the library's HIP
+kernels.  PyTorch provides device/pinned memory and the current HIP stream.
+The library is loaded on first use; if it is missing the call raises (there
+is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhcattn.so")
+
+ATTN_OK = 0
+STATUS = {0: "ATTN_OK", -1: "ATTN_EINVAL", -2: "ATTN_EUNSUPPORTED", -3: "ATTN_EWORKSPACE",
+          -4: "ATTN_EPOINTER", -5: "ATTN_EHIP"}
+
+_lib = None
+
+
+class HcAttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def lib():
+    """Load libhcattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m head_chunked_context_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    shape = [i64, i32, i32, i32, i32, i32, i64]
+    L.attn_fwd_workspace_bytes.argtypes = shape
+    L.attn_fwd_workspace_bytes.restype = sz
+    L.attn_bwd_workspace_bytes.argtypes = shape
+    L.attn_bwd_workspace_bytes.restype = sz
+    L.attn_fwd.argtypes = [vp] * 5 + shape + [vp, sz, vp]
+    L.attn_fwd.restype = ctypes.c_int
+    L.attn_bwd.argtypes = [vp] * 9 + shape + [vp, sz, vp]
+    L.attn_bwd.restype = ctypes.c_int
+    L.attn_last_error.argtypes = []
+    L.attn_last_error.restype = ctypes.c_char_p
+    L.attn_set_single_stream.argtypes = [ctypes.c_int]
+    L.attn_set_single_stream.restype = ctypes.c_int
+    L.attn_version.argtypes = []
+    L.attn_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().attn_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != ATTN_OK:
+        raise HcAttnError(rc, last_error())
+
+
+def _dims(q, k):
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [S, Hq, D] and k [S, Hkv, D]")
+    S, Hq, D = q.shape
+    if k.shape[0] != S or k.shape[2] != D:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    return S, Hq, k.shape[1], D
+
+
+def _bf16(name, t):
+    if t.dtype != torch.bfloat16 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
+
+
+def fwd_workspace_bytes(S, Hq, Hkv, D, causal=True, head_chunk=0, kv_trunk=0) -> int:
+    n = lib().attn_fwd_workspace_bytes(S, Hq, Hkv, D, int(causal), head_chunk, kv_trunk)
+    if n == 0:
+        raise HcAttnError(-1, last_error())
+    return n
+
+
+def bwd_workspace_bytes(S, Hq, Hkv, D, causal=True, head_chunk=0, kv_trunk=0) -> int:
+    n = lib().attn_bwd_workspace_bytes(S, Hq, Hkv, D, int(causal), head_chunk, kv_trunk)
+    if n == 0:
+        raise HcAttnError(-1, last_error())
+    return n
+
+
+def _stream(device) -> int:
+    if device.type != "cuda":  # the library rejects such tensors before using the stream
+        return torch.cuda.current_stream().cuda_stream
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, "
+                         f"needs {nbytes}")
+    return workspace
+
+
+def attn_fwd(q, k, v, *, head_chunk: int = 0, kv_trunk: int = 0, causal: bool = True,
+             out=None, lse=None, workspace=None):
+    """Causal GQA attention forward.  q [S,Hq,D] bf16 on the GPU; k, v [S,Hkv,D]
+    bf16 on the GPU or, with kv_trunk, in pinned host memory.  Returns
+    (o [S,Hq,D] bf16, lse [Hq,S] fp32)."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _bf16(n, t)
+    S, Hq, Hkv, D = _dims(q, k)
+    dev = q.device
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((Hq, S), dtype=torch.float32, device=dev) if lse is None else lse
+    nb = fwd_workspace_bytes(S, Hq, Hkv, D, causal, head_chunk, kv_trunk)
+    ws = _workspace(nb, dev, workspace)
+    rc = lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+                        S, Hq, Hkv, D, int(causal), head_chunk, kv_trunk, ws.data_ptr(), nb,
+                        _stream(dev))
+    _check(rc)
+    return o, l
+
+
+def attn_bwd(q, k, v, o, dout, lse, *, head_chunk: int = 0, kv_trunk: int = 0,
+             causal: bool = True, dq=None, dk=None, dv=None, workspace=None):
+    """Backward of attn_fwd.  Returns (dq, dk, dv) in bf16; dk/dv are placed
+    where k lives (device, or pinned host memory)."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _bf16(n, t)
+    S, Hq, Hkv, D = _dims(q, k)
+    dev = q.device
+    dq = torch.empty_like(q) if dq is None else dq
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=k.dtype, device=k.device,
+                         pin_memory=(k.device.type == "cpu"))
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=v.dtype, device=v.device,
+                         pin_memory=(v.device.type == "cpu"))
+    nb = bwd_workspace_bytes(S, Hq, Hkv, D, causal, head_chunk, kv_trunk)
+    ws = _workspace(nb, dev, workspace)
+    rc = lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), S, Hq, Hkv, D,
+                        int(causal), head_chunk, kv_trunk, ws.data_ptr(), nb, _stream(dev))
+    _check(rc)
+    return dq, dk, dv
+
+
+def set_single_stream(on: bool) -> bool:
+    """Run trunk copies on the caller's stream (race check); returns the old value."""
+    return bool(lib().attn_set_single_stream(int(on)))
+
+
+def version() -> str:
+    return lib().attn_version().decode()

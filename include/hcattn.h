@@ -1,0 +1,144 @@
+/*
+ * hcattn.h - C ABI of libhcattn.so: exact causal grouped-query attention,
+ * forward and backward, on one AMD MI355X (gfx950), scheduled in query-head
+ * chunks that reuse one workspace and, optionally, over key/value trunks that
+ * can stream from pinned host memory and are merged by log-sum-exp.
+ *
+ * What is computed (per query head h, key/value head kv = h / (Hq / Hkv),
+ * scale c = 1 / sqrt(D), query row i, visible keys J(i) = {0..i} when causal,
+ * {0..S-1} otherwise):
+ *     s_ij = c <q_i, k_j>,  LSE_i = log sum_{J(i)} exp(s_ij),
+ *     O_i = sum_{J(i)} exp(s_ij - LSE_i) v_j
+ * and the gradients of sum(O * dO) with respect to q, k, v.
+ *   - A query attends to the keys that precede it or sit at its position:
+ *     FPDT talk summary (MLSys 2025), "Technical Deep Dive", paragraph on the
+ *     auto-regressive nature of LLMs.
+ *   - Exact softmax attention computed block by block with running softmax
+ *     statistics (the maximum logit and the sum): same section, the paragraph
+ *     comparing trunk processing with online softmax and FlashAttention.
+ *   - Query heads processed a group ("chunk") at a time through buffers that
+ *     every chunk reuses: Road to 5 Million Tokens talk, the U-Pipe paragraph;
+ *     the UPipe abstract (arXiv 2602.21196) for head-level chunking.
+ *   - Key/value trunks, their host-memory offload and double-buffered
+ *     prefetch on a separate copy stream: FPDT summary, "Key Findings" items
+ *     1-3 and "Technical Deep Dive" (trunking, offloading, double buffer,
+ *     three streams).
+ *
+ * Common arguments
+ *   q, o, dout, dq : bf16 [S][Hq][D], token-major, contiguous, device memory.
+ *   k, v, dk, dv   : bf16 [S][Hkv][D], token-major, contiguous.  Device
+ *                    memory, or pinned host memory (hipHostMalloc / torch
+ *                    pin_memory) when kv_trunk selects the trunked path.
+ *   lse            : fp32 [Hq][S], device memory; natural-log LSE of the
+ *                    scaled scores (output of attn_fwd, input of attn_bwd).
+ *   S >= 1; Hq, Hkv >= 1 with Hq % Hkv == 0; D == 64 or 128;
+ *   causal 0 or 1 (1 is the measured case; 0 runs the same kernels).
+ *   head_chunk     : query heads per chunk, 0 means Hq; 1..Hq.  Chunks are
+ *                    consecutive ascending head ranges; the last may be short.
+ *   kv_trunk       : 0, or >= S, for the untrunked path; otherwise the trunk
+ *                    length in tokens, a positive multiple of 256.
+ *   workspace      : device memory of at least attn_*_workspace_bytes(...)
+ *                    bytes, 256-byte aligned; owned by the caller, fully
+ *                    overwritten; its contents are undefined afterwards.
+ *   stream         : a hipStream_t (NULL = the default stream).  All work is
+ *                    ordered after prior work on it; later work on it sees the
+ *                    outputs.  The call never synchronises the host.
+ *
+ * Ownership and concurrency
+ *   The caller owns every buffer.  The library allocates no device memory; it
+ *   creates one copy stream and a few events per device on first use and keeps
+ *   them until unload.  No pointer is kept after a call returns.  Outputs must
+ *   not alias inputs or the workspace.  Calls from several host threads on one
+ *   device are serialised while they enqueue work.
+ *
+ * Errors
+ *   Every entry point returns ATTN_OK (0) or a negative status.  Argument
+ *   checks run before anything is enqueued; on failure nothing is enqueued.
+ *   ATTN_EHIP means a HIP call failed mid-call: outputs are undefined, the
+ *   library stays usable.  attn_last_error() returns this thread's text for
+ *   the last non-zero status.
+ *
+ * Determinism
+ *   Results are bitwise reproducible run to run and bitwise identical for
+ *   every head_chunk value (no atomics; fixed accumulation orders).  The
+ *   backward result is also bitwise identical with and without kv_trunk for
+ *   the same o and lse; the trunked forward agrees with the untrunked one to
+ *   rounding (the log-sum-exp merge rounds).
+ */
+#ifndef HCATTN_H
+#define HCATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_EINVAL = -1,       /* bad shape, flag or size                      */
+    ATTN_EUNSUPPORTED = -2, /* valid but not built (e.g. D not 64/128)      */
+    ATTN_EWORKSPACE = -3,   /* workspace NULL, misaligned or too small      */
+    ATTN_EPOINTER = -4,     /* NULL, unregistered host or misplaced pointer */
+    ATTN_EHIP = -5          /* a HIP runtime call failed                    */
+};
+
+/*
+ * Bytes of device workspace attn_fwd needs for these arguments.  It grows
+ * with head_chunk (the chunk's packed Q/K/V, or with kv_trunk the chunk's
+ * query trunk, fp32 partials and the two-slot K/V ring), not with Hq.
+ * Returns 0 when the arguments are invalid (attn_last_error says why).
+ */
+size_t attn_fwd_workspace_bytes(int64_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t causal,
+                                int32_t head_chunk, int64_t kv_trunk);
+
+/* Same for attn_bwd (chunk's packed Q, dO, K, V, Delta, fp32 dQ/dK/dV carries,
+ * and with kv_trunk the K/V ring and dK/dV staging). 0 on invalid arguments. */
+size_t attn_bwd_workspace_bytes(int64_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t causal,
+                                int32_t head_chunk, int64_t kv_trunk);
+
+/*
+ * Forward: writes o (bf16, round-to-nearest-even from fp32) and lse.
+ * For each chunk the chunk's query heads and the key/value heads they read are
+ * packed head-major into the workspace (the one-device stand-in for the
+ * per-chunk all-to-all), then the flash kernel runs on them.  With kv_trunk,
+ * query trunk m attends to key/value trunks 0..m (0..N-1 non-causal), each
+ * copied into a ring slot on the copy stream while the previous trunk
+ * computes, and the partial outputs are merged by log-sum-exp.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t S,
+             int32_t Hq, int32_t Hkv, int32_t D, int32_t causal, int32_t head_chunk,
+             int64_t kv_trunk, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward: given q, k, v, the forward's o and lse, and dout, writes dq, dk,
+ * dv (bf16).  Delta = rowsum(dout * o) is computed first from the bf16 o; P is
+ * recomputed from lse.  dK/dV of a key/value head accumulate over the heads of
+ * its group in ascending order, then over query tiles in ascending order, in
+ * fp32 (carried exactly in fp32 across chunks when a group spans chunks);
+ * dQ accumulates over key tiles in ascending order (carried in fp32 across
+ * trunks).  With kv_trunk the key/value trunks are the outer loop.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int64_t S, int32_t Hq, int32_t Hkv,
+             int32_t D, int32_t causal, int32_t head_chunk, int64_t kv_trunk, void* workspace,
+             size_t workspace_bytes, void* stream);
+
+/* This thread's message for the last non-zero status ("" if none). */
+const char* attn_last_error(void);
+
+/*
+ * Debug switch: on != 0 makes the copy stream the caller's stream, so trunk
+ * copies and kernels run strictly in order (a race check: results must be
+ * bitwise equal to the overlapped run).  Returns the previous setting.
+ */
+int attn_set_single_stream(int on);
+
+/* Library version, "major.minor.patch". */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HCATTN_H */

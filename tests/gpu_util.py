@@ -1,0 +1,87 @@
+"""Helpers for the GPU parity tests: run the library through its C ABI binding
+and compare with the oracle on the same seeded bf16 inputs."""
+import numpy as np
+import torch
+
+from head_chunked_context_amd import attn_bwd, attn_fwd
+from head_chunked_context_amd.inputs import attention_inputs
+from oracle import oracle as orc
+
+DEV = "cuda"
+TOL = 2e-2       # max-abs, O / dQ / dK / dV (bf16 in, fp32 accumulate)
+TOL_LSE = 1e-3   # max-abs, LSE
+
+# O, dQ, dK and dV are returned in bf16, so even the exact result rounded to
+# bf16 is off by up to half a bf16 ulp of its own value (2^-8 relative at
+# worst): gradients of GQA groups reach |x| ~ 8-30, where that alone exceeds
+# 2e-2.  The bar is therefore applied to the error beyond the output's own
+# representation:  |gpu - oracle| - half_ulp_bf16(oracle) <= TOL.
+
+
+def inputs_cpu(S, Hq, Hkv, D, seed, q_scale=1.0):
+    return attention_inputs(S, Hq, Hkv, D, seed, device="cpu", q_scale=q_scale)
+
+
+def to_dev(inp, kv_host=False):
+    out = {}
+    for n, t in inp.items():
+        if kv_host and n in ("k", "v"):
+            out[n] = t.pin_memory()
+        else:
+            out[n] = t.to(DEV)
+    return out
+
+
+def gpu_fwd(d, hc, trunk=0, causal=True):
+    o, lse = attn_fwd(d["q"], d["k"], d["v"], head_chunk=hc, kv_trunk=trunk, causal=causal)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def gpu_bwd(d, o, lse, hc, trunk=0, causal=True):
+    g = attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, head_chunk=hc, kv_trunk=trunk,
+                 causal=causal)
+    torch.cuda.synchronize()
+    return g
+
+
+def f64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def maxabs(a, b):
+    return float(np.max(np.abs(np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64))))
+
+
+def half_ulp_bf16(x):
+    """Half a bf16 ulp of each value (bf16 keeps 8 significant bits)."""
+    a = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), np.finfo(np.float64).tiny)
+    return np.ldexp(1.0, np.floor(np.log2(a)).astype(np.int64) - 8)
+
+
+def bf16_excess(gpu, ref):
+    """max over elements of |gpu - ref| beyond half a bf16 ulp of ref."""
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(np.asarray(gpu, dtype=np.float64) - ref) - half_ulp_bf16(ref)))
+
+
+def check_fwd(inp, o, lse, causal=True, tol=TOL):
+    ro, rl = orc.attn_fwd(inp["q"], inp["k"], inp["v"], causal)
+    eo, el = bf16_excess(f64(o), ro), maxabs(f64(lse), rl)
+    print(f"  O max-abs {maxabs(f64(o), ro):.3e} (beyond bf16 rounding {eo:.3e}), "
+          f"LSE max-abs {el:.3e}", flush=True)
+    assert eo <= tol, f"O error beyond bf16 rounding {eo}"
+    assert el <= TOL_LSE, f"LSE max-abs error {el}"
+    return eo, el
+
+
+def check_bwd(inp, g, causal=True, rel=False):
+    ref = orc.attn_bwd(inp["q"], inp["k"], inp["v"], inp["dout"], causal)
+    errs = {}
+    for name, t in zip(("dq", "dk", "dv"), g):
+        errs[name] = bf16_excess(f64(t), ref[name])
+        bound = TOL * max(1.0, float(np.max(np.abs(ref[name])))) if rel else TOL
+        print(f"  {name} max-abs {maxabs(f64(t), ref[name]):.3e} (beyond bf16 rounding "
+              f"{errs[name]:.3e}, bound {bound:.2e})", flush=True)
+        assert errs[name] <= bound, f"{name} error beyond bf16 rounding {errs[name]}"
+    return errs

@@ -1,0 +1,158 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances: max-abs 2e-2 for O, dQ, dK, dV and 1e-3 for LSE, on the same
+seeded bf16 inputs (the oracle widens them exactly).  Results must also be
+bitwise identical across head_chunk values and run to run.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_util import (DEV, TOL, TOL_LSE, check_bwd, check_fwd, f64, gpu_bwd, gpu_fwd,
+                            inputs_cpu, maxabs, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_case(S, Hq, Hkv, D, hcs, seed, causal=True, q_scale=1.0, rel=False):
+    inp = inputs_cpu(S, Hq, Hkv, D, seed, q_scale)
+    d = to_dev(inp)
+    outs = {}
+    for hc in hcs:
+        print(f"case S={S} Hq={Hq} Hkv={Hkv} D={D} hc={hc} causal={causal}", flush=True)
+        o, lse = gpu_fwd(d, hc, causal=causal)
+        g = gpu_bwd(d, o, lse, hc, causal=causal)
+        outs[hc] = (o, lse) + tuple(g)
+    ref = outs[hcs[0]]
+    for hc in hcs[1:]:
+        for a, b, n in zip(ref, outs[hc], ("o", "lse", "dq", "dk", "dv")):
+            assert torch.equal(a, b), f"{n} differs bitwise between hc={hcs[0]} and hc={hc}"
+    check_fwd(inp, ref[0], ref[1], causal)
+    check_bwd(inp, ref[2:], causal, rel=rel)
+
+
+def test_tiny_exactness_case_all_head_chunks():
+    # S=256, Hq=4, Hkv=2, D=64, head_chunk in {1, 2, 4}
+    _run_case(256, 4, 2, 64, [4, 1, 2], seed=1)
+
+
+def test_ragged_tail_d128():
+    _run_case(1000, 4, 2, 128, [4, 1, 2], seed=11)
+
+
+def test_gqa_chunks_not_aligned_with_groups():
+    # g = 4; hc = 3 makes groups span chunks (two fp32 carry slots), hc = 1 nests
+    _run_case(700, 8, 2, 128, [8, 3, 1, 2], seed=12)
+
+
+def test_non_causal():
+    _run_case(300, 4, 1, 128, [4, 1], seed=13, causal=False)
+
+
+def test_non_causal_d64_ragged():
+    _run_case(333, 2, 2, 64, [2, 1], seed=14, causal=False)
+
+
+def test_peaked_softmax():
+    # Q scaled by 8 (scores ~N(0, 64)): a stress case outside the N(0,1) workloads,
+    # where |dK| reaches ~30; gradients are held to 2e-2 relative to their peak
+    _run_case(512, 2, 1, 128, [2, 1], seed=15, q_scale=8.0, rel=True)
+
+
+def test_single_token_and_tiny():
+    for S in (1, 2, 33):
+        _run_case(S, 2, 1, 128, [2, 1], seed=16 + S)
+
+
+def test_run_to_run_deterministic():
+    inp = inputs_cpu(777, 4, 2, 128, 21)
+    d = to_dev(inp)
+    a = gpu_fwd(d, 2)
+    b = gpu_fwd(d, 2)
+    ga = gpu_bwd(d, a[0], a[1], 2)
+    gb = gpu_bwd(d, b[0], b[1], 2)
+    for x, y in zip(a + ga, b + gb):
+        assert torch.equal(x, y)
+
+
+def test_q_zero_closed_form():
+    # q = 0: P is uniform over the visible keys, LSE_i = ln(i+1), O_i = mean(v_0..v_i)
+    S, Hq, Hkv, D = 4096, 2, 1, 128
+    inp = inputs_cpu(S, Hq, Hkv, D, 22)
+    inp["q"].zero_()
+    d = to_dev(inp)
+    o, lse = gpu_fwd(d, 1)
+    i = np.arange(S)
+    v = f64(inp["v"])[:, 0, :]
+    prefix = np.cumsum(v, 0) / (i + 1.0)[:, None]
+    for h in range(Hq):
+        assert maxabs(f64(lse)[h], np.log(i + 1.0)) <= 1e-5
+        assert maxabs(f64(o)[:, h, :], prefix) <= 1e-2
+    # O_0 = v_0 exactly (one visible key, p = 1)
+    assert torch.equal(o[0, 0].cpu(), inp["v"][0, 0])
+
+
+@pytest.mark.parametrize("kv_host", [False, True])
+def test_kv_trunks_match_oracle_and_untrunked_backward(kv_host):
+    S, Hq, Hkv, D, hc, T = 1100, 4, 2, 128, 2, 256  # 5 trunks, ragged last one
+    inp = inputs_cpu(S, Hq, Hkv, D, 31)
+    d = to_dev(inp)
+    dt = to_dev(inp, kv_host=kv_host)
+    print(f"trunked S={S} T={T} kv_host={kv_host}", flush=True)
+    ot, lt = gpu_fwd(dt, hc, trunk=T)
+    check_fwd(inp, ot, lt)
+    o, lse = gpu_fwd(d, hc)
+    assert maxabs(f64(ot), f64(o)) <= TOL
+    assert maxabs(f64(lt), f64(lse)) <= TOL_LSE
+    g = gpu_bwd(d, o, lse, hc)
+    gt = gpu_bwd(dt, o, lse, hc, trunk=T)
+    for a, b, n in zip(g, gt, ("dq", "dk", "dv")):
+        assert torch.equal(a.cpu(), b.cpu()), f"trunked {n} differs bitwise from untrunked"
+    check_bwd(inp, g)
+
+
+def test_trunked_groups_spanning_chunks_on_host():
+    # hc = 1 < g = 2: dK/dV carried in fp32 across chunks while K/V stream from host
+    S, Hq, Hkv, D, T = 768, 4, 2, 128, 256
+    inp = inputs_cpu(S, Hq, Hkv, D, 32)
+    d = to_dev(inp)
+    dt = to_dev(inp, kv_host=True)
+    o, lse = gpu_fwd(d, 1)
+    g = gpu_bwd(d, o, lse, 4)
+    gt = gpu_bwd(dt, o, lse, 1, trunk=T)
+    for a, b in zip(g, gt):
+        assert torch.equal(a.cpu(), b.cpu())
+
+
+def test_single_stream_equals_overlapped():
+    from head_chunked_context_amd import set_single_stream
+    S, Hq, Hkv, D, T = 1024, 2, 1, 128, 256
+    inp = inputs_cpu(S, Hq, Hkv, D, 33)
+    dt = to_dev(inp, kv_host=True)
+    o1, l1 = gpu_fwd(dt, 1, trunk=T)
+    g1 = gpu_bwd(dt, o1, l1, 1, trunk=T)
+    prev = set_single_stream(True)
+    try:
+        o2, l2 = gpu_fwd(dt, 1, trunk=T)
+        g2 = gpu_bwd(dt, o2, l2, 1, trunk=T)
+    finally:
+        set_single_stream(prev)
+    for a, b in zip((o1, l1) + tuple(g1), (o2, l2) + tuple(g2)):
+        assert torch.equal(a.cpu(), b.cpu())
+
+
+def test_errors_are_reported_without_work():
+    from head_chunked_context_amd import HcAttnError, attn_fwd
+    inp = inputs_cpu(64, 2, 1, 128, 34)
+    d = to_dev(inp)
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device=DEV)
+    with pytest.raises(HcAttnError) as e:
+        attn_fwd(inp["q"], d["k"], d["v"], workspace=ws)  # q in pageable host memory
+    assert e.value.code == -4
+    with pytest.raises((HcAttnError, ValueError)):
+        attn_fwd(d["q"], d["k"], d["v"], workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    with pytest.raises(HcAttnError) as e:
+        attn_fwd(d["q"], d["k"], d["v"], head_chunk=5)  # more than Hq
+    assert e.value.code == -1
