@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark: exact causal GQA attention, forward + backward, on one MI355X.
+
+One step = attn_fwd + attn_bwd (the whole path: chunk packing, flash forward,
+Delta preprocessing, dK/dV and dQ kernels, trunk copies and merges when the
+workload is trunked) over one batch of seeded synthetic bf16 inputs already
+resident in HBM.  Throughput counts the causal FLOPs 2*S^2*D*Hq for the
+forward and 2.5x that for the backward (7*S^2*D*Hq per step).
+
+Prints one JSON line.  Extra fields: the per-kernel roofline of the dominant
+kernel (HIP events around every launch, on the stream it runs on), workspace
+bytes per head_chunk (peak intermediate device memory), and the fp64 CPU
+oracle timed on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "causal attn fwd+bwd TFLOP/s & % bf16 MFMA peak; peak HBM bytes vs head_chunk"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 bf16 FLOP/clk x 2.4 GHz, dense
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="attention workload id (2 = Llama3-8B layer, S=32768)")
+    ap.add_argument("--head-chunk", type=int, default=0,
+                    help="query heads per chunk (default: one GQA group for workload 2/3)")
+    ap.add_argument("--no-compare", action="store_true", help="skip the other head_chunk")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=12288,
+                    help="tokens of the CPU-oracle sample (one GQA group)")
+    return ap.parse_args()
+
+
+def algorithmic_flops(family: str, S: int, Hq: int, D: int, causal: bool) -> float:
+    """MFMA work the algorithm asks of one kernel family for one full pass over
+    the workload: per visible (query, key) pair and head, QK^T and PV are 2*D
+    each (forward 4*D); dK/dV needs S, dP, dV, dK (8*D); dQ needs S, dP, dQ
+    (6*D).  Pairs per head = S^2/2 when causal (the counted convention)."""
+    pairs = S * S / 2.0 if causal else float(S) * S
+    per_pair = {"fwd": 4 * D, "dkdv": 8 * D, "dq": 6 * D}.get(family)
+    return 0.0 if per_pair is None else per_pair * pairs * Hq
+
+
+def cpu_oracle_baseline(D: int, g: int, tokens: int) -> dict:
+    """Time the fp64 oracle's forward + backward on one GQA group (g query
+    heads, 1 kv head) over the first `tokens` positions, seeded like the
+    workload; report its throughput in counted TFLOP/s."""
+    import torch
+
+    from head_chunked_context_amd.inputs import attention_inputs
+    from oracle import oracle as orc
+    inp = attention_inputs(tokens, g, 1, D, 900, device="cpu")
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    t0 = time.perf_counter()
+    orc.attn_fwd(inp["q"], inp["k"], inp["v"], True)
+    orc.attn_bwd(inp["q"], inp["k"], inp["v"], inp["dout"], True)
+    dt = time.perf_counter() - t0
+    counted = 7.0 * tokens * tokens * D * g
+    del torch
+    return {"value": counted / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 oracle forward+backward of one GQA group ({g} query heads, 1 kv "
+                      f"head, D={D}) over the first {tokens} tokens; {dt:.1f} s wall, counted "
+                      f"FLOPs 7*S^2*D*heads"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this attention path has no multi-GPU mode here "
+              "(the head-sharded all-to-all design is documented, not built). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import head_chunked_context_amd as hcm
+    from head_chunked_context_amd.inputs import WORKLOADS, attention_inputs
+
+    w = WORKLOADS[args.workload]
+    hc = args.head_chunk or w.head_chunks[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    S, Hq, Hkv, D, T = w.S, w.Hq, w.Hkv, w.D, w.kv_trunk
+    causal = True
+
+    inp = attention_inputs(S, Hq, Hkv, D, w.wid, device=dev)
+    if w.kv_on_host:
+        for n in ("k", "v"):
+            inp[n] = inp[n].cpu().pin_memory()
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["dout"]
+
+    def alloc_outputs():
+        o = torch.empty_like(q)
+        lse = torch.empty((Hq, S), dtype=torch.float32, device=dev)
+        dq = torch.empty_like(q)
+        pin = k.device.type == "cpu"
+        dk = torch.empty(k.shape, dtype=k.dtype, device=k.device, pin_memory=pin)
+        dv = torch.empty(v.shape, dtype=v.dtype, device=v.device, pin_memory=pin)
+        return o, lse, dq, dk, dv
+
+    o, lse, dq, dk, dv = alloc_outputs()
+    torch.cuda.synchronize()
+
+    def measure(hc_, steps, warmup, timing):
+        fb = hcm.fwd_workspace_bytes(S, Hq, Hkv, D, causal, hc_, T)
+        bb = hcm.bwd_workspace_bytes(S, Hq, Hkv, D, causal, hc_, T)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats(dev)
+        base = torch.cuda.memory_allocated(dev)
+        ws = torch.empty(max(fb, bb), dtype=torch.uint8, device=dev)
+
+        def step():
+            hcm.attn_fwd(q, k, v, head_chunk=hc_, kv_trunk=T, causal=causal, out=o, lse=lse,
+                         workspace=ws)
+            mid = torch.cuda.Event(enable_timing=True)
+            mid.record()
+            hcm.attn_bwd(q, k, v, o, do, lse, head_chunk=hc_, kv_trunk=T, causal=causal, dq=dq,
+                         dk=dk, dv=dv, workspace=ws)
+            return mid
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        if timing:
+            hcm.timing_reset()
+            hcm.timing_enable(True)
+        starts, mids = [], []
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        t_start.record()
+        for _ in range(steps):
+            s = torch.cuda.Event(enable_timing=True)
+            s.record()
+            starts.append(s)
+            mids.append(step())
+        t_end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        kern = None
+        if timing:
+            hcm.timing_enable(False)
+            kern = hcm.timing_read()
+            hcm.timing_reset()
+        total_ms = t_start.elapsed_time(t_end)
+        fwd_ms = sum(a.elapsed_time(b) for a, b in zip(starts, mids))
+        peak = torch.cuda.max_memory_allocated(dev) - base
+        del ws
+        return {"ms": total_ms / steps, "fwd_ms": fwd_ms / steps,
+                "bwd_ms": (total_ms - fwd_ms) / steps, "wall_s": wall, "kern": kern,
+                "ws_fwd": fb, "ws_bwd": bb, "peak_intermediate": peak}
+
+    r = measure(hc, args.steps, args.warmup, timing=True)
+    flops = 7.0 * S * S * D * Hq
+    tflops = flops / (r["ms"] / 1e3) / 1e12
+
+    # roofline of the dominant kernel family in the timed region
+    kern = r["kern"]
+    dom = max((f for f in kern if kern[f][0] > 0), key=lambda f: kern[f][1])
+    n_launch, dom_ms = kern[dom]
+    alg = algorithmic_flops(dom, S, Hq, D, causal) * args.steps
+    if alg > 0:
+        achieved = alg / (dom_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "launches": n_launch, "avg_launch_ms": round(dom_ms / n_launch, 4),
+                "flops_per_launch": alg / n_launch}
+    else:
+        roof = {"bound": "hbm", "kernel": dom, "achieved": None, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": None, "traffic": None}
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "S": S, "Hq": Hq, "Hkv": Hkv, "D": D,
+                   "head_chunk": hc, "kv_trunk": T, "kv_on_host": w.kv_on_host,
+                   "causal": causal, "batch": 1},
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(2.0 * S * S * D * Hq / (r["fwd_ms"] / 1e3) / 1e12, 2),
+        "bwd_tflops": round(5.0 * S * S * D * Hq / (r["bwd_ms"] / 1e3) / 1e12, 2),
+        "workspace_bytes": {str(hc): {"fwd": r["ws_fwd"], "bwd": r["ws_bwd"],
+                                      "peak_intermediate": r["peak_intermediate"]}},
+        "kernel_ms_per_step": {f: round(kern[f][1] / args.steps, 3) for f in kern if kern[f][0]},
+        "roofline": roof,
+    }
+    others = [h for h in w.head_chunks if h != hc]
+    if not args.no_compare and others:
+        other = Hq if Hq in others else others[-1]
+        r2 = measure(other, max(1, min(3, args.steps)), 1, timing=False)
+        line["workspace_bytes"][str(other)] = {"fwd": r2["ws_fwd"], "bwd": r2["ws_bwd"],
+                                               "peak_intermediate": r2["peak_intermediate"]}
+        line["head_chunk_compare"] = {
+            "head_chunk": other,
+            "value": round(flops / (r2["ms"] / 1e3) / 1e12, 2),
+            "ms_per_step": round(r2["ms"], 3),
+            "workspace_ratio": round(max(r["ws_fwd"], r["ws_bwd"]) /
+                                     max(r2["ws_fwd"], r2["ws_bwd"]), 4),
+        }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_oracle_baseline(D, Hq // Hkv, args.cpu_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -10,9 +10,10 @@
 // output tile, with fixed accumulation orders (dK/dV: the group's query heads
 // ascending, then query tiles ascending; dQ: key tiles ascending).
 //
-// dkdv_kernel: workgroup = 4 waves x 32 keys (128 keys) of one kv head.  K and
-// V stay in registers as MFMA operands; each step stages a 64-row query tile
-// of Q and dO (plus LSE and Delta) through LDS, double-buffered:
+// dkdv_kernel: workgroup = 4 waves x 32 keys (128 keys) of one query head's kv
+// head.  K and V stay in registers as MFMA operands; each step loads a 64-row
+// query tile of Q and dO (plus LSE and Delta) straight into LDS,
+// double-buffered:
 //   S[q][key]   = Q K^T        A = Q tile (LDS),   B = K (regs)
 //   dP[q][key]  = dO V^T       A = dO tile (LDS),  B = V (regs)
 //   dV^T[d][key] += dO^T P     A = dO tile, transposed LDS reads
@@ -20,7 +21,8 @@
 // so each lane owns one key (lanes l and l^32 split the 64 query rows).
 //
 // dq_kernel: workgroup = 4 waves x 32 query rows of one head; Q and dO stay in
-// registers; 64-key tiles of K and V go through LDS like the forward:
+// registers; 64-key tiles of K and V are loaded straight into LDS like the
+// forward:
 //   S^T = K Q^T,  dP^T = V dO^T,  dQ^T[d][q] += K^T dS^T (transposed K reads)
 #include "device_common.h"
 #include "kernels.h"
@@ -29,33 +31,68 @@ namespace hc {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// P and dS of one 64-row query tile against this lane's key, as bf16 MFMA
+// operands.  MASK adds the causal / ragged-edge test; the common interior
+// tiles skip it entirely.
+template <bool MASK>
+__device__ __forceinline__ void dkdv_p_ds(const f32x16 (&sacc)[2], const f32x16 (&dpacc)[2],
+                                          const float* s_lse, const float* s_delta, int hi,
+                                          float scale_log2, int qrel0, int krel, int qlim,
+                                          bf16x8 (&pb)[2][2], bf16x8 (&dsb)[2][2]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int qr = qb * 32 + g4 * 8 + hi * 4;  // tile rows qr..qr+3
+            const f32x4 L = *reinterpret_cast<const f32x4*>(s_lse + qr);
+            const f32x4 Dl = *reinterpret_cast<const f32x4*>(s_delta + qr);
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+                const int r = g4 * 4 + e;
+                float pv[2], dsv[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    float x = fast_exp2(sacc[qb][r + u] * scale_log2 - L[e + u] * kLog2e);
+                    if constexpr (MASK) {
+                        // qrel/krel: row and key relative to the key tile start;
+                        // visible iff key <= row (causal) and row < qlim
+                        const int qrel = qrel0 + qr + e + u;
+                        x = (krel <= qrel && qrel < qlim) ? x : 0.f;
+                    }
+                    pv[u] = x;
+                    dsv[u] = x * (dpacc[qb][r + u] - Dl[e + u]);
+                }
+                const bf16x2 pk = to_bf16x2(pv[0], pv[1]);
+                const bf16x2 dk2 = to_bf16x2(dsv[0], dsv[1]);
+                pb[qb][r >> 3][r & 7] = pk[0];
+                pb[qb][r >> 3][(r & 7) + 1] = pk[1];
+                dsb[qb][r >> 3][r & 7] = dk2[0];
+                dsb[qb][r >> 3][(r & 7) + 1] = dk2[1];
+            }
+        }
+    }
+}
+
 template <int HD>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
     constexpr int BQ = 64, WK = 32, BNK = 128;
     constexpr int NS = HD / 16, NDB = HD / 32;
     constexpr int TILE = BQ * HD * 2;
-    __shared__ __attribute__((aligned(16))) char smem[2][2][TILE];  // [buf][Q / dO]
+    __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [buf][Q / dO]
     __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];
     __shared__ __attribute__((aligned(16))) float s_delta[2][BQ];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hi = lane >> 5, l32 = lane & 31;
 
-    const int64_t nkt = (p.nk + BNK - 1) / BNK;
-    const int kvl = blockIdx.x % p.nkv;
-    const int64_t kt = nkt - 1 - (int64_t)(blockIdx.x / p.nkv);  // (any order works)
+    // heaviest first: key tile 0 sees every query tile when causal
+    const int hl = blockIdx.x % p.nh;
+    const int64_t kt = (int64_t)(blockIdx.x / p.nh);
     const int64_t j0 = kt * BNK;                  // first key of the workgroup
     const int64_t wj0 = j0 + wave * WK;           // first key of this wave
     const int64_t myk = wj0 + l32;                // this lane's key
-    const int64_t mykpos = p.k_pos0 + myk;
-    const int kvg = p.kv_base + kvl;              // global kv head
+    const int kvl = (p.h0 + hl) / p.group - p.kv_base;
 
-    // query heads of this chunk that read kv head kvg, ascending
-    int hb = kvg * p.group - p.h0, he = (kvg + 1) * p.group - p.h0;
-    hb = hb < 0 ? 0 : hb;
-    he = he > p.nh ? p.nh : he;
-
-    // K and V of this lane's key as B operands (rows past nk are zero)
     const uint16_t* kh = p.k + (int64_t)kvl * p.k_hs;
     const uint16_t* vh = p.v + (int64_t)kvl * p.v_hs;
     bf16x8 kf[NS], vf[NS];
@@ -69,75 +106,48 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
             vf[s] = bf16x8{};
         }
     }
-
     f32x16 dk[NDB], dv[NDB];
-    const bool carry_in = kvl == p.carry_kv_in && p.acc_in_k != nullptr;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
         dk[db] = f32x16{};
         dv[db] = f32x16{};
-        if (carry_in && myk < p.nk) {
-            const float* ak = p.acc_in_k + (int64_t)kvl * p.ain_hs + myk * p.ain_rs;
-            const float* av = p.acc_in_v + (int64_t)kvl * p.ain_hs + myk * p.ain_rs;
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(ak + db * 32 + g4 * 8 + hi * 4);
-                const f32x4 y = *reinterpret_cast<const f32x4*>(av + db * 32 + g4 * 8 + hi * 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    dk[db][g4 * 4 + e] = x[e];
-                    dv[db][g4 * 4 + e] = y[e];
-                }
-            }
-        }
     }
 
-    // query tiles: causal rows >= first key position of the workgroup
+    // query tiles: causal rows start at the workgroup's first key position
     const int64_t nqt = (p.nq + BQ - 1) / BQ;
     int64_t qt0 = 0;
     if (p.causal) {
         const int64_t first = p.k_pos0 + j0;
         qt0 = first >= p.nq ? nqt : first / BQ;
     }
-    const int64_t nqi = nqt - qt0;
-    const int64_t nsteps = (he > hb && j0 < p.nk) ? (int64_t)(he - hb) * nqi : 0;
+    const int64_t nsteps = j0 < p.nk ? nqt - qt0 : 0;
 
-    Tile64<HD> tq, tdo;
-    float lse_r = 0.f, dl_r = 0.f;
-    auto load_step = [&](int64_t n) {
-        const int hl = hb + (int)(n / nqi);
-        const int64_t i0 = (qt0 + n % nqi) * BQ;
-        const uint16_t* qb = p.q + (int64_t)hl * p.q_hs + i0 * p.q_rs;
-        const uint16_t* ob = p.dO + (int64_t)hl * p.do_hs + i0 * p.do_rs;
-        tq.load(qb, p.q_rs, p.nq - i0, tid);
-        tdo.load(ob, p.do_rs, p.nq - i0, tid);
-        if (tid < BQ) {
-            const int64_t row = i0 + tid;
-            lse_r = row < p.nq ? p.lse[(int64_t)(p.h0 + hl) * p.lse_hs + row] * kLog2e : INFINITY;
-            dl_r = row < p.nq ? p.delta[(int64_t)hl * p.delta_hs + row] : 0.f;
-        }
+    const uint16_t* qh = p.q + (int64_t)hl * p.q_hs;
+    const uint16_t* oh = p.dO + (int64_t)hl * p.do_hs;
+    const float* lseh = p.lse + (int64_t)(p.h0 + hl) * p.lse_hs;
+    const float* delh = p.delta + (int64_t)hl * p.delta_hs;
+    // one step = Q and dO rows [i0, i0 + 64) plus their LSE and Delta, loaded
+    // straight into LDS buffer b (waves 0/1 also fetch the 64 LSE / Delta)
+    auto issue_step = [&](int64_t n, int b) {
+        const int64_t i0 = (qt0 + n) * BQ;
+        direct_tile64<HD>(smem[b][0], qh + i0 * p.q_rs, p.q_rs, p.nq - i0, wave, lane);
+        direct_tile64<HD>(smem[b][1], oh + i0 * p.do_rs, p.do_rs, p.nq - i0, wave, lane);
+        if (wave == 0) direct_vec64(s_lse[b], lseh + i0, p.nq - i0, lane);
+        if (wave == 1) direct_vec64(s_delta[b], delh + i0, p.nq - i0, lane);
     };
-    auto store_step = [&](int buf) {
-        tq.store(smem[buf][0], tid);
-        tdo.store(smem[buf][1], tid);
-        if (tid < BQ) {
-            s_lse[buf][tid] = lse_r;
-            s_delta[buf][tid] = dl_r;
-        }
-    };
-    if (nsteps > 0) {
-        load_step(0);
-        store_step(0);
-    }
+    if (nsteps > 0) issue_step(0, 0);
+    wait_vm_loads();
     __syncthreads();
 
+    // positions relative to this wave's first key, in 32-bit
+    const int64_t wkpos = p.k_pos0 + wj0;
+    const int krel = l32;
     for (int64_t n = 0; n < nsteps; ++n) {
         const int buf = (int)(n & 1);
-        const bool more = n + 1 < nsteps;
-        if (more) load_step(n + 1);
-        const int64_t i0 = (qt0 + n % nqi) * BQ;
+        if (n + 1 < nsteps) issue_step(n + 1, buf ^ 1);
+        const int64_t i0 = (qt0 + n) * BQ;
         // a wave works on the tile only if some row sees one of its keys
-        const bool live = wj0 < p.nk && (!p.causal || i0 + BQ - 1 >= p.k_pos0 + wj0);
+        const bool live = wj0 < p.nk && (!p.causal || i0 + BQ - 1 >= wkpos);
         if (live) {
             const char* Qs = smem[buf][0];
             const char* Os = smem[buf][1];
@@ -152,40 +162,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
                     dpacc[qb] = mfma32(ao, vf[st], dpacc[qb]);
                 }
             }
-            const bool need_mask = (wj0 + WK > p.nk) || (i0 + BQ > p.nq) ||
-                                   (p.causal && i0 < p.k_pos0 + wj0 + WK - 1);
             bf16x8 pb[2][2], dsb[2][2];
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int qr = qb * 32 + g4 * 8 + hi * 4;  // rows qr..qr+3
-                    const f32x4 L = *reinterpret_cast<const f32x4*>(&s_lse[buf][qr]);
-                    const f32x4 Dl = *reinterpret_cast<const f32x4*>(&s_delta[buf][qr]);
-#pragma unroll
-                    for (int e = 0; e < 4; e += 2) {
-                        const int r = g4 * 4 + e;
-                        float pv[2], dsv[2];
-#pragma unroll
-                        for (int u = 0; u < 2; ++u) {
-                            float x = fast_exp2(sacc[qb][r + u] * p.scale_log2 - L[e + u]);
-                            if (need_mask) {
-                                const int64_t qrow = i0 + qr + e + u;
-                                const bool ok = myk < p.nk && qrow < p.nq &&
-                                                (!p.causal || mykpos <= qrow);
-                                x = ok ? x : 0.f;
-                            }
-                            pv[u] = x;
-                            dsv[u] = x * (dpacc[qb][r + u] - Dl[e + u]);
-                        }
-                        const bf16x2 pk = to_bf16x2(pv[0], pv[1]);
-                        const bf16x2 dk2 = to_bf16x2(dsv[0], dsv[1]);
-                        pb[qb][r >> 3][r & 7] = pk[0];
-                        pb[qb][r >> 3][(r & 7) + 1] = pk[1];
-                        dsb[qb][r >> 3][r & 7] = dk2[0];
-                        dsb[qb][r >> 3][(r & 7) + 1] = dk2[1];
-                    }
-                }
+            const bool edge_k = wj0 + WK > p.nk;
+            const bool edge_q = i0 + BQ > p.nq;
+            const bool diag = p.causal && i0 < wkpos + WK - 1;
+            if (edge_k || edge_q || diag) {
+                // rows relative to the wave's first key; keys past nk and rows
+                // past nq are invisible; non-causal sees every row
+                const int qrel0 = (int)(p.causal ? i0 - wkpos : WK + i0);
+                const int qlim = (int)(p.causal ? p.nq - wkpos : WK + p.nq);
+                const int kr = (myk < p.nk) ? krel : (1 << 30);
+                dkdv_p_ds<true>(sacc, dpacc, s_lse[buf], s_delta[buf], hi, p.scale_log2, qrel0,
+                                kr, qlim, pb, dsb);
+            } else {
+                dkdv_p_ds<false>(sacc, dpacc, s_lse[buf], s_delta[buf], hi, p.scale_log2, 0, 0, 0,
+                                 pb, dsb);
             }
             // dV^T += dO^T P and dK^T += Q^T dS, reduction over the 64 query rows
 #pragma unroll
@@ -202,42 +193,94 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
                 }
             }
         }
-        if (more) store_step(buf ^ 1);
+        wait_vm_loads();
         __syncthreads();
     }
 
     if (myk >= p.nk) return;
-    if (kvl == p.carry_kv_out && p.acc_out_k != nullptr) {
-        float* ak = p.acc_out_k + (int64_t)kvl * p.aout_hs + myk * p.aout_rs;
-        float* av = p.acc_out_v + (int64_t)kvl * p.aout_hs + myk * p.aout_rs;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                f32x4 x, y;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[e] = dk[db][g4 * 4 + e];
-                    y[e] = dv[db][g4 * 4 + e];
-                }
-                *reinterpret_cast<f32x4*>(ak + db * 32 + g4 * 8 + hi * 4) = x;
-                *reinterpret_cast<f32x4*>(av + db * 32 + g4 * 8 + hi * 4) = y;
-            }
-        }
-        return;
-    }
-    uint16_t* okp = p.dk + (int64_t)kvl * p.dk_hs + myk * p.dk_rs;
-    uint16_t* ovp = p.dv + (int64_t)kvl * p.dk_hs + myk * p.dk_rs;
+    float* ak = p.part_k + ((int64_t)hl * p.nk + myk) * HD;
+    float* av = p.part_v + ((int64_t)hl * p.nk + myk) * HD;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-            const bf16x2 a0 = to_bf16x2(dk[db][g4 * 4 + 0] * p.scale, dk[db][g4 * 4 + 1] * p.scale);
-            const bf16x2 a1 = to_bf16x2(dk[db][g4 * 4 + 2] * p.scale, dk[db][g4 * 4 + 3] * p.scale);
-            const bf16x2 b0 = to_bf16x2(dv[db][g4 * 4 + 0], dv[db][g4 * 4 + 1]);
-            const bf16x2 b1 = to_bf16x2(dv[db][g4 * 4 + 2], dv[db][g4 * 4 + 3]);
-            *reinterpret_cast<bf16x4*>(okp + db * 32 + g4 * 8 + hi * 4) = bf16x4{a0[0], a0[1], a1[0], a1[1]};
-            *reinterpret_cast<bf16x4*>(ovp + db * 32 + g4 * 8 + hi * 4) = bf16x4{b0[0], b0[1], b1[0], b1[1]};
+            f32x4 x, y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[e] = dk[db][g4 * 4 + e];
+                y[e] = dv[db][g4 * 4 + e];
+            }
+            *reinterpret_cast<f32x4*>(ak + db * 32 + g4 * 8 + hi * 4) = x;
+            *reinterpret_cast<f32x4*>(av + db * 32 + g4 * 8 + hi * 4) = y;
+        }
+    }
+}
+
+// One thread per 4 consecutive fp32 of a (kv head, key) row.
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(DkdvReduceParams p) {
+    const int cpr = p.D / 4;
+    const int64_t total = (int64_t)p.nkv * p.nk * cpr;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int c = (int)(idx % cpr);
+        const int64_t kr = idx / cpr;
+        const int64_t key = kr % p.nk;
+        const int kvl = (int)(kr / p.nk);
+        const int kvg = p.kv_base + kvl;
+        int hb = kvg * p.group - p.h0, he = (kvg + 1) * p.group - p.h0;
+        hb = hb < 0 ? 0 : hb;
+        he = he > p.nh ? p.nh : he;
+        f32x4 ak = {0.f, 0.f, 0.f, 0.f}, av = {0.f, 0.f, 0.f, 0.f};
+        if (kvl == p.carry_kv_in) {
+            ak = *reinterpret_cast<const f32x4*>(p.carry_in_k + key * p.D + c * 4);
+            av = *reinterpret_cast<const f32x4*>(p.carry_in_v + key * p.D + c * 4);
+        }
+        for (int h = hb; h < he; ++h) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(p.part_k + ((int64_t)h * p.nk + key) * p.D + c * 4);
+            const f32x4 y = *reinterpret_cast<const f32x4*>(p.part_v + ((int64_t)h * p.nk + key) * p.D + c * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ak[e] = ak[e] + x[e];
+                av[e] = av[e] + y[e];
+            }
+        }
+        if (kvl == p.carry_kv_out) {
+            *reinterpret_cast<f32x4*>(p.carry_out_k + key * p.D + c * 4) = ak;
+            *reinterpret_cast<f32x4*>(p.carry_out_v + key * p.D + c * 4) = av;
+        } else {
+            const bf16x2 k0 = to_bf16x2(ak[0] * p.scale, ak[1] * p.scale);
+            const bf16x2 k1 = to_bf16x2(ak[2] * p.scale, ak[3] * p.scale);
+            const bf16x2 v0 = to_bf16x2(av[0], av[1]), v1 = to_bf16x2(av[2], av[3]);
+            const int64_t o = (int64_t)kvl * p.dk_hs + key * p.dk_rs + c * 4;
+            *reinterpret_cast<bf16x4*>(p.dk + o) = bf16x4{k0[0], k0[1], k1[0], k1[1]};
+            *reinterpret_cast<bf16x4*>(p.dv + o) = bf16x4{v0[0], v0[1], v1[0], v1[1]};
+        }
+    }
+}
+
+// dS^T of one 64-key tile for this lane's query row as bf16 MFMA operands.
+// MASK adds the causal / ragged test with keys relative to the tile.
+template <bool MASK>
+__device__ __forceinline__ void dq_ds(const f32x16 (&s)[2], const f32x16 (&dp)[2], float scale_log2,
+                                      float lse2, float dlt, int hi, int qrel, int klim,
+                                      bf16x8 (&dsb)[2][2]) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            float dsv[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                float x = fast_exp2(s[b][r + u] * scale_log2 - lse2);
+                if constexpr (MASK) {
+                    const int key = b * 32 + ((r + u) >> 2) * 8 + hi * 4 + ((r + u) & 3);
+                    x = (key <= qrel && key < klim) ? x : 0.f;
+                }
+                dsv[u] = x * (dp[b][r + u] - dlt);
+            }
+            const bf16x2 d2 = to_bf16x2(dsv[0], dsv[1]);
+            dsb[b][r >> 3][r & 7] = d2[0];
+            dsb[b][r >> 3][(r & 7) + 1] = d2[1];
         }
     }
 }
@@ -247,7 +290,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(DqParams p) {
     constexpr int BN = 64, WQ = 32, BM = 128;
     constexpr int NS = HD / 16, NDB = HD / 32;
     constexpr int TILE = BN * HD * 2;
-    __shared__ __attribute__((aligned(16))) char smem[2][2][TILE];  // [buf][K / V]
+    __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [buf][K / V]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hi = lane >> 5, l32 = lane & 31;
@@ -306,22 +349,20 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(DqParams p) {
     const int ntiles = kend > 0 ? (int)((kend + BN - 1) / BN) : 0;
     const int ntiles_w = kend_w > 0 ? (int)((kend_w + BN - 1) / BN) : 0;
 
-    Tile64<HD> tk, tv;
     if (ntiles > 0) {
-        tk.load(kh, p.k_rs, p.nk, tid);
-        tv.load(vh, p.v_rs, p.nk, tid);
-        tk.store(smem[0][0], tid);
-        tv.store(smem[0][1], tid);
+        direct_tile64<HD>(smem[0][0], kh, p.k_rs, p.nk, wave, lane);
+        direct_tile64<HD>(smem[0][1], vh, p.v_rs, p.nk, wave, lane);
     }
+    wait_vm_loads();
     __syncthreads();
 
+    const int64_t qrel_base = myq - p.k_pos0;  // query position relative to key 0
     for (int j = 0; j < ntiles; ++j) {
         const int buf = j & 1;
-        const bool more = j + 1 < ntiles;
-        if (more) {
+        if (j + 1 < ntiles) {
             const int64_t nb = (int64_t)(j + 1) * BN;
-            tk.load(kh + nb * p.k_rs, p.k_rs, p.nk - nb, tid);
-            tv.load(vh + nb * p.v_rs, p.v_rs, p.nk - nb, tid);
+            direct_tile64<HD>(smem[buf ^ 1][0], kh + nb * p.k_rs, p.k_rs, p.nk - nb, wave, lane);
+            direct_tile64<HD>(smem[buf ^ 1][1], vh + nb * p.v_rs, p.v_rs, p.nk - nb, wave, lane);
         }
         if (j < ntiles_w) {
             const char* Ks = smem[buf][0];
@@ -340,25 +381,11 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(DqParams p) {
             const int64_t kb = (int64_t)j * BN;
             const bool need_mask = (kb + BN > p.nk) || (p.causal && p.k_pos0 + kb + BN - 1 > wq0);
             bf16x8 dsb[2][2];
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    float dsv[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        float x = fast_exp2(s[b][r + u] * p.scale_log2 - lse2);
-                        if (need_mask) {
-                            const int64_t key = kb + b * 32 + ((r + u) >> 2) * 8 + hi * 4 + ((r + u) & 3);
-                            const bool ok = key < p.nk && (!p.causal || p.k_pos0 + key <= myq);
-                            x = ok ? x : 0.f;
-                        }
-                        dsv[u] = x * (dp[b][r + u] - dlt);
-                    }
-                    const bf16x2 d2 = to_bf16x2(dsv[0], dsv[1]);
-                    dsb[b][r >> 3][r & 7] = d2[0];
-                    dsb[b][r >> 3][(r & 7) + 1] = d2[1];
-                }
+            if (need_mask) {
+                const int64_t qr = p.causal ? qrel_base - kb : (int64_t)BN;
+                dq_ds<true>(s, dp, p.scale_log2, lse2, dlt, hi, (int)qr, (int)(p.nk - kb), dsb);
+            } else {
+                dq_ds<false>(s, dp, p.scale_log2, lse2, dlt, hi, 0, 0, dsb);
             }
             // dQ^T += K^T dS^T over the tile's 64 keys
 #pragma unroll
@@ -373,10 +400,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(DqParams p) {
                 }
             }
         }
-        if (more) {
-            tk.store(smem[buf ^ 1][0], tid);
-            tv.store(smem[buf ^ 1][1], tid);
-        }
+        wait_vm_loads();
         __syncthreads();
     }
 
@@ -408,8 +432,8 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(DqParams p) {
 }
 
 hipError_t launch_dkdv(const DkdvParams& p, int D, hipStream_t st) {
-    if (p.nk <= 0 || p.nkv <= 0) return hipSuccess;
-    const int64_t blocks = (p.nk + kDkdvBlockN - 1) / kDkdvBlockN * p.nkv;
+    if (p.nk <= 0 || p.nh <= 0) return hipSuccess;
+    const int64_t blocks = (p.nk + kDkdvBlockN - 1) / kDkdvBlockN * p.nh;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (D == 128)
         hipLaunchKernelGGL(dkdv_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, st, p);
@@ -417,6 +441,14 @@ hipError_t launch_dkdv(const DkdvParams& p, int D, hipStream_t st) {
         hipLaunchKernelGGL(dkdv_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, st, p);
     else
         return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_dkdv_reduce(const DkdvReduceParams& p, hipStream_t st) {
+    if (p.nk <= 0 || p.nkv <= 0) return hipSuccess;
+    int64_t b = ((int64_t)p.nkv * p.nk * (p.D / 4) + 255) / 256;
+    b = b > 65536 ? 65536 : b;
+    hipLaunchKernelGGL(dkdv_reduce_kernel, dim3((unsigned)b), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

@@ -11,10 +11,14 @@
 // straight from a row-major tile.
 //
 // LDS tiles are row-major [rows][HD] bf16 with the 16-byte chunks of each row
-// XOR-swizzled by swz(row) = 2 * (row % 4) + (row / 4) % 2, which keeps both
-// access patterns free of bank conflicts: 16-byte reads of one chunk column
-// from 8 consecutive rows hit 8 different chunk slots, and the transposed
-// reads (4 rows x 32 bytes per 16 lanes) hit 8 different chunk slots too.
+// XOR-swizzled.  For HD = 128 (16 chunks per row) swz(row) = 4 * (row % 4) +
+// (row / 4) % 4: 16 consecutive rows read at one chunk column land in 16
+// different chunk slots (16-byte reads), and the 4 rows x 64 bytes that 32
+// lanes touch in a transposed read land in 16 different slots; row-major
+// 16-byte writes of whole rows are conflict-free too.  (Checked with the
+// SQ_LDS_BANK_CONFLICT counter on gfx950: zero conflicts for all three
+// patterns, where a row % 8 XOR conflicts on the transposed reads.)  HD = 64
+// (8 chunks per row) uses 4 * (row % 2) + (row / 2) % 4.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,12 +37,16 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309f;
 
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+template <int HD>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (HD == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return ((row & 1) << 2) | ((row >> 1) & 3);
+}
 
 // byte offset of element (row, col) in a swizzled [rows][HD] bf16 LDS tile
 template <int HD>
 __device__ __forceinline__ int lds_off(int row, int col) {
-    return row * (HD * 2) + ((((col >> 3) ^ swz(row))) << 4) + ((col & 7) << 1);
+    return row * (HD * 2) + ((((col >> 3) ^ swz<HD>(row))) << 4) + ((col & 7) << 1);
 }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -84,6 +92,43 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ bf16x2 to_bf16x2(float a, float b) {
     f32x2 f = {a, b};
     return __builtin_convertvector(f, bf16x2);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait until every vector-memory load of this wave has landed (including the
+// direct global -> LDS loads below, which do not pass through registers).
+__device__ __forceinline__ void wait_vm_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 64-row x HD-column bf16 tile loaded straight from global memory into the
+// swizzled LDS layout with global_load_lds_dwordx4: lane l of a wave writes
+// LDS bytes base + 16 l, so each lane fetches the global chunk that the
+// swizzle maps there.  4 waves share the tile (16 rows each).  Rows at or past
+// nvalid (>= 1) re-read row nvalid - 1: finite values that the kernels mask.
+template <int HD>
+__device__ __forceinline__ void direct_tile64(char* lds_tile, const uint16_t* base, int64_t rs,
+                                              int64_t nvalid, int wave, int lane) {
+    constexpr int ROWB = HD * 2;          // bytes per row
+    constexpr int CPR = ROWB / 16;        // chunks per row
+    constexpr int RPI = 1024 / ROWB;      // rows per wave instruction
+    constexpr int NI = 64 / (4 * RPI);    // instructions per wave
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int blk = wave * NI + i;
+        const int row = blk * RPI + lane / CPR;
+        const int lc = (lane % CPR) ^ swz<HD>(row);
+        const int64_t srow = row < nvalid ? row : nvalid - 1;
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(base + srow * rs + lc * 8),
+                                         (lds_void*)(lds_tile + blk * 1024), 16, 0, 0);
+    }
+}
+
+// 64 consecutive fp32 (one per lane of one wave) straight into LDS; entries at
+// or past nvalid (>= 1) repeat entry nvalid - 1.
+__device__ __forceinline__ void direct_vec64(float* lds_vec, const float* src, int64_t nvalid, int lane) {
+    const int64_t i = lane < nvalid ? lane : nvalid - 1;
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + i),
+                                     (lds_void*)(lds_vec), 4, 0, 0);
 }
 
 // 64-row x HD-column bf16 tile: global -> registers -> swizzled LDS, 256 threads.

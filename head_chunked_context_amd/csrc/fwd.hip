@@ -7,9 +7,9 @@
 // or before its own position (same section, auto-regressive paragraph).
 //
 // Workgroup = 4 waves x 32 query rows of one head (128 rows); the key loop
-// walks 64-key tiles of K and V staged through LDS (double-buffered, one
-// barrier per tile).  Per wave and tile, in the transposed form that keeps
-// one query row per lane pair:
+// walks 64-key tiles of K and V loaded straight from global memory into LDS
+// (global_load_lds, double-buffered, one barrier per tile).  Per wave and
+// tile, in the transposed form that keeps one query row per lane pair:
 //   S^T[key][q] = K Q^T          A = K tile (LDS, 16-byte reads), B = Q (regs)
 //   online softmax on S^T        lane l and l^32 share query l % 32
 //   O^T[d][q]  += V^T P^T        A = V tile (LDS transposed reads), B = P (regs)
@@ -22,13 +22,60 @@
 
 namespace hc {
 
+// Online-softmax update of one 64-key tile for this lane's query row.  The
+// scores s (S^T blocks, lane = query) are scaled to log2 units in place; MASK
+// adds the causal / ragged test with keys and rows relative to the tile.
+template <bool MASK>
+__device__ __forceinline__ void fwd_softmax(f32x16 (&s)[2], float scale_log2, int hi, int krel0,
+                                            int qrel, int klim, float& m, float& lpart,
+                                            float& alpha, bf16x8 (&pb)[2][2]) {
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float x = s[b][r] * scale_log2;
+            if constexpr (MASK) {
+                // key (relative to the tile) visible iff key <= query and key < klim
+                const int key = krel0 + b * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+                x = (key <= qrel && key < klim) ? x : -INFINITY;
+            }
+            s[b][r] = x;
+            rmax = fmaxf(rmax, x);
+        }
+    }
+    rmax = pair_max(rmax);
+    const float mnew = fmaxf(m, rmax);
+    const float msafe = mnew == -INFINITY ? 0.f : mnew;
+    alpha = fast_exp2(m - msafe);
+    m = mnew;
+    float psum = 0.f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const float p0 = fast_exp2(s[b][h2 * 8 + e] - msafe);
+                const float p1 = fast_exp2(s[b][h2 * 8 + e + 1] - msafe);
+                psum += p0;
+                psum += p1;
+                const bf16x2 pk = to_bf16x2(p0, p1);
+                pb[b][h2][e] = pk[0];
+                pb[b][h2][e + 1] = pk[1];
+            }
+        }
+    }
+    lpart = lpart * alpha + psum;
+}
+
 template <int HD>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     constexpr int BN = 64, WQ = 32, BM = 128;
     constexpr int NS = HD / 16;  // reduction steps of K Q^T
     constexpr int NDB = HD / 32; // 32-wide d blocks of O
     constexpr int TILE = BN * HD * 2;
-    __shared__ __attribute__((aligned(16))) char smem[2][2][TILE];
+    __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hi = lane >> 5, l32 = lane & 31;
@@ -75,23 +122,21 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
 
-    Tile64<HD> tk, tv;
     if (ntiles > 0) {
-        tk.load(kh, p.k_rs, p.nk, tid);
-        tv.load(vh, p.v_rs, p.nk, tid);
-        tk.store(smem[0][0], tid);
-        tv.store(smem[0][1], tid);
+        direct_tile64<HD>(smem[0][0], kh, p.k_rs, p.nk, wave, lane);
+        direct_tile64<HD>(smem[0][1], vh, p.v_rs, p.nk, wave, lane);
     }
+    wait_vm_loads();
     __syncthreads();
 
-    const int64_t qpos = p.q_pos0 + myq;
+    // this lane's query position relative to the key positions of tile 0
+    const int64_t qrel_base = p.q_pos0 + myq - p.k_pos0;
     for (int j = 0; j < ntiles; ++j) {
         const int buf = j & 1;
-        const bool more = j + 1 < ntiles;
-        if (more) {
+        if (j + 1 < ntiles) {
             const int64_t nb = (int64_t)(j + 1) * BN;
-            tk.load(kh + nb * p.k_rs, p.k_rs, p.nk - nb, tid);
-            tv.load(vh + nb * p.v_rs, p.v_rs, p.nk - nb, tid);
+            direct_tile64<HD>(smem[buf ^ 1][0], kh + nb * p.k_rs, p.k_rs, p.nk - nb, wave, lane);
+            direct_tile64<HD>(smem[buf ^ 1][1], vh + nb * p.v_rs, p.v_rs, p.nk - nb, wave, lane);
         }
         if (j < ntiles_w) {
             const char* Ks = smem[buf][0];
@@ -109,46 +154,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
             const int64_t kb = (int64_t)j * BN;
             const bool need_mask = (kb + BN > p.nk) ||
                                    (p.causal && p.k_pos0 + kb + BN - 1 > p.q_pos0 + wq0);
-            float rmax = -INFINITY;
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float x = s[b][r] * p.scale_log2;
-                    if (need_mask) {
-                        const int64_t key = kb + b * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-                        const bool ok = key < p.nk && (!p.causal || p.k_pos0 + key <= qpos);
-                        x = ok ? x : -INFINITY;
-                    }
-                    s[b][r] = x;
-                    rmax = fmaxf(rmax, x);
-                }
-            }
-            rmax = pair_max(rmax);
-            const float mnew = fmaxf(m, rmax);
-            const float msafe = mnew == -INFINITY ? 0.f : mnew;
-            const float alpha = fast_exp2(m - msafe);
-            m = mnew;
-            // P = exp2(s - m) in fp32 (row sum) and bf16 (MFMA operand)
+            float alpha;
             bf16x8 pb[2][2];
-            float psum = 0.f;
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2) {
-                        const float p0 = fast_exp2(s[b][h2 * 8 + e] - msafe);
-                        const float p1 = fast_exp2(s[b][h2 * 8 + e + 1] - msafe);
-                        psum += p0;
-                        psum += p1;
-                        bf16x2 pk = to_bf16x2(p0, p1);
-                        pb[b][h2][e] = pk[0];
-                        pb[b][h2][e + 1] = pk[1];
-                    }
-                }
+            if (need_mask) {
+                const int64_t qr = p.causal ? qrel_base - kb : (int64_t)BN;
+                fwd_softmax<true>(s, p.scale_log2, hi, 0, (int)qr, (int)(p.nk - kb), m, lpart,
+                                  alpha, pb);
+            } else {
+                fwd_softmax<false>(s, p.scale_log2, hi, 0, 0, 0, m, lpart, alpha, pb);
             }
-            lpart = lpart * alpha + psum;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) o[db] *= alpha;
             // O^T += V^T P^T: reduction over the tile's 64 keys in 4 steps of 16
@@ -164,10 +178,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
                 }
             }
         }
-        if (more) {
-            tk.store(smem[buf ^ 1][0], tid);
-            tv.store(smem[buf ^ 1][1], tid);
-        }
+        wait_vm_loads();
         __syncthreads();
     }
 

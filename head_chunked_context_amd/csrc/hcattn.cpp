@@ -22,6 +22,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "../../include/hcattn.h"
 #include "kernels.h"
@@ -192,11 +193,55 @@ int leave(Common& c) {
     return ATTN_OK;
 }
 
+// ------------------------------------------------------------ kernel timing
+
+enum Kid { K_FWD, K_MERGE, K_PACK, K_PREP, K_DKDV, K_REDUCE, K_DQ, K_COUNT };
+const char* const kKernelNames[K_COUNT] = {"fwd", "merge", "pack", "prep", "dkdv", "reduce", "dq"};
+
+struct TimingRec {
+    int kid;
+    hipEvent_t a, b;
+};
+std::atomic<int> g_timing{0};
+std::mutex g_tmu;
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t pool_event() {
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Launch through `launch` (returns hipError_t); when timing is on, bracket it
+// with events on stream st.
+template <class F>
+hipError_t timed(int kid, hipStream_t st, F&& launch) {
+    if (!g_timing.load()) return launch();
+    std::lock_guard<std::mutex> lk(g_tmu);
+    TimingRec r{kid, pool_event(), pool_event()};
+    if (r.a == nullptr || r.b == nullptr) return hipErrorOutOfMemory;
+    hipError_t e = hipEventRecord(r.a, st);
+    if (e != hipSuccess) return e;
+    e = launch();
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(r.b, st);
+    if (e != hipSuccess) return e;
+    g_recs.push_back(r);
+    return hipSuccess;
+}
+
 #define KCHK(expr)                                                                         \
     do {                                                                                   \
         hipError_t e_ = (expr);                                                            \
         if (e_ != hipSuccess) return fail(ATTN_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
     } while (0)
+#define LAUNCH(kid, call) KCHK(timed(kid, c.st, [&]() { return (call); }))
 
 // ------------------------------------------------------------------ forward
 
@@ -211,11 +256,11 @@ int fwd_untrunked(Common& c, const uint16_t* q, const uint16_t* k, const uint16_
     for (int ci = 0; ci < p.nchunks; ++ci) {
         const hc::Chunk ch = p.chunk(ci);
         hc::PackParams pk{q + (size_t)ch.h0 * D, (int64_t)p.Hq * D, D, Qc, D, S * D, ch.nh, S, D};
-        KCHK(hc::launch_pack(pk, c.st));
+        LAUNCH(K_PACK, hc::launch_pack(pk, c.st));
         pk = {k + (size_t)ch.kv0 * D, (int64_t)p.Hkv * D, D, Kc, D, S * D, ch.nkv, S, D};
-        KCHK(hc::launch_pack(pk, c.st));
+        LAUNCH(K_PACK, hc::launch_pack(pk, c.st));
         pk = {v + (size_t)ch.kv0 * D, (int64_t)p.Hkv * D, D, Vc, D, S * D, ch.nkv, S, D};
-        KCHK(hc::launch_pack(pk, c.st));
+        LAUNCH(K_PACK, hc::launch_pack(pk, c.st));
         hc::FwdParams f{};
         f.q = Qc; f.q_rs = D; f.q_hs = S * D;
         f.k = Kc; f.k_rs = D; f.k_hs = S * D;
@@ -225,7 +270,7 @@ int fwd_untrunked(Common& c, const uint16_t* q, const uint16_t* k, const uint16_
         f.nh = ch.nh; f.group = p.g; f.h0 = ch.h0; f.kv_base = ch.kv0;
         f.nq = S; f.q_pos0 = 0; f.nk = S; f.k_pos0 = 0;
         f.causal = p.causal; f.mode = hc::kFwdFinal; f.scale_log2 = c.scale_log2;
-        KCHK(hc::launch_fwd(f, D, c.st));
+        LAUNCH(K_FWD, hc::launch_fwd(f, D, c.st));
     }
     return ATTN_OK;
 }
@@ -246,7 +291,7 @@ int fwd_trunked(Common& c, const uint16_t* q, const void* k, const void* v, uint
             const int64_t qr0 = p.trunk_begin(m), nq = p.trunk_rows(m);
             hc::PackParams pk{q + ((size_t)qr0 * p.Hq + ch.h0) * D, (int64_t)p.Hq * D, D, Qm, D,
                               T * D, ch.nh, nq, D};
-            KCHK(hc::launch_pack(pk, c.st));
+            LAUNCH(K_PACK, hc::launch_pack(pk, c.st));
             const int64_t tlast = p.causal ? m : p.N - 1;
             for (int64_t t = 0; t <= tlast; ++t) {
                 int slot = 0;
@@ -270,7 +315,7 @@ int fwd_trunked(Common& c, const uint16_t* q, const void* k, const void* v, uint
                     f.o = t == 0 ? Orun : Ot; f.o_rs = D; f.o_hs = nq * D;
                     f.lse = t == 0 ? Lrun : Lt; f.lse_hs = nq;
                 }
-                KCHK(hc::launch_fwd(f, D, c.st));
+                LAUNCH(K_FWD, hc::launch_fwd(f, D, c.st));
                 r = ring.release(slot);
                 if (r) return r;
                 if (t > 0) {
@@ -281,7 +326,7 @@ int fwd_trunked(Common& c, const uint16_t* q, const void* k, const void* v, uint
                     mg.out = o + ((size_t)qr0 * p.Hq + ch.h0) * D; mg.out_rs = (int64_t)p.Hq * D;
                     mg.out_hs = D;
                     mg.lse_out = lse + (size_t)ch.h0 * p.S + qr0; mg.lse_hs = p.S;
-                    KCHK(hc::launch_merge(mg, c.st));
+                    LAUNCH(K_MERGE, hc::launch_merge(mg, c.st));
                 }
             }
         }
@@ -300,8 +345,8 @@ struct BwdIO {
     bool kv_host;
 };
 
-// dK/dV kernel parameters for chunk ch over keys [kr0, kr0 + nk) held in (kk, vv)
-hc::DkdvParams dkdv_params(const Common& c, const hc::Chunk& ch, int ci, const BwdIO& io,
+// dK/dV partial kernel parameters for chunk ch over keys [kr0, kr0 + nk) held in (kk, vv)
+hc::DkdvParams dkdv_params(const Common& c, const hc::Chunk& ch, const BwdIO& io,
                            const uint16_t* kk, const uint16_t* vv, int64_t k_rs, int64_t k_hs,
                            int64_t kr0, int64_t nk) {
     const hc::Plan& p = c.pl;
@@ -312,25 +357,41 @@ hc::DkdvParams dkdv_params(const Common& c, const hc::Chunk& ch, int ci, const B
     d.lse = io.lse; d.lse_hs = p.S;
     d.delta = reinterpret_cast<const float*>(c.ws + p.delta_c); d.delta_hs = p.S;
     d.k = kk; d.v = vv; d.k_rs = d.v_rs = k_rs; d.k_hs = d.v_hs = k_hs;
-    d.nh = ch.nh; d.group = p.g; d.h0 = ch.h0; d.kv_base = ch.kv0; d.nkv = ch.nkv;
+    d.nh = ch.nh; d.group = p.g; d.h0 = ch.h0; d.kv_base = ch.kv0;
     d.nq = p.S; d.nk = nk; d.k_pos0 = kr0; d.causal = p.causal;
-    d.scale = c.scale; d.scale_log2 = c.scale_log2;
+    d.scale_log2 = c.scale_log2;
+    d.part_k = reinterpret_cast<float*>(c.ws + p.part_k);
+    d.part_v = reinterpret_cast<float*>(c.ws + p.part_v);
+    return d;
+}
+
+// Ordered head sum of the partials, with the fp32 carries of groups that span
+// chunks; final bf16 rows go to (dk, dv) with the given strides.
+hc::DkdvReduceParams reduce_params(const Common& c, const hc::Chunk& ch, int ci, int64_t kr0,
+                                   int64_t nk, uint16_t* dk, uint16_t* dv, int64_t rs, int64_t hs) {
+    const hc::Plan& p = c.pl;
+    const int D = p.D;
+    hc::DkdvReduceParams r{};
+    r.part_k = reinterpret_cast<const float*>(c.ws + p.part_k);
+    r.part_v = reinterpret_cast<const float*>(c.ws + p.part_v);
+    r.nh = ch.nh; r.group = p.g; r.h0 = ch.h0; r.kv_base = ch.kv0; r.nkv = ch.nkv;
+    r.nk = nk; r.D = D;
     const int in_s = p.carry_in_slot(ci), out_s = p.carry_out_slot(ci);
-    d.carry_kv_in = -1;
-    d.carry_kv_out = -1;
+    r.carry_kv_in = -1;
+    r.carry_kv_out = -1;
     if (in_s >= 0) {
-        d.acc_in_k = reinterpret_cast<const float*>(c.ws + p.carry_k[in_s]) + (size_t)kr0 * D;
-        d.acc_in_v = reinterpret_cast<const float*>(c.ws + p.carry_v[in_s]) + (size_t)kr0 * D;
-        d.ain_rs = D; d.ain_hs = 0;  // one kv head per slot
-        d.carry_kv_in = 0;
+        r.carry_in_k = reinterpret_cast<const float*>(c.ws + p.carry_k[in_s]) + (size_t)kr0 * D;
+        r.carry_in_v = reinterpret_cast<const float*>(c.ws + p.carry_v[in_s]) + (size_t)kr0 * D;
+        r.carry_kv_in = 0;
     }
     if (out_s >= 0) {
-        d.acc_out_k = reinterpret_cast<float*>(c.ws + p.carry_k[out_s]) + (size_t)kr0 * D;
-        d.acc_out_v = reinterpret_cast<float*>(c.ws + p.carry_v[out_s]) + (size_t)kr0 * D;
-        d.aout_rs = D; d.aout_hs = 0;
-        d.carry_kv_out = ch.nkv - 1;
+        r.carry_out_k = reinterpret_cast<float*>(c.ws + p.carry_k[out_s]) + (size_t)kr0 * D;
+        r.carry_out_v = reinterpret_cast<float*>(c.ws + p.carry_v[out_s]) + (size_t)kr0 * D;
+        r.carry_kv_out = ch.nkv - 1;
     }
-    return d;
+    r.dk = dk; r.dv = dv; r.dk_rs = rs; r.dk_hs = hs;
+    r.scale = c.scale;
+    return r;
 }
 
 int bwd_chunk_prep(Common& c, const hc::Chunk& ch, const BwdIO& io) {
@@ -339,14 +400,14 @@ int bwd_chunk_prep(Common& c, const hc::Chunk& ch, const BwdIO& io) {
     const int64_t S = p.S;
     uint16_t* Qc = reinterpret_cast<uint16_t*>(c.ws + p.q_c);
     hc::PackParams pk{io.q + (size_t)ch.h0 * D, (int64_t)p.Hq * D, D, Qc, D, S * D, ch.nh, S, D};
-    KCHK(hc::launch_pack(pk, c.st));
+    LAUNCH(K_PACK, hc::launch_pack(pk, c.st));
     hc::PrepParams pr{};
     pr.o = io.o + (size_t)ch.h0 * D; pr.o_rs = (int64_t)p.Hq * D; pr.o_hs = D;
     pr.dO = io.dout + (size_t)ch.h0 * D; pr.do_rs = (int64_t)p.Hq * D; pr.do_hs = D;
     pr.dO_c = reinterpret_cast<uint16_t*>(c.ws + p.do_c); pr.c_rs = D; pr.c_hs = S * D;
     pr.delta = reinterpret_cast<float*>(c.ws + p.delta_c); pr.delta_hs = S;
     pr.nh = ch.nh; pr.rows = S; pr.D = D;
-    KCHK(hc::launch_prep(pr, c.st));
+    LAUNCH(K_PREP, hc::launch_prep(pr, c.st));
     return ATTN_OK;
 }
 
@@ -382,16 +443,17 @@ int bwd_untrunked(Common& c, const BwdIO& io) {
         const uint16_t* k = static_cast<const uint16_t*>(io.k);
         const uint16_t* v = static_cast<const uint16_t*>(io.v);
         hc::PackParams pk{k + (size_t)ch.kv0 * D, (int64_t)p.Hkv * D, D, Kc, D, S * D, ch.nkv, S, D};
-        KCHK(hc::launch_pack(pk, c.st));
+        LAUNCH(K_PACK, hc::launch_pack(pk, c.st));
         pk = {v + (size_t)ch.kv0 * D, (int64_t)p.Hkv * D, D, Vc, D, S * D, ch.nkv, S, D};
-        KCHK(hc::launch_pack(pk, c.st));
-        hc::DkdvParams dk = dkdv_params(c, ch, ci, io, Kc, Vc, D, S * D, 0, S);
-        dk.dk = static_cast<uint16_t*>(io.dk) + (size_t)ch.kv0 * D;
-        dk.dv = static_cast<uint16_t*>(io.dv) + (size_t)ch.kv0 * D;
-        dk.dk_rs = (int64_t)p.Hkv * D; dk.dk_hs = D;
-        KCHK(hc::launch_dkdv(dk, D, c.st));
+        LAUNCH(K_PACK, hc::launch_pack(pk, c.st));
+        hc::DkdvParams dk = dkdv_params(c, ch, io, Kc, Vc, D, S * D, 0, S);
+        LAUNCH(K_DKDV, hc::launch_dkdv(dk, D, c.st));
+        hc::DkdvReduceParams rd = reduce_params(
+            c, ch, ci, 0, S, static_cast<uint16_t*>(io.dk) + (size_t)ch.kv0 * D,
+            static_cast<uint16_t*>(io.dv) + (size_t)ch.kv0 * D, (int64_t)p.Hkv * D, D);
+        LAUNCH(K_REDUCE, hc::launch_dkdv_reduce(rd, c.st));
         hc::DqParams dq = dq_params(c, ch, io, Kc, Vc, D, S * D, 0, S);
-        KCHK(hc::launch_dq(dq, D, c.st));
+        LAUNCH(K_DQ, hc::launch_dq(dq, D, c.st));
     }
     return ATTN_OK;
 }
@@ -416,28 +478,32 @@ int bwd_trunked(Common& c, const BwdIO& io) {
             if (r) return r;
             const uint16_t* kk = reinterpret_cast<const uint16_t*>(c.ws + p.ring_k[slot]);
             const uint16_t* vv = reinterpret_cast<const uint16_t*>(c.ws + p.ring_v[slot]);
-            hc::DkdvParams dk = dkdv_params(c, ch, ci, io, kk, vv, (int64_t)ch.nkv * D, D, kr0, nk);
+            hc::DkdvParams dk = dkdv_params(c, ch, io, kk, vv, (int64_t)ch.nkv * D, D, kr0, nk);
+            LAUNCH(K_DKDV, hc::launch_dkdv(dk, D, c.st));
             int ss = -1;
+            hc::DkdvReduceParams rd;
             if (io.kv_host) {
                 ss = nstage & 1;
                 Device* d = c.dev;
                 if (stage_uses[ss] > 0) HIPCHK(hipStreamWaitEvent(c.st, d->ev[EV_SFREE0 + ss], 0));
-                dk.dk = reinterpret_cast<uint16_t*>(c.ws + p.stage_k[ss]);
-                dk.dv = reinterpret_cast<uint16_t*>(c.ws + p.stage_v[ss]);
-                dk.dk_rs = (int64_t)ch.nkv * D; dk.dk_hs = D;
+                rd = reduce_params(c, ch, ci, kr0, nk, reinterpret_cast<uint16_t*>(c.ws + p.stage_k[ss]),
+                                   reinterpret_cast<uint16_t*>(c.ws + p.stage_v[ss]),
+                                   (int64_t)ch.nkv * D, D);
             } else {
-                dk.dk = static_cast<uint16_t*>(io.dk) + ((size_t)kr0 * p.Hkv + ch.kv0) * D;
-                dk.dv = static_cast<uint16_t*>(io.dv) + ((size_t)kr0 * p.Hkv + ch.kv0) * D;
-                dk.dk_rs = (int64_t)p.Hkv * D; dk.dk_hs = D;
+                rd = reduce_params(
+                    c, ch, ci, kr0, nk,
+                    static_cast<uint16_t*>(io.dk) + ((size_t)kr0 * p.Hkv + ch.kv0) * D,
+                    static_cast<uint16_t*>(io.dv) + ((size_t)kr0 * p.Hkv + ch.kv0) * D,
+                    (int64_t)p.Hkv * D, D);
             }
-            KCHK(hc::launch_dkdv(dk, D, c.st));
+            LAUNCH(K_REDUCE, hc::launch_dkdv_reduce(rd, c.st));
             hc::DqParams dq = dq_params(c, ch, io, kk, vv, (int64_t)ch.nkv * D, D, kr0, nk);
             dq.q_begin = p.causal ? kr0 : 0;
             dq.acc_in = t == 0 ? nullptr : dQacc;
             dq.ain_rs = D; dq.ain_hs = S * D;
             dq.acc_out = dQacc; dq.aout_rs = D; dq.aout_hs = S * D;
             dq.final_before = p.causal ? kr0 + nk : (t == p.N - 1 ? S : 0);
-            KCHK(hc::launch_dq(dq, D, c.st));
+            LAUNCH(K_DQ, hc::launch_dq(dq, D, c.st));
             r = ring.release(slot);
             if (r) return r;
             if (io.kv_host && nfin > 0) {
@@ -566,5 +632,38 @@ const char* attn_last_error(void) { return g_err; }
 int attn_set_single_stream(int on) { return g_single_stream.exchange(on ? 1 : 0); }
 
 const char* attn_version(void) { return "0.1.0"; }
+
+int attn_timing_enable(int on) { return g_timing.exchange(on ? 1 : 0); }
+
+void attn_timing_reset(void) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    for (const TimingRec& r : g_recs) {
+        (void)hipEventSynchronize(r.b);
+        g_pool.push_back(r.a);
+        g_pool.push_back(r.b);
+    }
+    g_recs.clear();
+}
+
+int attn_timing_read(const char* name, int64_t* launches, double* total_ms) {
+    int kid = -1;
+    for (int i = 0; i < K_COUNT; ++i)
+        if (name && std::strcmp(name, kKernelNames[i]) == 0) kid = i;
+    if (kid < 0) return fail(ATTN_EINVAL, "unknown kernel family '%s'", name ? name : "(null)");
+    std::lock_guard<std::mutex> lk(g_tmu);
+    int64_t n = 0;
+    double ms = 0.0;
+    for (const TimingRec& r : g_recs) {
+        if (r.kid != kid) continue;
+        HIPCHK(hipEventSynchronize(r.b));
+        float t = 0.f;
+        HIPCHK(hipEventElapsedTime(&t, r.a, r.b));
+        ms += t;
+        ++n;
+    }
+    if (launches) *launches = n;
+    if (total_ms) *total_ms = ms;
+    return ATTN_OK;
+}
 
 }  // extern "C"

@@ -69,31 +69,41 @@ struct PrepParams {
     int D;
 };
 
-// dK/dV of one chunk over a key range: one workgroup per (key tile, kv head).
-// For each kv head the chunk's query heads of its group are walked in
-// ascending order, each over its query tiles in ascending order.
+// dK/dV partials of one chunk over a key range: one workgroup per (key tile
+// of 128 keys, query head of the chunk).  Each head's contribution over its
+// query tiles (ascending) is written in fp32, unscaled, to part_k/part_v
+// [nh][nk][D]; dkdv_reduce then adds the heads of each group in ascending
+// order.  Rows of part_* are keys of this launch (0..nk).
 struct DkdvParams {
     const uint16_t* q;  int64_t q_rs, q_hs;    // chunk query heads (local 0..nh)
     const uint16_t* dO; int64_t do_rs, do_hs;
-    const float* lse;   int64_t lse_hs;        // natural LSE, [head][row]
-    const float* delta; int64_t delta_hs;
+    const float* lse;   int64_t lse_hs;        // natural LSE, [global head][row]
+    const float* delta; int64_t delta_hs;      // [local head][row]
     const uint16_t* k;  int64_t k_rs, k_hs;    // kv heads (local 0..nkv)
     const uint16_t* v;  int64_t v_rs, v_hs;
-    int nh, group, h0, kv_base, nkv;
+    int nh, group, h0, kv_base;
     int64_t nq;                                // query rows (positions 0..nq)
     int64_t nk, k_pos0;                        // keys of this launch, position of key 0
     int causal;
-    float scale;                               // softmax scale
     float scale_log2;
-    // accumulator in/out: fp32 carry [kv][row][D] (row = key index in launch)
-    const float* acc_in_k; const float* acc_in_v; int64_t ain_rs, ain_hs;  // null = start at 0
-    int carry_kv_in;    // local kv index whose accumulator comes from acc_in (-1 none)
-    float* acc_out_k; float* acc_out_v; int64_t aout_rs, aout_hs;
-    int carry_kv_out;   // local kv index that writes fp32 to acc_out (-1 none)
-    uint16_t* dk; uint16_t* dv; int64_t dk_rs, dk_hs;   // final bf16 output for the others
+    float* part_k; float* part_v;              // [nh][nk][D] fp32
 };
-// acc_in/acc_out rows are indexed by key within this launch (0..nk); dk/dv
-// rows likewise.
+
+// Ordered sum over a group's heads: for each kv head of the chunk and key,
+//   acc = (carry_in or 0) + part[h_first] + part[h_first+1] + ...  (ascending)
+// then either acc -> carry_out (fp32, group continues in the next chunk) or
+// bf16(acc * scale) -> dk and bf16(acc) -> dv.  Carries are [nk][D] fp32 of
+// one kv head: carry_kv_in / carry_kv_out name the local kv head (-1 none).
+struct DkdvReduceParams {
+    const float* part_k; const float* part_v;
+    int nh, group, h0, kv_base, nkv;
+    int64_t nk;
+    int D;
+    const float* carry_in_k; const float* carry_in_v; int carry_kv_in;
+    float* carry_out_k; float* carry_out_v; int carry_kv_out;
+    uint16_t* dk; uint16_t* dv; int64_t dk_rs, dk_hs;
+    float scale;
+};
 
 // dQ of one chunk over a key range: one workgroup per (query tile, head).
 struct DqParams {
@@ -120,6 +130,7 @@ hipError_t launch_pack(const PackParams& p, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, hipStream_t st);
 hipError_t launch_prep(const PrepParams& p, hipStream_t st);
 hipError_t launch_dkdv(const DkdvParams& p, int D, hipStream_t st);
+hipError_t launch_dkdv_reduce(const DkdvReduceParams& p, hipStream_t st);
 hipError_t launch_dq(const DqParams& p, int D, hipStream_t st);
 
 // Tile sizes the host planner relies on (query rows per forward/dQ workgroup,

@@ -53,6 +53,13 @@ def lib():
     L.attn_set_single_stream.restype = ctypes.c_int
     L.attn_version.argtypes = []
     L.attn_version.restype = ctypes.c_char_p
+    L.attn_timing_enable.argtypes = [ctypes.c_int]
+    L.attn_timing_enable.restype = ctypes.c_int
+    L.attn_timing_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
+                                   ctypes.POINTER(ctypes.c_double)]
+    L.attn_timing_read.restype = ctypes.c_int
+    L.attn_timing_reset.argtypes = []
+    L.attn_timing_reset.restype = None
     _lib = L
     return L
 
@@ -160,3 +167,25 @@ def set_single_stream(on: bool) -> bool:
 
 def version() -> str:
     return lib().attn_version().decode()
+
+
+KERNEL_FAMILIES = ("fwd", "merge", "pack", "prep", "dkdv", "reduce", "dq")
+
+
+def timing_enable(on: bool) -> bool:
+    """Bracket every library kernel launch with HIP events (measurement only)."""
+    return bool(lib().attn_timing_enable(int(on)))
+
+
+def timing_reset() -> None:
+    lib().attn_timing_reset()
+
+
+def timing_read() -> dict:
+    """{family: (launches, total_ms)} for the launches since the last reset."""
+    out = {}
+    for name in KERNEL_FAMILIES:
+        n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
+        _check(lib().attn_timing_read(name.encode(), ctypes.byref(n), ctypes.byref(ms)))
+        out[name] = (int(n.value), float(ms.value))
+    return out

@@ -135,6 +135,20 @@ const char* attn_last_error(void);
  */
 int attn_set_single_stream(int on);
 
+/*
+ * Kernel timing for measurement tools.  While enabled, every kernel the
+ * library launches is bracketed by two HIP timing events recorded on the
+ * stream it runs on (the caller's stream); attn_timing_read waits for those
+ * events and returns, for the kernel family `name` ("fwd", "merge", "pack",
+ * "prep", "dkdv", "reduce", "dq"), the number of launches and their summed
+ * duration in milliseconds since the last reset.  Events come from a pool the library
+ * keeps until unload.  attn_timing_enable returns the previous setting;
+ * attn_timing_read returns ATTN_OK or ATTN_EINVAL (unknown name) or ATTN_EHIP.
+ */
+int attn_timing_enable(int on);
+int attn_timing_read(const char* name, int64_t* launches, double* total_ms);
+void attn_timing_reset(void);
+
 /* Library version, "major.minor.patch". */
 const char* attn_version(void);
 
