@@ -79,6 +79,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
     constexpr int NS = HD / 16, NDB = HD / 32;
     constexpr int TILE = BQ * HD * 2;
     __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [buf][Q / dO]
+    __shared__ __attribute__((aligned(1024))) char skv[2][2 * TILE];  // this tile's K, V
     __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];
     __shared__ __attribute__((aligned(16))) float s_delta[2][BQ];
 
@@ -93,18 +94,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
     const int64_t myk = wj0 + l32;                // this lane's key
     const int kvl = (p.h0 + hl) / p.group - p.kv_base;
 
-    const uint16_t* kh = p.k + (int64_t)kvl * p.k_hs;
-    const uint16_t* vh = p.v + (int64_t)kvl * p.v_hs;
-    bf16x8 kf[NS], vf[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        if (myk < p.nk) {
-            kf[s] = *reinterpret_cast<const bf16x8*>(kh + myk * p.k_rs + s * 16 + hi * 8);
-            vf[s] = *reinterpret_cast<const bf16x8*>(vh + myk * p.v_rs + s * 16 + hi * 8);
-        } else {
-            kf[s] = bf16x8{};
-            vf[s] = bf16x8{};
-        }
+    // the workgroup's 128 keys of K and V stay in LDS (rows past nk repeat the
+    // last key; their P is masked to zero); each step re-reads this wave's
+    // 32 keys as MFMA operands, which keeps register pressure low
+    const uint16_t* kh = p.k + (int64_t)kvl * p.k_hs + j0 * p.k_rs;
+    const uint16_t* vh = p.v + (int64_t)kvl * p.v_hs + j0 * p.v_rs;
+    if (j0 < p.nk) {
+        const int64_t nv = p.nk - j0;
+        direct_tile64<HD>(skv[0], kh, p.k_rs, nv, wave, lane);
+        direct_tile64<HD>(skv[0] + TILE, kh + 64 * p.k_rs, p.k_rs, nv > 64 ? nv - 64 : 1, wave, lane);
+        direct_tile64<HD>(skv[1], vh, p.v_rs, nv, wave, lane);
+        direct_tile64<HD>(skv[1] + TILE, vh + 64 * p.v_rs, p.v_rs, nv > 64 ? nv - 64 : 1, wave, lane);
     }
     f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -151,15 +151,19 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
         if (live) {
             const char* Qs = smem[buf][0];
             const char* Os = smem[buf][1];
-            f32x16 sacc[2] = {f32x16{}, f32x16{}}, dpacc[2] = {f32x16{}, f32x16{}};
+            f32x16 sacc[2], dpacc[2];
 #pragma unroll
             for (int st = 0; st < NS; ++st) {
+                const int ko = lds_off<HD>(wave * 32 + l32, st * 16 + hi * 8);
+                const bf16x8 kf = lds_read_b128(skv[0], ko);
+                const bf16x8 vf = lds_read_b128(skv[1], ko);
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
-                    bf16x8 aq = lds_read_b128(Qs, lds_off<HD>(qb * 32 + l32, st * 16 + hi * 8));
-                    sacc[qb] = mfma32(aq, kf[st], sacc[qb]);
-                    bf16x8 ao = lds_read_b128(Os, lds_off<HD>(qb * 32 + l32, st * 16 + hi * 8));
-                    dpacc[qb] = mfma32(ao, vf[st], dpacc[qb]);
+                    const int qo = lds_off<HD>(qb * 32 + l32, st * 16 + hi * 8);
+                    const bf16x8 aq = lds_read_b128(Qs, qo);
+                    const bf16x8 ao = lds_read_b128(Os, qo);
+                    sacc[qb] = mfma32(aq, kf, st == 0 ? f32x16{} : sacc[qb]);
+                    dpacc[qb] = mfma32(ao, vf, st == 0 ? f32x16{} : dpacc[qb]);
                 }
             }
             bf16x8 pb[2][2], dsb[2][2];
@@ -367,15 +371,16 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(DqParams p) {
         if (j < ntiles_w) {
             const char* Ks = smem[buf][0];
             const char* Vs = smem[buf][1];
-            f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+            f32x16 s[2], dp[2];
 #pragma unroll
             for (int st = 0; st < NS; ++st) {
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
-                    bf16x8 ak = lds_read_b128(Ks, lds_off<HD>(b * 32 + l32, st * 16 + hi * 8));
-                    s[b] = mfma32(ak, qf[st], s[b]);
-                    bf16x8 av = lds_read_b128(Vs, lds_off<HD>(b * 32 + l32, st * 16 + hi * 8));
-                    dp[b] = mfma32(av, df[st], dp[b]);
+                    const int o = lds_off<HD>(b * 32 + l32, st * 16 + hi * 8);
+                    const bf16x8 ak = lds_read_b128(Ks, o);
+                    const bf16x8 av = lds_read_b128(Vs, o);
+                    s[b] = mfma32(ak, qf[st], st == 0 ? f32x16{} : s[b]);
+                    dp[b] = mfma32(av, df[st], st == 0 ? f32x16{} : dp[b]);
                 }
             }
             const int64_t kb = (int64_t)j * BN;

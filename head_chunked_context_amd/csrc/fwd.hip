@@ -23,28 +23,32 @@
 namespace hc {
 
 // Online-softmax update of one 64-key tile for this lane's query row.  The
-// scores s (S^T blocks, lane = query) are scaled to log2 units in place; MASK
-// adds the causal / ragged test with keys and rows relative to the tile.
+// raw scores s (S^T blocks, lane = query) stay unscaled: the row maximum is
+// taken on them and the scale (softmax scale * log2 e) is folded into the
+// exponent, p = 2^(s * c - m) with m the running maximum in log2 units.  MASK
+// adds the causal / ragged test with keys relative to the tile.
 template <bool MASK>
-__device__ __forceinline__ void fwd_softmax(f32x16 (&s)[2], float scale_log2, int hi, int krel0,
-                                            int qrel, int klim, float& m, float& lpart,
-                                            float& alpha, bf16x8 (&pb)[2][2]) {
+__device__ __forceinline__ void fwd_softmax(f32x16 (&s)[2], float c, int hi, int qrel, int klim,
+                                            float& m, float& lpart, float& alpha,
+                                            bf16x8 (&pb)[2][2]) {
+    if constexpr (MASK) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                // key (relative to the tile) visible iff key <= query and key < klim
+                const int key = b * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+                s[b][r] = (key <= qrel && key < klim) ? s[b][r] : -INFINITY;
+            }
+        }
+    }
     float rmax = -INFINITY;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float x = s[b][r] * scale_log2;
-            if constexpr (MASK) {
-                // key (relative to the tile) visible iff key <= query and key < klim
-                const int key = krel0 + b * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-                x = (key <= qrel && key < klim) ? x : -INFINITY;
-            }
-            s[b][r] = x;
-            rmax = fmaxf(rmax, x);
-        }
+        for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[b][r]);
     }
-    rmax = pair_max(rmax);
+    rmax = pair_max(rmax) * c;
     const float mnew = fmaxf(m, rmax);
     const float msafe = mnew == -INFINITY ? 0.f : mnew;
     alpha = fast_exp2(m - msafe);
@@ -56,8 +60,8 @@ __device__ __forceinline__ void fwd_softmax(f32x16 (&s)[2], float scale_log2, in
         for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                const float p0 = fast_exp2(s[b][h2 * 8 + e] - msafe);
-                const float p1 = fast_exp2(s[b][h2 * 8 + e + 1] - msafe);
+                const float p0 = fast_exp2(__builtin_fmaf(s[b][h2 * 8 + e], c, -msafe));
+                const float p1 = fast_exp2(__builtin_fmaf(s[b][h2 * 8 + e + 1], c, -msafe));
                 psum += p0;
                 psum += p1;
                 const bf16x2 pk = to_bf16x2(p0, p1);
@@ -141,10 +145,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         if (j < ntiles_w) {
             const char* Ks = smem[buf][0];
             const char* Vs = smem[buf][1];
-            // S^T = K Q^T for two 32-key blocks
-            f32x16 s[2] = {f32x16{}, f32x16{}};
+            // S^T = K Q^T for two 32-key blocks (first step starts from zero)
+            f32x16 s[2];
 #pragma unroll
-            for (int st = 0; st < NS; ++st) {
+            for (int b = 0; b < 2; ++b)
+                s[b] = mfma32(lds_read_b128(Ks, lds_off<HD>(b * 32 + l32, hi * 8)), qf[0], f32x16{});
+#pragma unroll
+            for (int st = 1; st < NS; ++st) {
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
                     bf16x8 a = lds_read_b128(Ks, lds_off<HD>(b * 32 + l32, st * 16 + hi * 8));
@@ -158,13 +165,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
             bf16x8 pb[2][2];
             if (need_mask) {
                 const int64_t qr = p.causal ? qrel_base - kb : (int64_t)BN;
-                fwd_softmax<true>(s, p.scale_log2, hi, 0, (int)qr, (int)(p.nk - kb), m, lpart,
+                fwd_softmax<true>(s, p.scale_log2, hi, (int)qr, (int)(p.nk - kb), m, lpart,
                                   alpha, pb);
             } else {
-                fwd_softmax<false>(s, p.scale_log2, hi, 0, 0, 0, m, lpart, alpha, pb);
+                fwd_softmax<false>(s, p.scale_log2, hi, 0, 0, m, lpart, alpha, pb);
             }
+            // rescale O only when some row of the wave saw a new maximum
+            // (alpha is exactly 1 otherwise, so skipping changes no bits)
+            if (__any(alpha != 1.f)) {
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+                for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+            }
             // O^T += V^T P^T: reduction over the tile's 64 keys in 4 steps of 16
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
