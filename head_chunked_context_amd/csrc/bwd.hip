@@ -290,7 +290,7 @@ __device__ __forceinline__ void dq_ds(const f32x16 (&s)[2], const f32x16 (&dp)[2
 }
 
 template <int HD>
-__global__ __launch_bounds__(256, 1) void dq_kernel(DqParams p) {
+__global__ __launch_bounds__(256, 2) void dq_kernel(DqParams p) {
     constexpr int BN = 64, WQ = 32, BM = 128;
     constexpr int NS = HD / 16, NDB = HD / 32;
     constexpr int TILE = BN * HD * 2;
