@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=12288,
                     help="tokens of the CPU-oracle sample (one GQA group)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the steps, run one plain device-to-device copy of MIB MiB "
+                         "(the known-size reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -49,6 +52,42 @@ def algorithmic_flops(family: str, S: int, Hq: int, D: int, causal: bool) -> flo
     pairs = S * S / 2.0 if causal else float(S) * S
     per_pair = {"fwd": 4 * D, "dkdv": 8 * D, "dq": 6 * D}.get(family)
     return 0.0 if per_pair is None else per_pair * pairs * Hq
+
+
+# the sources each kernel family is compiled from (traffic figures taken with
+# the profiler are only used while these are unchanged)
+FAMILY_SOURCES = {"fwd": ["fwd.hip"], "dkdv": ["bwd.hip"], "dq": ["bwd.hip"]}
+COMMON_SOURCES = ["device_common.h", "kernels.h"]
+
+
+def kernel_source_hash(family: str) -> str:
+    import hashlib
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "head_chunked_context_amd",
+                        "csrc")
+    h = hashlib.sha256()
+    for name in FAMILY_SOURCES.get(family, []) + COMMON_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(family: str, shape: str, hc: int):
+    """HBM bytes per launch of `family` on this shape from the committed
+    counter summary (profiles/traffic_<family>_<shape>_hc<hc>.md, line
+    `traffic_json: {...}`), or None when there is none or the kernel's sources
+    changed since the counters were taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"traffic_{family}_{shape}_hc{hc}.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic_json:"):
+                rec = json.loads(line.split(":", 1)[1])
+                if rec.get("source_sha256") != kernel_source_hash(family):
+                    return None
+                return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    return None
 
 
 def cpu_oracle_baseline(D: int, g: int, tokens: int) -> dict:
@@ -112,6 +151,14 @@ def main():
 
     o, lse, dq, dk, dv = alloc_outputs()
     torch.cuda.synchronize()
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        a = torch.ones(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     def measure(hc_, steps, warmup, timing):
         fb = hcm.fwd_workspace_bytes(S, Hq, Hkv, D, causal, hc_, T)
@@ -175,7 +222,8 @@ def main():
         achieved = alg / (dom_ms / 1e3) / 1e12
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom, f"S{S}_Hq{Hq}_Hkv{Hkv}_D{D}", hc),
                 "launches": n_launch, "avg_launch_ms": round(dom_ms / n_launch, 4),
                 "flops_per_launch": alg / n_launch}
     else:
