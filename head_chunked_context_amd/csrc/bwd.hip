@@ -10,15 +10,19 @@
 // output tile, with fixed accumulation orders (dK/dV: the group's query heads
 // ascending, then query tiles ascending; dQ: key tiles ascending).
 //
-// dkdv_kernel: workgroup = 4 waves x 32 keys (128 keys) of one query head's kv
-// head.  K and V stay in registers as MFMA operands; each step loads a 64-row
-// query tile of Q and dO (plus LSE and Delta) straight into LDS,
-// double-buffered:
-//   S[q][key]   = Q K^T        A = Q tile (LDS),   B = K (regs)
-//   dP[q][key]  = dO V^T       A = dO tile (LDS),  B = V (regs)
-//   dV^T[d][key] += dO^T P     A = dO tile, transposed LDS reads
-//   dK^T[d][key] += Q^T dS     A = Q tile, transposed LDS reads
-// so each lane owns one key (lanes l and l^32 split the 64 query rows).
+// dkdv_kernel: workgroup = 8 waves on 128 keys of one query head's kv head;
+// K and V of the 128 keys sit in LDS for the whole kernel.  Each step loads a
+// 64-row query tile of Q and dO (plus LSE and Delta) straight into LDS,
+// double-buffered.  Waves w and w + 4 share keys 32 (w % 4) .. +31 and take
+// the lower / upper 32 rows of every tile:
+//   S[q][key]   = Q K^T        A = Q rows (LDS),   B = K (LDS)
+//   dP[q][key]  = dO V^T       A = dO rows (LDS),  B = V (LDS)
+//   dV^T[d][key] += dO^T P     A = dO rows, transposed LDS reads
+//   dK^T[d][key] += Q^T dS     A = Q rows, transposed LDS reads
+// so each lane owns one key (lanes l and l^32 split the wave's rows).  Two
+// waves per SIMD let one wave's softmax-side VALU work run under the other's
+// MFMAs.  At the end the upper-half wave hands its dK/dV partial to its
+// partner through LDS, which adds it after its own (fixed order).
 //
 // dq_kernel: workgroup = 4 waves x 32 query rows of one head; Q and dO stay in
 // registers; 64-key tiles of K and V are loaded straight into LDS like the
@@ -34,13 +38,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 // P and dS of one 64-row query tile against this lane's key, as bf16 MFMA
 // operands.  MASK adds the causal / ragged-edge test; the common interior
 // tiles skip it entirely.
-template <bool MASK>
-__device__ __forceinline__ void dkdv_p_ds(const f32x16 (&sacc)[2], const f32x16 (&dpacc)[2],
+template <int NQB, bool MASK>
+__device__ __forceinline__ void dkdv_p_ds(const f32x16 (&sacc)[NQB], const f32x16 (&dpacc)[NQB],
                                           const float* s_lse, const float* s_delta, int hi,
                                           float scale_log2, int qrel0, int krel, int qlim,
-                                          bf16x8 (&pb)[2][2], bf16x8 (&dsb)[2][2]) {
+                                          bf16x8 (&pb)[NQB][2], bf16x8 (&dsb)[NQB][2]) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             const int qr = qb * 32 + g4 * 8 + hi * 4;  // tile rows qr..qr+3
@@ -74,8 +78,8 @@ __device__ __forceinline__ void dkdv_p_ds(const f32x16 (&sacc)[2], const f32x16 
 }
 
 template <int HD>
-__global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
-    constexpr int BQ = 64, WK = 32, BNK = 128;
+__global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
+    constexpr int BQ = 64, WQ = 32, WK = 32, BNK = 128;
     constexpr int NS = HD / 16, NDB = HD / 32;
     constexpr int TILE = BQ * HD * 2;
     __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [buf][Q / dO]
@@ -85,26 +89,26 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hi = lane >> 5, l32 = lane & 31;
+    const int kw = wave & 3;   // key block of the wave (32 keys)
+    const int rh = wave >> 2;  // half of every 64-row query tile the wave takes
 
     // heaviest first: key tile 0 sees every query tile when causal
     const int hl = blockIdx.x % p.nh;
     const int64_t kt = (int64_t)(blockIdx.x / p.nh);
     const int64_t j0 = kt * BNK;                  // first key of the workgroup
-    const int64_t wj0 = j0 + wave * WK;           // first key of this wave
+    const int64_t wj0 = j0 + kw * WK;             // first key of this wave
     const int64_t myk = wj0 + l32;                // this lane's key
     const int kvl = (p.h0 + hl) / p.group - p.kv_base;
 
-    // the workgroup's 128 keys of K and V stay in LDS (rows past nk repeat the
-    // last key; their P is masked to zero); each step re-reads this wave's
-    // 32 keys as MFMA operands, which keeps register pressure low
-    const uint16_t* kh = p.k + (int64_t)kvl * p.k_hs + j0 * p.k_rs;
-    const uint16_t* vh = p.v + (int64_t)kvl * p.v_hs + j0 * p.v_rs;
+    // the workgroup's 128 keys of K (waves 0-3) and V (waves 4-7) go to LDS
+    // (rows past nk repeat the last key; their P is masked to zero)
     if (j0 < p.nk) {
         const int64_t nv = p.nk - j0;
-        direct_tile64<HD>(skv[0], kh, p.k_rs, nv, wave, lane);
-        direct_tile64<HD>(skv[0] + TILE, kh + 64 * p.k_rs, p.k_rs, nv > 64 ? nv - 64 : 1, wave, lane);
-        direct_tile64<HD>(skv[1], vh, p.v_rs, nv, wave, lane);
-        direct_tile64<HD>(skv[1] + TILE, vh + 64 * p.v_rs, p.v_rs, nv > 64 ? nv - 64 : 1, wave, lane);
+        const int64_t rs = rh == 0 ? p.k_rs : p.v_rs;
+        const uint16_t* src = rh == 0 ? p.k + (int64_t)kvl * p.k_hs + j0 * p.k_rs
+                                      : p.v + (int64_t)kvl * p.v_hs + j0 * p.v_rs;
+        direct_tile64<HD>(skv[rh], src, rs, nv, kw, lane);
+        direct_tile64<HD>(skv[rh] + TILE, src + 64 * rs, rs, nv > 64 ? nv - 64 : 1, kw, lane);
     }
     f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -126,14 +130,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
     const uint16_t* oh = p.dO + (int64_t)hl * p.do_hs;
     const float* lseh = p.lse + (int64_t)(p.h0 + hl) * p.lse_hs;
     const float* delh = p.delta + (int64_t)hl * p.delta_hs;
-    // one step = Q and dO rows [i0, i0 + 64) plus their LSE and Delta, loaded
-    // straight into LDS buffer b (waves 0/1 also fetch the 64 LSE / Delta)
+    // one step = Q (waves 0-3) and dO (waves 4-7) rows [i0, i0 + 64) plus
+    // their LSE (wave 0) and Delta (wave 4), straight into LDS buffer b
     auto issue_step = [&](int64_t n, int b) {
         const int64_t i0 = (qt0 + n) * BQ;
-        direct_tile64<HD>(smem[b][0], qh + i0 * p.q_rs, p.q_rs, p.nq - i0, wave, lane);
-        direct_tile64<HD>(smem[b][1], oh + i0 * p.do_rs, p.do_rs, p.nq - i0, wave, lane);
+        if (rh == 0)
+            direct_tile64<HD>(smem[b][0], qh + i0 * p.q_rs, p.q_rs, p.nq - i0, kw, lane);
+        else
+            direct_tile64<HD>(smem[b][1], oh + i0 * p.do_rs, p.do_rs, p.nq - i0, kw, lane);
         if (wave == 0) direct_vec64(s_lse[b], lseh + i0, p.nq - i0, lane);
-        if (wave == 1) direct_vec64(s_delta[b], delh + i0, p.nq - i0, lane);
+        if (wave == 4) direct_vec64(s_delta[b], delh + i0, p.nq - i0, lane);
     };
     if (nsteps > 0) issue_step(0, 0);
     wait_vm_loads();
@@ -145,55 +151,49 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
     for (int64_t n = 0; n < nsteps; ++n) {
         const int buf = (int)(n & 1);
         if (n + 1 < nsteps) issue_step(n + 1, buf ^ 1);
-        const int64_t i0 = (qt0 + n) * BQ;
-        // a wave works on the tile only if some row sees one of its keys
-        const bool live = wj0 < p.nk && (!p.causal || i0 + BQ - 1 >= wkpos);
+        const int64_t r0 = (qt0 + n) * BQ + rh * WQ;  // first row of this wave
+        // a wave works on the tile only if some of its rows sees one of its keys
+        const bool live = wj0 < p.nk && r0 < p.nq && (!p.causal || r0 + WQ - 1 >= wkpos);
         if (live) {
             const char* Qs = smem[buf][0];
             const char* Os = smem[buf][1];
-            f32x16 sacc[2], dpacc[2];
+            f32x16 sacc[1], dpacc[1];
 #pragma unroll
             for (int st = 0; st < NS; ++st) {
-                const int ko = lds_off<HD>(wave * 32 + l32, st * 16 + hi * 8);
+                const int ko = lds_off<HD>(kw * 32 + l32, st * 16 + hi * 8);
+                const int qo = lds_off<HD>(rh * 32 + l32, st * 16 + hi * 8);
                 const bf16x8 kf = lds_read_b128(skv[0], ko);
                 const bf16x8 vf = lds_read_b128(skv[1], ko);
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    const int qo = lds_off<HD>(qb * 32 + l32, st * 16 + hi * 8);
-                    const bf16x8 aq = lds_read_b128(Qs, qo);
-                    const bf16x8 ao = lds_read_b128(Os, qo);
-                    sacc[qb] = mfma32(aq, kf, st == 0 ? f32x16{} : sacc[qb]);
-                    dpacc[qb] = mfma32(ao, vf, st == 0 ? f32x16{} : dpacc[qb]);
-                }
+                const bf16x8 aq = lds_read_b128(Qs, qo);
+                const bf16x8 ao = lds_read_b128(Os, qo);
+                sacc[0] = mfma32(aq, kf, st == 0 ? f32x16{} : sacc[0]);
+                dpacc[0] = mfma32(ao, vf, st == 0 ? f32x16{} : dpacc[0]);
             }
-            bf16x8 pb[2][2], dsb[2][2];
+            bf16x8 pb[1][2], dsb[1][2];
+            const float* sl = s_lse[buf] + rh * WQ;
+            const float* sd = s_delta[buf] + rh * WQ;
             const bool edge_k = wj0 + WK > p.nk;
-            const bool edge_q = i0 + BQ > p.nq;
-            const bool diag = p.causal && i0 < wkpos + WK - 1;
+            const bool edge_q = r0 + WQ > p.nq;
+            const bool diag = p.causal && r0 < wkpos + WK - 1;
             if (edge_k || edge_q || diag) {
                 // rows relative to the wave's first key; keys past nk and rows
                 // past nq are invisible; non-causal sees every row
-                const int qrel0 = (int)(p.causal ? i0 - wkpos : WK + i0);
+                const int qrel0 = (int)(p.causal ? r0 - wkpos : WK + r0);
                 const int qlim = (int)(p.causal ? p.nq - wkpos : WK + p.nq);
                 const int kr = (myk < p.nk) ? krel : (1 << 30);
-                dkdv_p_ds<true>(sacc, dpacc, s_lse[buf], s_delta[buf], hi, p.scale_log2, qrel0,
-                                kr, qlim, pb, dsb);
+                dkdv_p_ds<1, true>(sacc, dpacc, sl, sd, hi, p.scale_log2, qrel0, kr, qlim, pb, dsb);
             } else {
-                dkdv_p_ds<false>(sacc, dpacc, s_lse[buf], s_delta[buf], hi, p.scale_log2, 0, 0, 0,
-                                 pb, dsb);
+                dkdv_p_ds<1, false>(sacc, dpacc, sl, sd, hi, p.scale_log2, 0, 0, 0, pb, dsb);
             }
-            // dV^T += dO^T P and dK^T += Q^T dS, reduction over the 64 query rows
+            // dV^T += dO^T P and dK^T += Q^T dS, reduction over the wave's 32 rows
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        bf16x8 ao = lds_read_tr_operand<HD>(Os, qb * 32 + h2 * 16, db * 32, lane);
-                        dv[db] = mfma32(ao, pb[qb][h2], dv[db]);
-                        bf16x8 aq = lds_read_tr_operand<HD>(Qs, qb * 32 + h2 * 16, db * 32, lane);
-                        dk[db] = mfma32(aq, dsb[qb][h2], dk[db]);
-                    }
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    bf16x8 ao = lds_read_tr_operand<HD>(Os, rh * 32 + h2 * 16, db * 32, lane);
+                    dv[db] = mfma32(ao, pb[0][h2], dv[db]);
+                    bf16x8 aq = lds_read_tr_operand<HD>(Qs, rh * 32 + h2 * 16, db * 32, lane);
+                    dk[db] = mfma32(aq, dsb[0][h2], dk[db]);
                 }
             }
         }
@@ -201,18 +201,42 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
         __syncthreads();
     }
 
-    if (myk >= p.nk) return;
+    // the two waves of a key block hold partial sums over the two row halves:
+    // waves 4-7 hand theirs over through LDS (free after the last barrier) and
+    // waves 0-3 add them, lower half first
+    f32x4* xk = reinterpret_cast<f32x4*>(&smem[0][0][0]) + kw * (NDB * 4 * 64);
+    f32x4* xv = reinterpret_cast<f32x4*>(&skv[0][0]) + kw * (NDB * 4 * 64);
+    if (rh == 1) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 x, y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[e] = dk[db][g4 * 4 + e];
+                    y[e] = dv[db][g4 * 4 + e];
+                }
+                xk[(db * 4 + g4) * 64 + lane] = x;
+                xv[(db * 4 + g4) * 64 + lane] = y;
+            }
+        }
+    }
+    __syncthreads();
+    if (rh == 1 || myk >= p.nk) return;
     float* ak = p.part_k + ((int64_t)hl * p.nk + myk) * HD;
     float* av = p.part_v + ((int64_t)hl * p.nk + myk) * HD;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 ok = xk[(db * 4 + g4) * 64 + lane];
+            const f32x4 ov = xv[(db * 4 + g4) * 64 + lane];
             f32x4 x, y;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                x[e] = dk[db][g4 * 4 + e];
-                y[e] = dv[db][g4 * 4 + e];
+                x[e] = dk[db][g4 * 4 + e] + ok[e];
+                y[e] = dv[db][g4 * 4 + e] + ov[e];
             }
             *reinterpret_cast<f32x4*>(ak + db * 32 + g4 * 8 + hi * 4) = x;
             *reinterpret_cast<f32x4*>(av + db * 32 + g4 * 8 + hi * 4) = y;
@@ -441,9 +465,9 @@ hipError_t launch_dkdv(const DkdvParams& p, int D, hipStream_t st) {
     const int64_t blocks = (p.nk + kDkdvBlockN - 1) / kDkdvBlockN * p.nh;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (D == 128)
-        hipLaunchKernelGGL(dkdv_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, st, p);
+        hipLaunchKernelGGL(dkdv_kernel<128>, dim3((unsigned)blocks), dim3(512), 0, st, p);
     else if (D == 64)
-        hipLaunchKernelGGL(dkdv_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, st, p);
+        hipLaunchKernelGGL(dkdv_kernel<64>, dim3((unsigned)blocks), dim3(512), 0, st, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
