@@ -25,7 +25,7 @@ namespace hc {
 // Online-softmax update of one 64-key tile for this lane's query row.  The
 // raw scores s (S^T blocks, lane = query) stay unscaled: the row maximum is
 // taken on them and the scale (softmax scale * log2 e) is folded into the
-// exponent, p = 2^(s * c - m) with m the running maximum in log2 units.  MASK
+// exponent, p = 2^(s * c - m) with m a running reference in log2 units.  MASK
 // adds the causal / ragged test with keys relative to the tile.
 template <bool MASK>
 __device__ __forceinline__ void fwd_softmax(f32x16 (&s)[2], float c, int hi, int qrel, int klim,
@@ -49,11 +49,16 @@ __device__ __forceinline__ void fwd_softmax(f32x16 (&s)[2], float c, int hi, int
         for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[b][r]);
     }
     rmax = pair_max(rmax) * c;
-    const float mnew = fmaxf(m, rmax);
+    // lazy reference: m moves (to the tile's maximum) only when that maximum
+    // exceeds it by more than 8 in log2 units, so every p = 2^(s c - m) stays
+    // <= 2^8, well inside fp32 and bf16 range, and O is rescaled only on such
+    // jumps; the softmax itself does not depend on the choice of m
+    const float mnew = (rmax > m + 8.0f) ? rmax : m;
     const float msafe = mnew == -INFINITY ? 0.f : mnew;
     alpha = fast_exp2(m - msafe);
     m = mnew;
     float psum = 0.f;
+
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
