@@ -100,6 +100,15 @@ def cpu_oracle_baseline(D: int, g: int, tokens: int) -> dict:
     from oracle import oracle as orc
     inp = attention_inputs(tokens, g, 1, D, 900, device="cpu")
     cores = len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     os.environ.setdefault("OMP_NUM_THREADS", str(cores))
     t0 = time.perf_counter()
     orc.attn_fwd(inp["q"], inp["k"], inp["v"], True)
@@ -108,6 +117,7 @@ def cpu_oracle_baseline(D: int, g: int, tokens: int) -> dict:
     counted = 7.0 * tokens * tokens * D * g
     del torch
     return {"value": counted / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu": cpu_model,
             "sample": f"fp64 oracle forward+backward of one GQA group ({g} query heads, 1 kv "
                       f"head, D={D}) over the first {tokens} tokens; {dt:.1f} s wall, counted "
                       f"FLOPs 7*S^2*D*heads"}
@@ -180,6 +190,8 @@ def main():
         for _ in range(warmup):
             step()
         torch.cuda.synchronize()
+        print(f"head_chunk={hc_}: {warmup} warm-up step(s) done, timing {steps}", file=sys.stderr,
+              flush=True)
         if timing:
             hcm.timing_reset()
             hcm.timing_enable(True)
@@ -196,10 +208,11 @@ def main():
         t_end.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
-        kern = None
+        kern = moved = None
         if timing:
             hcm.timing_enable(False)
             kern = hcm.timing_read()
+            moved = hcm.timing_bytes()
             hcm.timing_reset()
         total_ms = t_start.elapsed_time(t_end)
         fwd_ms = sum(a.elapsed_time(b) for a, b in zip(starts, mids))
@@ -207,6 +220,7 @@ def main():
         del ws
         return {"ms": total_ms / steps, "fwd_ms": fwd_ms / steps,
                 "bwd_ms": (total_ms - fwd_ms) / steps, "wall_s": wall, "kern": kern,
+                "moved": moved,
                 "ws_fwd": fb, "ws_bwd": bb, "peak_intermediate": peak}
 
     r = measure(hc, args.steps, args.warmup, timing=True)
@@ -253,6 +267,13 @@ def main():
                                       "peak_intermediate": r["peak_intermediate"]}},
         "kernel_ms_per_step": {f: round(kern[f][1] / args.steps, 3) for f in kern if kern[f][0]},
         "roofline": roof,
+        # the HBM-bound passes: algorithmic bytes (fixed by each launch's
+        # parameters) over their HIP-event time, against the 8 TB/s peak
+        "hbm_passes": {f: {"ms_per_step": round(kern[f][1] / args.steps, 4),
+                           "bytes_per_step": r["moved"][f] / args.steps,
+                           "gbs": round(r["moved"][f] / (kern[f][1] / 1e3) / 1e9, 1),
+                           "frac": round(r["moved"][f] / (kern[f][1] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+                       for f in ("pack", "prep", "merge", "reduce") if kern[f][0] and kern[f][1] > 0},
     }
     others = [h for h in w.head_chunks if h != hc]
     if not args.no_compare and others:

@@ -6,4 +6,4 @@ use, so importing this package does not need a GPU.
 """
 from .hcattn import (HcAttnError, attn_bwd, attn_fwd, bwd_workspace_bytes,  # noqa: F401
                      fwd_workspace_bytes, last_error, set_single_stream, timing_enable,
-                     timing_read, timing_reset, version)
+                     timing_bytes, timing_read, timing_reset, version)

@@ -201,6 +201,7 @@ const char* const kKernelNames[K_COUNT] = {"fwd", "merge", "pack", "prep", "dkdv
 struct TimingRec {
     int kid;
     hipEvent_t a, b;
+    double bytes;  // HBM bytes the launch reads and writes by its parameters (0: not a pass)
 };
 std::atomic<int> g_timing{0};
 std::mutex g_tmu;
@@ -221,10 +222,10 @@ hipEvent_t pool_event() {
 // Launch through `launch` (returns hipError_t); when timing is on, bracket it
 // with events on stream st.
 template <class F>
-hipError_t timed(int kid, hipStream_t st, F&& launch) {
+hipError_t timed(int kid, hipStream_t st, double bytes, F&& launch) {
     if (!g_timing.load()) return launch();
     std::lock_guard<std::mutex> lk(g_tmu);
-    TimingRec r{kid, pool_event(), pool_event()};
+    TimingRec r{kid, pool_event(), pool_event(), bytes};
     if (r.a == nullptr || r.b == nullptr) return hipErrorOutOfMemory;
     hipError_t e = hipEventRecord(r.a, st);
     if (e != hipSuccess) return e;
@@ -241,7 +242,32 @@ hipError_t timed(int kid, hipStream_t st, F&& launch) {
         hipError_t e_ = (expr);                                                            \
         if (e_ != hipSuccess) return fail(ATTN_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
     } while (0)
-#define LAUNCH(kid, call) KCHK(timed(kid, c.st, [&]() { return (call); }))
+#define LAUNCH(kid, call) KCHK(timed(kid, c.st, 0.0, [&]() { return (call); }))
+// the streaming passes also record the bytes they move (read + write), which
+// follow from their parameters alone
+#define LAUNCH_PASS(kid, prm, call) KCHK(timed(kid, c.st, moved_bytes(prm), [&]() { return (call); }))
+
+double moved_bytes(const hc::PackParams& p) {
+    return 2.0 * p.nh * (double)p.rows * p.D * 2;  // bf16 in, bf16 out
+}
+double moved_bytes(const hc::PrepParams& p) {
+    // O and dO in, packed dO out (bf16); Delta out (fp32)
+    return (double)p.nh * p.rows * (3.0 * p.D * 2 + 4);
+}
+double moved_bytes(const hc::MergeParams& p) {
+    // running and trunk O (fp32) and LSE in; running O / LSE or bf16 O / LSE out
+    const double out = p.final_out ? p.D * 2.0 + 4 : p.D * 4.0 + 4;
+    return (double)p.nh * p.rows * (2.0 * p.D * 4 + 8 + out);
+}
+double moved_bytes(const hc::DkdvReduceParams& p) {
+    const double row = (double)p.nk * p.D;
+    double b = p.nh * row * 8;                    // fp32 dK and dV partials of every head
+    if (p.carry_kv_in >= 0) b += row * 8;         // fp32 carry in
+    const int carry_out = p.carry_kv_out >= 0 ? 1 : 0;
+    b += (p.nkv - carry_out) * row * 4;           // bf16 dK, dV
+    b += carry_out * row * 8;                     // fp32 carry out
+    return b;
+}
 
 // ------------------------------------------------------------------ forward
 
@@ -256,11 +282,11 @@ int fwd_untrunked(Common& c, const uint16_t* q, const uint16_t* k, const uint16_
     for (int ci = 0; ci < p.nchunks; ++ci) {
         const hc::Chunk ch = p.chunk(ci);
         hc::PackParams pk{q + (size_t)ch.h0 * D, (int64_t)p.Hq * D, D, Qc, D, S * D, ch.nh, S, D};
-        LAUNCH(K_PACK, hc::launch_pack(pk, c.st));
+        LAUNCH_PASS(K_PACK, pk, hc::launch_pack(pk, c.st));
         pk = {k + (size_t)ch.kv0 * D, (int64_t)p.Hkv * D, D, Kc, D, S * D, ch.nkv, S, D};
-        LAUNCH(K_PACK, hc::launch_pack(pk, c.st));
+        LAUNCH_PASS(K_PACK, pk, hc::launch_pack(pk, c.st));
         pk = {v + (size_t)ch.kv0 * D, (int64_t)p.Hkv * D, D, Vc, D, S * D, ch.nkv, S, D};
-        LAUNCH(K_PACK, hc::launch_pack(pk, c.st));
+        LAUNCH_PASS(K_PACK, pk, hc::launch_pack(pk, c.st));
         hc::FwdParams f{};
         f.q = Qc; f.q_rs = D; f.q_hs = S * D;
         f.k = Kc; f.k_rs = D; f.k_hs = S * D;
@@ -291,7 +317,7 @@ int fwd_trunked(Common& c, const uint16_t* q, const void* k, const void* v, uint
             const int64_t qr0 = p.trunk_begin(m), nq = p.trunk_rows(m);
             hc::PackParams pk{q + ((size_t)qr0 * p.Hq + ch.h0) * D, (int64_t)p.Hq * D, D, Qm, D,
                               T * D, ch.nh, nq, D};
-            LAUNCH(K_PACK, hc::launch_pack(pk, c.st));
+            LAUNCH_PASS(K_PACK, pk, hc::launch_pack(pk, c.st));
             const int64_t tlast = p.causal ? m : p.N - 1;
             for (int64_t t = 0; t <= tlast; ++t) {
                 int slot = 0;
@@ -326,7 +352,7 @@ int fwd_trunked(Common& c, const uint16_t* q, const void* k, const void* v, uint
                     mg.out = o + ((size_t)qr0 * p.Hq + ch.h0) * D; mg.out_rs = (int64_t)p.Hq * D;
                     mg.out_hs = D;
                     mg.lse_out = lse + (size_t)ch.h0 * p.S + qr0; mg.lse_hs = p.S;
-                    LAUNCH(K_MERGE, hc::launch_merge(mg, c.st));
+                    LAUNCH_PASS(K_MERGE, mg, hc::launch_merge(mg, c.st));
                 }
             }
         }
@@ -400,14 +426,14 @@ int bwd_chunk_prep(Common& c, const hc::Chunk& ch, const BwdIO& io) {
     const int64_t S = p.S;
     uint16_t* Qc = reinterpret_cast<uint16_t*>(c.ws + p.q_c);
     hc::PackParams pk{io.q + (size_t)ch.h0 * D, (int64_t)p.Hq * D, D, Qc, D, S * D, ch.nh, S, D};
-    LAUNCH(K_PACK, hc::launch_pack(pk, c.st));
+    LAUNCH_PASS(K_PACK, pk, hc::launch_pack(pk, c.st));
     hc::PrepParams pr{};
     pr.o = io.o + (size_t)ch.h0 * D; pr.o_rs = (int64_t)p.Hq * D; pr.o_hs = D;
     pr.dO = io.dout + (size_t)ch.h0 * D; pr.do_rs = (int64_t)p.Hq * D; pr.do_hs = D;
     pr.dO_c = reinterpret_cast<uint16_t*>(c.ws + p.do_c); pr.c_rs = D; pr.c_hs = S * D;
     pr.delta = reinterpret_cast<float*>(c.ws + p.delta_c); pr.delta_hs = S;
     pr.nh = ch.nh; pr.rows = S; pr.D = D;
-    LAUNCH(K_PREP, hc::launch_prep(pr, c.st));
+    LAUNCH_PASS(K_PREP, pr, hc::launch_prep(pr, c.st));
     return ATTN_OK;
 }
 
@@ -443,15 +469,15 @@ int bwd_untrunked(Common& c, const BwdIO& io) {
         const uint16_t* k = static_cast<const uint16_t*>(io.k);
         const uint16_t* v = static_cast<const uint16_t*>(io.v);
         hc::PackParams pk{k + (size_t)ch.kv0 * D, (int64_t)p.Hkv * D, D, Kc, D, S * D, ch.nkv, S, D};
-        LAUNCH(K_PACK, hc::launch_pack(pk, c.st));
+        LAUNCH_PASS(K_PACK, pk, hc::launch_pack(pk, c.st));
         pk = {v + (size_t)ch.kv0 * D, (int64_t)p.Hkv * D, D, Vc, D, S * D, ch.nkv, S, D};
-        LAUNCH(K_PACK, hc::launch_pack(pk, c.st));
+        LAUNCH_PASS(K_PACK, pk, hc::launch_pack(pk, c.st));
         hc::DkdvParams dk = dkdv_params(c, ch, io, Kc, Vc, D, S * D, 0, S);
         LAUNCH(K_DKDV, hc::launch_dkdv(dk, D, c.st));
         hc::DkdvReduceParams rd = reduce_params(
             c, ch, ci, 0, S, static_cast<uint16_t*>(io.dk) + (size_t)ch.kv0 * D,
             static_cast<uint16_t*>(io.dv) + (size_t)ch.kv0 * D, (int64_t)p.Hkv * D, D);
-        LAUNCH(K_REDUCE, hc::launch_dkdv_reduce(rd, c.st));
+        LAUNCH_PASS(K_REDUCE, rd, hc::launch_dkdv_reduce(rd, c.st));
         hc::DqParams dq = dq_params(c, ch, io, Kc, Vc, D, S * D, 0, S);
         LAUNCH(K_DQ, hc::launch_dq(dq, D, c.st));
     }
@@ -496,7 +522,7 @@ int bwd_trunked(Common& c, const BwdIO& io) {
                     static_cast<uint16_t*>(io.dv) + ((size_t)kr0 * p.Hkv + ch.kv0) * D,
                     (int64_t)p.Hkv * D, D);
             }
-            LAUNCH(K_REDUCE, hc::launch_dkdv_reduce(rd, c.st));
+            LAUNCH_PASS(K_REDUCE, rd, hc::launch_dkdv_reduce(rd, c.st));
             hc::DqParams dq = dq_params(c, ch, io, kk, vv, (int64_t)ch.nkv * D, D, kr0, nk);
             dq.q_begin = p.causal ? kr0 : 0;
             dq.acc_in = t == 0 ? nullptr : dQacc;
@@ -663,6 +689,20 @@ int attn_timing_read(const char* name, int64_t* launches, double* total_ms) {
     }
     if (launches) *launches = n;
     if (total_ms) *total_ms = ms;
+    return ATTN_OK;
+}
+
+int attn_timing_bytes(const char* name, double* bytes) {
+    int kid = -1;
+    for (int i = 0; i < K_COUNT; ++i)
+        if (name && std::strcmp(name, kKernelNames[i]) == 0) kid = i;
+    if (kid < 0) return fail(ATTN_EINVAL, "unknown kernel family '%s'", name ? name : "(null)");
+    if (bytes == nullptr) return fail(ATTN_EPOINTER, "bytes is NULL");
+    std::lock_guard<std::mutex> lk(g_tmu);
+    double b = 0.0;
+    for (const TimingRec& r : g_recs)
+        if (r.kid == kid) b += r.bytes;
+    *bytes = b;
     return ATTN_OK;
 }
 

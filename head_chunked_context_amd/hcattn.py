@@ -60,6 +60,8 @@ def lib():
     L.attn_timing_read.restype = ctypes.c_int
     L.attn_timing_reset.argtypes = []
     L.attn_timing_reset.restype = None
+    L.attn_timing_bytes.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double)]
+    L.attn_timing_bytes.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -179,6 +181,17 @@ def timing_enable(on: bool) -> bool:
 
 def timing_reset() -> None:
     lib().attn_timing_reset()
+
+
+def timing_bytes() -> dict:
+    """{family: bytes} moved by the timed streaming-pass launches since the
+    last reset (read + write, fixed by their parameters; 0 for MFMA kernels)."""
+    out = {}
+    for name in KERNEL_FAMILIES:
+        b = ctypes.c_double(0.0)
+        _check(lib().attn_timing_bytes(name.encode(), ctypes.byref(b)))
+        out[name] = float(b.value)
+    return out
 
 
 def timing_read() -> dict:

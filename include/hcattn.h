@@ -149,6 +149,15 @@ int attn_timing_enable(int on);
 int attn_timing_read(const char* name, int64_t* launches, double* total_ms);
 void attn_timing_reset(void);
 
+/*
+ * Bytes moved (read + written) by the timed launches of one streaming-pass
+ * family ("pack", "prep", "merge", "reduce") since the last reset, as their
+ * parameters fix them: the algorithmic traffic, against which the timed
+ * duration gives GB/s.  The MFMA families report 0.  Returns ATTN_OK,
+ * ATTN_EINVAL (unknown name) or ATTN_EPOINTER (bytes NULL).
+ */
+int attn_timing_bytes(const char* name, double* bytes);
+
 /* Library version, "major.minor.patch". */
 const char* attn_version(void);
 
