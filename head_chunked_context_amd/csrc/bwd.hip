@@ -286,14 +286,14 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(DkdvReduceParams p) {
     }
 }
 
-// dS^T of one 64-key tile for this lane's query row as bf16 MFMA operands.
-// MASK adds the causal / ragged test with keys relative to the tile.
-template <bool MASK>
-__device__ __forceinline__ void dq_ds(const f32x16 (&s)[2], const f32x16 (&dp)[2], float scale_log2,
+// dS^T of NB 32-key blocks for this lane's query row as bf16 MFMA operands.
+// MASK adds the causal / ragged test with keys relative to the first block.
+template <int NB, bool MASK>
+__device__ __forceinline__ void dq_ds(const f32x16 (&s)[NB], const f32x16 (&dp)[NB], float scale_log2,
                                       float lse2, float dlt, int hi, int qrel, int klim,
-                                      bf16x8 (&dsb)[2][2]) {
+                                      bf16x8 (&dsb)[NB][2]) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < NB; ++b) {
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
             float dsv[2];
@@ -382,6 +382,15 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(DqParams p) {
         direct_tile64<HD>(smem[0][1], vh, p.v_rs, p.nk, wave, lane);
     }
     wait_vm_loads();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        settle(qf[s]);
+        settle(df[s]);
+    }
+    settle(lse2);
+    settle(dlt);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) settle(acc[db]);
     __syncthreads();
 
     const int64_t qrel_base = myq - p.k_pos0;  // query position relative to key 0
@@ -395,36 +404,36 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(DqParams p) {
         if (j < ntiles_w) {
             const char* Ks = smem[buf][0];
             const char* Vs = smem[buf][1];
-            f32x16 s[2], dp[2];
+            const int64_t kb = (int64_t)j * BN;
+            const bool need_mask = (kb + BN > p.nk) || (p.causal && p.k_pos0 + kb + BN - 1 > wq0);
+            // the tile's two 32-key halves one after the other (half the score
+            // registers live at a time)
 #pragma unroll
-            for (int st = 0; st < NS; ++st) {
+            for (int b = 0; b < 2; ++b) {
+                f32x16 s[1], dp[1];
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
+                for (int st = 0; st < NS; ++st) {
                     const int o = lds_off<HD>(b * 32 + l32, st * 16 + hi * 8);
                     const bf16x8 ak = lds_read_b128(Ks, o);
                     const bf16x8 av = lds_read_b128(Vs, o);
-                    s[b] = mfma32(ak, qf[st], st == 0 ? f32x16{} : s[b]);
-                    dp[b] = mfma32(av, df[st], st == 0 ? f32x16{} : dp[b]);
+                    s[0] = mfma32(ak, qf[st], st == 0 ? f32x16{} : s[0]);
+                    dp[0] = mfma32(av, df[st], st == 0 ? f32x16{} : dp[0]);
                 }
-            }
-            const int64_t kb = (int64_t)j * BN;
-            const bool need_mask = (kb + BN > p.nk) || (p.causal && p.k_pos0 + kb + BN - 1 > wq0);
-            bf16x8 dsb[2][2];
-            if (need_mask) {
-                const int64_t qr = p.causal ? qrel_base - kb : (int64_t)BN;
-                dq_ds<true>(s, dp, p.scale_log2, lse2, dlt, hi, (int)qr, (int)(p.nk - kb), dsb);
-            } else {
-                dq_ds<false>(s, dp, p.scale_log2, lse2, dlt, hi, 0, 0, dsb);
-            }
-            // dQ^T += K^T dS^T over the tile's 64 keys
+                bf16x8 dsb[1][2];
+                if (need_mask) {
+                    const int64_t qr = p.causal ? qrel_base - kb - b * 32 : (int64_t)BN;
+                    const int kl = (int)(p.nk - kb - b * 32);
+                    dq_ds<1, true>(s, dp, p.scale_log2, lse2, dlt, hi, (int)qr, kl, dsb);
+                } else {
+                    dq_ds<1, false>(s, dp, p.scale_log2, lse2, dlt, hi, 0, 0, dsb);
+                }
+                // dQ^T += K^T dS^T over the half's 32 keys
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
+                for (int db = 0; db < NDB; ++db) {
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) {
                         bf16x8 ak = lds_read_tr_operand<HD>(Ks, b * 32 + h2 * 16, db * 32, lane);
-                        acc[db] = mfma32(ak, dsb[b][h2], acc[db]);
+                        acc[db] = mfma32(ak, dsb[0][h2], acc[db]);
                     }
                 }
             }

@@ -37,6 +37,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309f;
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int HD>
 __device__ __forceinline__ int swz(int row) {
     if constexpr (HD == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
@@ -94,11 +96,34 @@ __device__ __forceinline__ bf16x2 to_bf16x2(float a, float b) {
     return __builtin_convertvector(f, bf16x2);
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 // Wait until every vector-memory load of this wave has landed (including the
 // direct global -> LDS loads below, which do not pass through registers).
 __device__ __forceinline__ void wait_vm_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Direct global -> LDS loads (global_load_lds_dword[x4]): lane l's 4 / 16 bytes
+// from `src` land at LDS byte lds_addr + 4 l / 16 l (M0 holds the wave-uniform
+// base).  Issued as inline assembly on purpose: the compiler then does not
+// treat them as pending LDS writes, and adds no vmcnt wait before the reads of
+// the other buffer while the prefetch is in flight; the kernels order them
+// with wait_vm_loads() and a barrier before the buffer is read.  M0 is written
+// by these loads only (no other code in the kernels uses it).
+// An empty use of registers loaded from global memory: the compiler places
+// the wait for those loads here (before a loop) rather than at their first use
+// inside the loop, where it would also wait for prefetches in flight.
+template <class T>
+__device__ __forceinline__ void settle(const T& x) { asm volatile("" :: "v"(x)); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)((const lds_void*)p);
+}
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(lds_base) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(src), "s"(lds_base) : "memory");
+}
 
 // 64-row x HD-column bf16 tile loaded straight from global memory into the
 // swizzled LDS layout with global_load_lds_dwordx4: lane l of a wave writes
@@ -118,8 +143,7 @@ __device__ __forceinline__ void direct_tile64(char* lds_tile, const uint16_t* ba
         const int row = blk * RPI + lane / CPR;
         const int lc = (lane % CPR) ^ swz<HD>(row);
         const int64_t srow = row < nvalid ? row : nvalid - 1;
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(base + srow * rs + lc * 8),
-                                         (lds_void*)(lds_tile + blk * 1024), 16, 0, 0);
+        lds_dma16(base + srow * rs + lc * 8, lds_addr(lds_tile + blk * 1024));
     }
 }
 
@@ -127,8 +151,7 @@ __device__ __forceinline__ void direct_tile64(char* lds_tile, const uint16_t* ba
 // or past nvalid (>= 1) repeat entry nvalid - 1.
 __device__ __forceinline__ void direct_vec64(float* lds_vec, const float* src, int64_t nvalid, int lane) {
     const int64_t i = lane < nvalid ? lane : nvalid - 1;
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + i),
-                                     (lds_void*)(lds_vec), 4, 0, 0);
+    lds_dma4(src + i, lds_addr(lds_vec));
 }
 
 // 64-row x HD-column bf16 tile: global -> registers -> swizzled LDS, 256 threads.

@@ -136,6 +136,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         direct_tile64<HD>(smem[0][1], vh, p.v_rs, p.nk, wave, lane);
     }
     wait_vm_loads();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) settle(qf[s]);
     __syncthreads();
 
     // this lane's query position relative to the key positions of tile 0
