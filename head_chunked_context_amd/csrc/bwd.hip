@@ -87,7 +87,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
     __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];
     __shared__ __attribute__((aligned(16))) float s_delta[2][BQ];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values scalar
     const int hi = lane >> 5, l32 = lane & 31;
     const int kw = wave & 3;   // key block of the wave (32 keys)
     const int rh = wave >> 2;  // half of every 64-row query tile the wave takes
@@ -320,7 +321,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(DqParams p) {
     constexpr int TILE = BN * HD * 2;
     __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [buf][K / V]
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values scalar
     const int hi = lane >> 5, l32 = lane & 31;
 
     const int64_t qtb = p.q_begin / BM;

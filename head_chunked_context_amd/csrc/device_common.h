@@ -110,19 +110,30 @@ __device__ __forceinline__ void wait_vm_loads() { asm volatile("s_waitcnt vmcnt(
 // An empty use of registers loaded from global memory: the compiler places
 // the wait for those loads here (before a loop) rather than at their first use
 // inside the loop, where it would also wait for prefetches in flight.
+// (The host pass of hipcc parses this too; the operand is a GPU register only
+// in the device pass.)
 template <class T>
-__device__ __forceinline__ void settle(const T& x) { asm volatile("" :: "v"(x)); }
+__device__ __forceinline__ void settle(const T& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" :: "v"(x));
+#else
+    (void)x;
+#endif
+}
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)((const lds_void*)p);
 }
+// (lds_base must be the same in all lanes; readfirstlane makes it a scalar.)
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(src), "s"(lds_base) : "memory");
+                 :: "v"(src), "s"(m0) : "memory");
 }
 __device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-                 :: "v"(src), "s"(lds_base) : "memory");
+                 :: "v"(src), "s"(m0) : "memory");
 }
 
 // 64-row x HD-column bf16 tile loaded straight from global memory into the

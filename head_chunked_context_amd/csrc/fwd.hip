@@ -86,7 +86,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     constexpr int TILE = BN * HD * 2;
     __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values scalar
     const int hi = lane >> 5, l32 = lane & 31;
 
     const int64_t nqt = (p.nq + BM - 1) / BM;
