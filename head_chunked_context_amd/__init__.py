@@ -5,5 +5,6 @@
 use, so importing this package does not need a GPU.
 """
 from .hcattn import (HcAttnError, attn_bwd, attn_fwd, bwd_workspace_bytes,  # noqa: F401
-                     fwd_workspace_bytes, last_error, set_single_stream, timing_enable,
+                     fwd_workspace_bytes, last_error, set_single_stream, set_trunk_merge,
+                     timing_enable,
                      timing_bytes, timing_read, timing_reset, version)

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
             bf16x2 lo = to_bf16x2(z[0], z[1]), hi = to_bf16x2(z[2], z[3]);
             bf16x4 w = {lo[0], lo[1], hi[0], hi[1]};
             *reinterpret_cast<bf16x4*>(p.out + h * p.out_hs + row * p.out_rs + c * 4) = w;
-            if (c == 0) p.lse_out[h * p.lse_hs + row] = L;
+            if (c == 0 && p.lse_out != nullptr) p.lse_out[h * p.lse_hs + row] = L;
         } else {
             *reinterpret_cast<f32x4*>(p.o_r + hr * p.D + c * 4) = z;
         }

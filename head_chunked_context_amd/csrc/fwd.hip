@@ -131,6 +131,26 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     f32x16 o[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
+    // continue the state a previous key range left for this row
+    if (p.carry_in && myq < p.nq) {
+        const int64_t sr = (int64_t)head * p.st_hs + myq;
+        m = p.st_m[sr];
+        lpart = p.st_l[2 * sr + hi];
+        const float* so = p.st_o + (int64_t)head * p.st_o_hs + myq * HD;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(so + db * 32 + g4 * 8 + hi * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[db][g4 * 4 + e] = x[e];
+            }
+        }
+        settle(m);
+        settle(lpart);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) settle(o[db]);
+    }
 
     if (ntiles > 0) {
         direct_tile64<HD>(smem[0][0], kh, p.k_rs, p.nk, wave, lane);
@@ -202,6 +222,24 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     }
 
     if (!wave_live || myq >= p.nq) return;
+    if (p.carry_out) {
+        // hand the unnormalised state to the next key range, bit for bit
+        const int64_t sr = (int64_t)head * p.st_hs + myq;
+        if (hi == 0) p.st_m[sr] = m;
+        p.st_l[2 * sr + hi] = lpart;
+        float* so = p.st_o + (int64_t)head * p.st_o_hs + myq * HD;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = o[db][g4 * 4 + e];
+                *reinterpret_cast<f32x4*>(so + db * 32 + g4 * 8 + hi * 4) = x;
+            }
+        }
+        return;
+    }
     const float ltot = pair_sum(lpart);
     if (p.mode == kFwdFinal) {
         const float inv = 1.0f / ltot;
@@ -216,7 +254,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
                 *reinterpret_cast<bf16x4*>(orow + db * 32 + g4 * 8 + hi * 4) = w;
             }
         }
-        if (hi == 0) p.lse[(int64_t)head * p.lse_hs + myq] = (m + __builtin_log2f(ltot)) * kLn2;
+        if (hi == 0 && p.lse != nullptr)
+            p.lse[(int64_t)head * p.lse_hs + myq] = (m + __builtin_log2f(ltot)) * kLn2;
     } else {
         const bool empty = !(ltot > 0.f);
         const float inv = empty ? 0.f : 1.0f / ltot;

@@ -5,10 +5,17 @@
 //   untrunked: pack the chunk's Q, K, V head-major -> flash kernel -> bf16 O, LSE
 //   trunked  : for query trunk m: pack Q_m; for key trunk t = 0..m (causal) the
 //              copy stream fills ring slot t%2 with K_t, V_t (pinned host or
-//              device) while the previous trunk computes; flash kernel gives
-//              the trunk partial; log-sum-exp merge into the running output
-//              (FPDT summary, "Technical Deep Dive": trunking, host offload,
-//              double buffer, separate compute and offload streams).
+//              device) while the previous trunk computes (FPDT summary,
+//              "Technical Deep Dive": trunking, host offload, double buffer,
+//              separate compute and offload streams).  The flash kernel
+//              carries the query trunk's running softmax state (O, m, row
+//              sums, fp32) from key trunk to key trunk and normalises after
+//              the last one, which makes the result bitwise that of the
+//              untrunked forward; attn_set_trunk_merge(1) selects the
+//              partial-output schedule instead: each key trunk gives a
+//              normalised partial with its LSE, merged into the running
+//              output by log-sum-exp (same section, softmax statistics
+//              updated until the trunk's final output).
 // Backward, per head chunk: pack Q, dO (+ Delta), then per key range (the
 // whole sequence, or key trunk t with the same ring) the dK/dV kernel and the
 // dQ kernel; dQ is carried in fp32 across trunks, dK/dV in fp32 across chunks
@@ -32,6 +39,7 @@ namespace {
 
 thread_local char g_err[512];
 std::atomic<int> g_single_stream{0};
+std::atomic<int> g_trunk_merge{0};
 
 int fail(int code, const char* fmt, ...) {
     va_list ap;
@@ -292,7 +300,7 @@ int fwd_untrunked(Common& c, const uint16_t* q, const uint16_t* k, const uint16_
         f.k = Kc; f.k_rs = D; f.k_hs = S * D;
         f.v = Vc; f.v_rs = D; f.v_hs = S * D;
         f.o = o + (size_t)ch.h0 * D; f.o_rs = (int64_t)p.Hq * D; f.o_hs = D;
-        f.lse = lse + (size_t)ch.h0 * S; f.lse_hs = S;
+        f.lse = lse ? lse + (size_t)ch.h0 * S : nullptr; f.lse_hs = S;
         f.nh = ch.nh; f.group = p.g; f.h0 = ch.h0; f.kv_base = ch.kv0;
         f.nq = S; f.q_pos0 = 0; f.nk = S; f.k_pos0 = 0;
         f.causal = p.causal; f.mode = hc::kFwdFinal; f.scale_log2 = c.scale_log2;
@@ -305,11 +313,13 @@ int fwd_trunked(Common& c, const uint16_t* q, const void* k, const void* v, uint
     const hc::Plan& p = c.pl;
     const int D = p.D;
     const int64_t T = p.T;
+    const bool merge = g_trunk_merge.load() != 0;
     uint16_t* Qm = reinterpret_cast<uint16_t*>(c.ws + p.q_c);
     float* Orun = reinterpret_cast<float*>(c.ws + p.o_run);
     float* Ot = reinterpret_cast<float*>(c.ws + p.o_t);
     float* Lrun = reinterpret_cast<float*>(c.ws + p.l_run);
     float* Lt = reinterpret_cast<float*>(c.ws + p.l_t);
+    float* Lpair = reinterpret_cast<float*>(c.ws + p.st_l);
     Ring ring{&c};
     for (int ci = 0; ci < p.nchunks; ++ci) {
         const hc::Chunk ch = p.chunk(ci);
@@ -318,6 +328,8 @@ int fwd_trunked(Common& c, const uint16_t* q, const void* k, const void* v, uint
             hc::PackParams pk{q + ((size_t)qr0 * p.Hq + ch.h0) * D, (int64_t)p.Hq * D, D, Qm, D,
                               T * D, ch.nh, nq, D};
             LAUNCH_PASS(K_PACK, pk, hc::launch_pack(pk, c.st));
+            float* lse_m = lse ? lse + (size_t)ch.h0 * p.S + qr0 : nullptr;
+            uint16_t* o_m = o + ((size_t)qr0 * p.Hq + ch.h0) * D;
             const int64_t tlast = p.causal ? m : p.N - 1;
             for (int64_t t = 0; t <= tlast; ++t) {
                 int slot = 0;
@@ -332,10 +344,21 @@ int fwd_trunked(Common& c, const uint16_t* q, const void* k, const void* v, uint
                 f.nh = ch.nh; f.group = p.g; f.h0 = ch.h0; f.kv_base = ch.kv0;
                 f.nq = nq; f.q_pos0 = qr0; f.nk = p.trunk_rows(t); f.k_pos0 = p.trunk_begin(t);
                 f.causal = p.causal; f.scale_log2 = c.scale_log2;
-                if (tlast == 0) {
+                const bool last = t == tlast;
+                if (!merge) {
+                    // the running softmax state goes from trunk to trunk through
+                    // the workspace; the last trunk writes the normalised output
+                    f.carry_in = t > 0;
+                    f.carry_out = !last;
+                    f.st_o = Orun; f.st_o_hs = nq * D;
+                    f.st_m = Lrun; f.st_l = Lpair; f.st_hs = nq;
                     f.mode = hc::kFwdFinal;
-                    f.o = o + ((size_t)qr0 * p.Hq + ch.h0) * D; f.o_rs = (int64_t)p.Hq * D; f.o_hs = D;
-                    f.lse = lse + (size_t)ch.h0 * p.S + qr0; f.lse_hs = p.S;
+                    f.o = o_m; f.o_rs = (int64_t)p.Hq * D; f.o_hs = D;
+                    f.lse = lse_m; f.lse_hs = p.S;
+                } else if (tlast == 0) {
+                    f.mode = hc::kFwdFinal;
+                    f.o = o_m; f.o_rs = (int64_t)p.Hq * D; f.o_hs = D;
+                    f.lse = lse_m; f.lse_hs = p.S;
                 } else {
                     f.mode = hc::kFwdPartial;
                     f.o = t == 0 ? Orun : Ot; f.o_rs = D; f.o_hs = nq * D;
@@ -344,14 +367,13 @@ int fwd_trunked(Common& c, const uint16_t* q, const void* k, const void* v, uint
                 LAUNCH(K_FWD, hc::launch_fwd(f, D, c.st));
                 r = ring.release(slot);
                 if (r) return r;
-                if (t > 0) {
+                if (merge && t > 0) {
                     hc::MergeParams mg{};
                     mg.o_r = Orun; mg.l_r = Lrun; mg.o_t = Ot; mg.l_t = Lt;
                     mg.nh = ch.nh; mg.rows = nq; mg.D = D;
-                    mg.final_out = t == tlast;
-                    mg.out = o + ((size_t)qr0 * p.Hq + ch.h0) * D; mg.out_rs = (int64_t)p.Hq * D;
-                    mg.out_hs = D;
-                    mg.lse_out = lse + (size_t)ch.h0 * p.S + qr0; mg.lse_hs = p.S;
+                    mg.final_out = last;
+                    mg.out = o_m; mg.out_rs = (int64_t)p.Hq * D; mg.out_hs = D;
+                    mg.lse_out = lse_m; mg.lse_hs = p.S;
                     LAUNCH_PASS(K_MERGE, mg, hc::launch_merge(mg, c.st));
                 }
             }
@@ -605,7 +627,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     bool kh = false, vh = false;
     if ((r = check_ptr(q, "q", false, nullptr)) || (r = check_ptr(k, "k", pl.trunked, &kh)) ||
         (r = check_ptr(v, "v", pl.trunked, &vh)) || (r = check_ptr(o, "o", false, nullptr)) ||
-        (r = check_ptr(lse, "lse", false, nullptr)) ||
+        (lse != nullptr && (r = check_ptr(lse, "lse", false, nullptr))) ||
         (r = check_ptr(workspace, "workspace", false, nullptr)))
         return r;
     Common c;
@@ -656,6 +678,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
 const char* attn_last_error(void) { return g_err; }
 
 int attn_set_single_stream(int on) { return g_single_stream.exchange(on ? 1 : 0); }
+
+int attn_set_trunk_merge(int on) { return g_trunk_merge.exchange(on ? 1 : 0); }
 
 const char* attn_version(void) { return "0.1.0"; }
 

@@ -33,6 +33,15 @@ struct FwdParams {
     int causal;
     int mode;
     float scale_log2;   // softmax scale * log2(e)
+    // Running state of the online softmax carried across key ranges (trunks):
+    // with carry_in the kernel starts from the state in st_*, with carry_out
+    // it stores its state there instead of an output (mode is then unused).
+    // State per (head, row): unnormalised O [D] fp32 at st_o + head * st_o_hs
+    // + row * D, the reference m (log2 units) at st_m[head * st_hs + row] and
+    // the two lanes' partial sums at st_l[2 * (head * st_hs + row) + 0 / 1].
+    int carry_in, carry_out;
+    float* st_o; int64_t st_o_hs;
+    float* st_m; float* st_l; int64_t st_hs;
 };
 
 // Copy nh heads x rows x D bf16 between strided layouts (16-byte vectors).

@@ -35,7 +35,8 @@ struct Plan {
 
     // workspace regions, byte offsets
     size_t q_c = 0, k_c = 0, v_c = 0;                   // packed chunk buffers
-    size_t o_run = 0, o_t = 0, l_run = 0, l_t = 0;      // fwd trunk partials
+    size_t o_run = 0, o_t = 0, l_run = 0, l_t = 0;      // fwd trunk partials / carried state
+    size_t st_l = 0;                                    // fwd carried lane-pair row sums
     size_t ring_k[2] = {0, 0}, ring_v[2] = {0, 0};      // trunk ring slots
     size_t do_c = 0, delta_c = 0, dq_acc = 0;           // bwd chunk buffers
     size_t part_k = 0, part_v = 0;                      // bwd per-head fp32 dK/dV
@@ -131,6 +132,7 @@ static inline int make_plan(bool bwd, int64_t S, int Hq, int Hkv, int D, int cau
             p.o_t = take(p.hc * Et * 2);                      // fp32 trunk partial
             p.l_run = take((size_t)p.hc * p.T * 4);
             p.l_t = take((size_t)p.hc * p.T * 4);
+            p.st_l = take((size_t)p.hc * p.T * 8);            // carried row sums, 2 per row
             for (int s = 0; s < 2; ++s) {
                 p.ring_k[s] = take(p.kvc * Et);
                 p.ring_v[s] = take(p.kvc * Et);

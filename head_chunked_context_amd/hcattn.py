@@ -51,6 +51,8 @@ def lib():
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_set_single_stream.argtypes = [ctypes.c_int]
     L.attn_set_single_stream.restype = ctypes.c_int
+    L.attn_set_trunk_merge.argtypes = [ctypes.c_int]
+    L.attn_set_trunk_merge.restype = ctypes.c_int
     L.attn_version.argtypes = []
     L.attn_version.restype = ctypes.c_char_p
     L.attn_timing_enable.argtypes = [ctypes.c_int]
@@ -119,19 +121,23 @@ def _workspace(nbytes, device, workspace):
 
 
 def attn_fwd(q, k, v, *, head_chunk: int = 0, kv_trunk: int = 0, causal: bool = True,
-             out=None, lse=None, workspace=None):
+             out=None, lse=None, workspace=None, with_lse: bool = True):
     """Causal GQA attention forward.  q [S,Hq,D] bf16 on the GPU; k, v [S,Hkv,D]
     bf16 on the GPU or, with kv_trunk, in pinned host memory.  Returns
-    (o [S,Hq,D] bf16, lse [Hq,S] fp32)."""
+    (o [S,Hq,D] bf16, lse [Hq,S] fp32); with_lse=False (forward-only use)
+    keeps no LSE and returns (o, None)."""
     for n, t in (("q", q), ("k", k), ("v", v)):
         _bf16(n, t)
     S, Hq, Hkv, D = _dims(q, k)
     dev = q.device
     o = torch.empty_like(q) if out is None else out
-    l = torch.empty((Hq, S), dtype=torch.float32, device=dev) if lse is None else lse
+    l = None
+    if with_lse:
+        l = torch.empty((Hq, S), dtype=torch.float32, device=dev) if lse is None else lse
     nb = fwd_workspace_bytes(S, Hq, Hkv, D, causal, head_chunk, kv_trunk)
     ws = _workspace(nb, dev, workspace)
-    rc = lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+    rc = lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                        l.data_ptr() if l is not None else None,
                         S, Hq, Hkv, D, int(causal), head_chunk, kv_trunk, ws.data_ptr(), nb,
                         _stream(dev))
     _check(rc)
@@ -165,6 +171,12 @@ def attn_bwd(q, k, v, o, dout, lse, *, head_chunk: int = 0, kv_trunk: int = 0,
 def set_single_stream(on: bool) -> bool:
     """Run trunk copies on the caller's stream (race check); returns the old value."""
     return bool(lib().attn_set_single_stream(int(on)))
+
+
+def set_trunk_merge(on: bool) -> bool:
+    """Trunked forward by log-sum-exp merge of per-trunk partials (True) instead
+    of the in-kernel carried state (False, default); returns the old value."""
+    return bool(lib().attn_set_trunk_merge(int(on)))
 
 
 def version() -> str:

@@ -31,6 +31,7 @@
  *                    pin_memory) when kv_trunk selects the trunked path.
  *   lse            : fp32 [Hq][S], device memory; natural-log LSE of the
  *                    scaled scores (output of attn_fwd, input of attn_bwd).
+ *                    attn_fwd accepts NULL (forward-only use: no LSE kept).
  *   S >= 1; Hq, Hkv >= 1 with Hq % Hkv == 0; D == 64 or 128;
  *   causal 0 or 1 (1 is the measured case; 0 runs the same kernels).
  *   head_chunk     : query heads per chunk, 0 means Hq; 1..Hq.  Chunks are
@@ -62,8 +63,10 @@
  *   Results are bitwise reproducible run to run and bitwise identical for
  *   every head_chunk value (no atomics; fixed accumulation orders).  The
  *   backward result is also bitwise identical with and without kv_trunk for
- *   the same o and lse; the trunked forward agrees with the untrunked one to
- *   rounding (the log-sum-exp merge rounds).
+ *   the same o and lse, and so is the forward (the softmax state is carried
+ *   from trunk to trunk exactly); with attn_set_trunk_merge(1) the trunked
+ *   forward agrees with the untrunked one to rounding (the log-sum-exp merge
+ *   rounds).
  */
 #ifndef HCATTN_H
 #define HCATTN_H
@@ -99,13 +102,16 @@ size_t attn_bwd_workspace_bytes(int64_t S, int32_t Hq, int32_t Hkv, int32_t D, i
                                 int32_t head_chunk, int64_t kv_trunk);
 
 /*
- * Forward: writes o (bf16, round-to-nearest-even from fp32) and lse.
- * For each chunk the chunk's query heads and the key/value heads they read are
- * packed head-major into the workspace (the one-device stand-in for the
- * per-chunk all-to-all), then the flash kernel runs on them.  With kv_trunk,
- * query trunk m attends to key/value trunks 0..m (0..N-1 non-causal), each
- * copied into a ring slot on the copy stream while the previous trunk
- * computes, and the partial outputs are merged by log-sum-exp.
+ * Forward: writes o (bf16, round-to-nearest-even from fp32) and lse (unless
+ * lse is NULL).  For each chunk the chunk's query heads and the key/value
+ * heads they read are packed head-major into the workspace (the one-device
+ * stand-in for the per-chunk all-to-all), then the flash kernel runs on them.
+ * With kv_trunk, query trunk m attends to key/value trunks 0..m (0..N-1
+ * non-causal), each copied into a ring slot on the copy stream while the
+ * previous trunk computes; the query trunk's running softmax state (O, the
+ * running maximum, row sums; fp32) passes from trunk to trunk through the
+ * workspace, or, after attn_set_trunk_merge(1), each trunk's normalised
+ * partial output is merged into the running one by log-sum-exp.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t S,
              int32_t Hq, int32_t Hkv, int32_t D, int32_t causal, int32_t head_chunk,
@@ -134,6 +140,18 @@ const char* attn_last_error(void);
  * bitwise equal to the overlapped run).  Returns the previous setting.
  */
 int attn_set_single_stream(int on);
+
+/*
+ * Schedule of the trunked forward.  on == 0 (the default): the flash kernel
+ * carries the running softmax state across key/value trunks (result bitwise
+ * equal to the untrunked forward; no merge pass).  on != 0: every trunk
+ * yields a normalised fp32 partial output and its LSE, folded into the
+ * running output by a log-sum-exp merge pass after each trunk, the order the
+ * FPDT talk summary describes ("Technical Deep Dive": the softmax statistics
+ * of a query trunk are updated until its final output).  Both need the same
+ * workspace.  Process-wide; returns the previous setting.
+ */
+int attn_set_trunk_merge(int on);
 
 /*
  * Kernel timing for measurement tools.  While enabled, every kernel the
