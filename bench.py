@@ -38,6 +38,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=12288,
                     help="tokens of the CPU-oracle sample (one GQA group)")
+    ap.add_argument("--kv-trunk", type=int, default=-1,
+                    help="key/value trunk length in tokens (default: the workload's; 0 = untrunked)")
+    ap.add_argument("--trunk-merge", action="store_true",
+                    help="trunked forward by per-trunk log-sum-exp merge (default: carried state)")
+    ap.add_argument("--h2d-probe", action="store_true",
+                    help="also time one pinned-host to device copy of the K/V trunk size")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, run one plain device-to-device copy of MIB MiB "
                          "(the known-size reference for HBM byte counters)")
@@ -142,8 +148,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     S, Hq, Hkv, D, T = w.S, w.Hq, w.Hkv, w.D, w.kv_trunk
+    if args.kv_trunk >= 0:
+        T = args.kv_trunk
     causal = True
 
+    if args.trunk_merge:
+        hcm.set_trunk_merge(True)
     inp = attention_inputs(S, Hq, Hkv, D, w.wid, device=dev)
     if w.kv_on_host:
         for n in ("k", "v"):
@@ -259,6 +269,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "S": S, "Hq": Hq, "Hkv": Hkv, "D": D,
                    "head_chunk": hc, "kv_trunk": T, "kv_on_host": w.kv_on_host,
+                   "trunk_schedule": ("merge" if args.trunk_merge else "carry") if T else None,
                    "causal": causal, "batch": 1},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(2.0 * S * S * D * Hq / (r["fwd_ms"] / 1e3) / 1e12, 2),
@@ -288,6 +299,21 @@ def main():
             "workspace_ratio": round(max(r["ws_fwd"], r["ws_bwd"]) /
                                      max(r2["ws_fwd"], r2["ws_bwd"]), 4),
         }
+    if args.h2d_probe and T > 0:
+        # host-to-device rate of one trunk's K and V (the per-trunk copy)
+        hb = torch.empty(2 * T * Hkv * D, dtype=torch.bfloat16, pin_memory=True)
+        db = torch.empty(hb.shape, dtype=hb.dtype, device=dev)
+        db.copy_(hb, non_blocking=True)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            db.copy_(hb, non_blocking=True)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        line["h2d_probe"] = {"bytes": hb.numel() * 2, "ms": round(ms, 4),
+                             "gbs": round(hb.numel() * 2 / (ms / 1e3) / 1e9, 2)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_oracle_baseline(D, Hq // Hkv, args.cpu_tokens)
     print(json.dumps(line), flush=True)
