@@ -66,13 +66,16 @@ FAMILY_SOURCES = {"fwd": ["fwd.hip"], "dkdv": ["bwd.hip"], "dq": ["bwd.hip"]}
 COMMON_SOURCES = ["device_common.h", "kernels.h"]
 
 
+ROOT_DIR = os.path.dirname(os.path.abspath(__file__))
+CSRC_DIR = os.path.join(ROOT_DIR, "head_chunked_context_amd", "csrc")
+PROFILES_DIR = os.path.join(ROOT_DIR, "profiles")
+
+
 def kernel_source_hash(family: str) -> str:
     import hashlib
-    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "head_chunked_context_amd",
-                        "csrc")
     h = hashlib.sha256()
     for name in FAMILY_SOURCES.get(family, []) + COMMON_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(CSRC_DIR, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
@@ -82,8 +85,7 @@ def measured_traffic(family: str, shape: str, hc: int):
     counter summary (profiles/traffic_<family>_<shape>_hc<hc>.md, line
     `traffic_json: {...}`), or None when there is none or the kernel's sources
     changed since the counters were taken."""
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                        f"traffic_{family}_{shape}_hc{hc}.md")
+    path = os.path.join(PROFILES_DIR, f"traffic_{family}_{shape}_hc{hc}.md")
     if not os.path.exists(path):
         return None
     with open(path) as f:

@@ -114,6 +114,25 @@ def test_kv_trunks_match_oracle_and_untrunked_backward(kv_host):
     check_bwd(inp, g)
 
 
+@pytest.mark.parametrize("causal,D", [(False, 128), (True, 64)])
+def test_trunks_non_causal_and_d64(causal, D):
+    # non-causal: every query trunk attends all key trunks; D = 64 tiles
+    S, Hq, Hkv, hc, T = 900, 4, 1, 2, 256
+    inp = inputs_cpu(S, Hq, Hkv, D, 37)
+    d = to_dev(inp)
+    dt = to_dev(inp, kv_host=True)
+    print(f"trunked S={S} D={D} causal={causal} T={T}", flush=True)
+    ot, lt = gpu_fwd(dt, hc, trunk=T, causal=causal)
+    check_fwd(inp, ot, lt, causal)
+    o, lse = gpu_fwd(d, hc, causal=causal)
+    assert torch.equal(ot, o) and torch.equal(lt, lse)
+    g = gpu_bwd(d, o, lse, hc, causal=causal)
+    gt = gpu_bwd(dt, o, lse, hc, trunk=T, causal=causal)
+    for a, b, n in zip(g, gt, ("dq", "dk", "dv")):
+        assert torch.equal(a.cpu(), b.cpu()), f"trunked {n} differs bitwise from untrunked"
+    check_bwd(inp, g, causal)
+
+
 @pytest.mark.parametrize("kv_host", [False, True])
 def test_trunk_merge_schedule_matches_oracle(kv_host):
     # per-trunk partial outputs merged by log-sum-exp: equal to rounding
