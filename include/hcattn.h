@@ -52,6 +52,13 @@
  *   not alias inputs or the workspace.  Calls from several host threads on one
  *   device are serialised while they enqueue work.
  *
+ * Graph capture
+ *   attn_fwd and attn_bwd may be captured into a HIP graph on `stream`: the
+ *   library's copy stream forks from and joins `stream` through events, and
+ *   nothing else is enqueued (no memset nodes).  Make one ordinary call on the
+ *   device first (it creates the copy stream and events), keep kernel timing
+ *   off while capturing, and pass buffers that stay valid for every replay.
+ *
  * Errors
  *   Every entry point returns ATTN_OK (0) or a negative status.  Argument
  *   checks run before anything is enqueued; on failure nothing is enqueued.

@@ -209,3 +209,51 @@ def test_errors_are_reported_without_work():
     with pytest.raises(HcAttnError) as e:
         attn_fwd(d["q"], d["k"], d["v"], head_chunk=5)  # more than Hq
     assert e.value.code == -1
+
+
+@pytest.mark.parametrize("trunk,kv_host", [(0, False), (256, True)])
+def test_hip_graph_capture_replays_bitwise(trunk, kv_host):
+    # attn_fwd + attn_bwd captured into one graph (the library's copy stream
+    # forks from and joins the captured stream); every replay, with eager work
+    # in between, gives the eager result bit for bit
+    from head_chunked_context_amd import (attn_bwd, attn_fwd, bwd_workspace_bytes,
+                                          fwd_workspace_bytes)
+    S, Hq, Hkv, D, hc = 640, 4, 2, 128, 2
+    inp = inputs_cpu(S, Hq, Hkv, D, 38)
+    d = to_dev(inp, kv_host=kv_host)
+    q, k, v, do = d["q"], d["k"], d["v"], d["dout"]
+    o_e, l_e = attn_fwd(q, k, v, head_chunk=hc, kv_trunk=trunk)
+    g_e = attn_bwd(q, k, v, o_e, do, l_e, head_chunk=hc, kv_trunk=trunk)
+    torch.cuda.synchronize()
+    o, lse = torch.empty_like(o_e), torch.empty_like(l_e)
+    dq = torch.empty_like(g_e[0])
+    dk = torch.empty(k.shape, dtype=k.dtype, device=k.device, pin_memory=kv_host)
+    dv = torch.empty(v.shape, dtype=v.dtype, device=v.device, pin_memory=kv_host)
+    fws = torch.empty(fwd_workspace_bytes(S, Hq, Hkv, D, True, hc, trunk), dtype=torch.uint8,
+                      device=DEV)
+    bws = torch.empty(bwd_workspace_bytes(S, Hq, Hkv, D, True, hc, trunk), dtype=torch.uint8,
+                      device=DEV)
+
+    def step():
+        attn_fwd(q, k, v, head_chunk=hc, kv_trunk=trunk, out=o, lse=lse, workspace=fws)
+        attn_bwd(q, k, v, o, do, lse, head_chunk=hc, kv_trunk=trunk, dq=dq, dk=dk, dv=dv,
+                 workspace=bws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, capture_error_mode="thread_local"):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (o, lse, dq, dk, dv):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for x, y, n in zip((o, lse, dq, dk, dv), (o_e, l_e) + tuple(g_e), ("o", "lse", "dq", "dk", "dv")):
+            assert torch.equal(x.cpu(), y.cpu()), f"replay {rep}: {n} differs from the eager result"
