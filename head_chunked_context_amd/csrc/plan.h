@@ -91,8 +91,10 @@ static inline int make_plan(bool bwd, int64_t S, int Hq, int Hkv, int D, int cau
         snprintf(err, errlen, "head dimension %d not supported (64 or 128)", D);
         return -2;
     }
-    if (S > (int64_t(1) << 31)) {
-        snprintf(err, errlen, "S = %lld exceeds 2^31 rows", (long long)S);
+    // row and key offsets inside the kernels are 32-bit (with up to a tile of
+    // headroom), so sequences are limited to 2^30 tokens
+    if (S > (int64_t(1) << 30)) {
+        snprintf(err, errlen, "S = %lld exceeds 2^30 tokens", (long long)S);
         return -2;
     }
     Plan p;

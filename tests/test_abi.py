@@ -93,6 +93,7 @@ def test_head_chunk_zero_means_all_heads():
     ((64, 4, 2, 128, 1, 5, 0), -1),      # head_chunk > Hq
     ((4096, 4, 2, 128, 1, 0, 100), -1),  # trunk not a multiple of 256
     ((64, 4, 2, 128, 1, -1, 0), -1),
+    (((1 << 30) + 1, 4, 2, 128, 1, 0, 0), -2),  # beyond 2^30 tokens
 ])
 def test_invalid_arguments_return_status_before_any_gpu_work(args, code):
     L = lib()
