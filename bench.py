@@ -38,8 +38,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=12288,
                     help="tokens of the CPU-oracle sample (one GQA group)")
-    ap.add_argument("--kv-trunk", type=int, default=-1,
-                    help="key/value trunk length in tokens (default: the workload's; 0 = untrunked)")
+    ap.add_argument("--kv-trunk", default="-1",
+                    help="key/value trunk length in tokens (default: the workload's; 0 = "
+                         "untrunked; 'auto' = attn_pick_kv_trunk for --budget-gib)")
+    ap.add_argument("--budget-gib", type=float, default=0.0,
+                    help="workspace budget for --kv-trunk auto (GiB; 0 = no limit)")
     ap.add_argument("--trunk-merge", action="store_true",
                     help="trunked forward by per-trunk log-sum-exp merge (default: carried state)")
     ap.add_argument("--h2d-probe", action="store_true",
@@ -150,8 +153,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     S, Hq, Hkv, D, T = w.S, w.Hq, w.Hkv, w.D, w.kv_trunk
-    if args.kv_trunk >= 0:
-        T = args.kv_trunk
+    if args.kv_trunk == "auto":
+        T = hcm.pick_kv_trunk(S, Hq, Hkv, D, True, hc, kv_on_host=w.kv_on_host,
+                              budget_bytes=int(args.budget_gib * 2**30))
+    elif int(args.kv_trunk) >= 0:
+        T = int(args.kv_trunk)
     causal = True
 
     if args.trunk_merge:
@@ -272,6 +278,8 @@ def main():
         "config": {"workload": w.name, "S": S, "Hq": Hq, "Hkv": Hkv, "D": D,
                    "head_chunk": hc, "kv_trunk": T, "kv_on_host": w.kv_on_host,
                    "trunk_schedule": ("merge" if args.trunk_merge else "carry") if T else None,
+                   "kv_trunk_choice": ("auto" if args.kv_trunk == "auto"
+                                       else "given" if int(args.kv_trunk) >= 0 else "workload"),
                    "causal": causal, "batch": 1},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(2.0 * S * S * D * Hq / (r["fwd_ms"] / 1e3) / 1e12, 2),

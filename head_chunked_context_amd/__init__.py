@@ -5,6 +5,6 @@
 use, so importing this package does not need a GPU.
 """
 from .hcattn import (HcAttnError, attn_bwd, attn_fwd, bwd_workspace_bytes,  # noqa: F401
-                     fwd_workspace_bytes, last_error, set_single_stream, set_trunk_merge,
-                     timing_enable,
-                     timing_bytes, timing_read, timing_reset, version)
+                     fwd_workspace_bytes, last_error, pick_kv_trunk, set_single_stream,
+                     set_trunk_merge, timing_bytes, timing_enable, timing_read, timing_reset,
+                     version)

@@ -616,6 +616,29 @@ size_t attn_bwd_workspace_bytes(int64_t S, int32_t Hq, int32_t Hkv, int32_t D, i
     return pl.total;
 }
 
+int attn_pick_kv_trunk(int64_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t causal,
+                       int32_t head_chunk, int32_t kv_on_host, int32_t with_backward,
+                       size_t budget_bytes, double link_bytes_per_s, double flops_per_s,
+                       int32_t num_cus, int64_t* kv_trunk) {
+    g_err[0] = 0;
+    if (kv_trunk == nullptr) return fail(ATTN_EPOINTER, "kv_trunk is NULL");
+    // defaults: the pinned-host-to-device copy rate and the forward kernel's
+    // rate measured on one MI355X, and its compute-unit count
+    const double link = link_bytes_per_s > 0.0 ? link_bytes_per_s : 57.0e9;
+    const double flops = flops_per_s > 0.0 ? flops_per_s : 1.0e15;
+    const int cus = num_cus > 0 ? num_cus : 256;
+    char msg[256];
+    int64_t t = 0;
+    const int r = hc::pick_kv_trunk(S, Hq, Hkv, D, causal, head_chunk, kv_on_host != 0,
+                                    with_backward != 0, budget_bytes, link, flops, cus, &t, msg,
+                                    sizeof msg);
+    if (r == -1) return fail(ATTN_EINVAL, "%s", msg);
+    if (r == -2) return fail(ATTN_EUNSUPPORTED, "%s", msg);
+    if (r == -3) return fail(ATTN_EWORKSPACE, "%s", msg);
+    *kv_trunk = t;
+    return ATTN_OK;
+}
+
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t S,
              int32_t Hq, int32_t Hkv, int32_t D, int32_t causal, int32_t head_chunk,
              int64_t kv_trunk, void* workspace, size_t workspace_bytes, void* stream) {

@@ -169,4 +169,74 @@ static inline int make_plan(bool bwd, int64_t S, int Hq, int Hkv, int D, int cau
     return 0;
 }
 
+// Key/value trunk length for a memory budget (FPDT summary, "Technical Deep
+// Dive": the trunk is sized so that fetching the next trunk takes about as
+// long as computing on the current one; past that point a longer trunk only
+// costs device memory).  Candidates are T = 256 * 2^k < S.  T qualifies when
+//   fits:     the workspace of attn_fwd (and of attn_bwd, if with_bwd) at T is
+//             within the budget (budget 0 = no limit);
+//   balanced: with K/V in host memory, copying one trunk of the chunk's K and
+//             V heads (4 T kvc D bytes) takes no longer than one full
+//             query-trunk x key-trunk block of the forward (4 T^2 D hc FLOP):
+//             T >= kvc * flops / (hc * link);
+//   fills:    one forward launch has at least two rounds of workgroups (128
+//             query rows each, two resident per compute unit):
+//             ceil(T / 128) * hc >= 4 * num_cus.
+// The smallest qualifying T wins.  Device-resident K/V whose untrunked
+// workspaces fit take T = 0 (no trunks).  When no T qualifies, the longest
+// one that fits is taken.  Returns 0, -1 (bad arguments or host K/V with
+// S <= 256, which cannot be trunked) or -3 (nothing fits the budget).
+static inline int pick_kv_trunk(int64_t S, int Hq, int Hkv, int D, int causal, int head_chunk,
+                                bool kv_on_host, bool with_bwd, size_t budget, double link,
+                                double flops, int num_cus, int64_t* out, char* err, size_t errlen) {
+    Plan p;
+    int r = make_plan(false, S, Hq, Hkv, D, causal, head_chunk, 0, &p, err, errlen);
+    if (r) return r;
+    if (!(link > 0.0) || !(flops > 0.0) || num_cus < 1) {
+        snprintf(err, errlen, "link rate, FLOP rate and compute-unit count must be positive");
+        return -1;
+    }
+    auto need = [&](int64_t T, size_t* bytes) -> int {
+        Plan f, b;
+        int rr = make_plan(false, S, Hq, Hkv, D, causal, head_chunk, T, &f, err, errlen);
+        if (rr) return rr;
+        size_t n = f.total;
+        if (with_bwd) {
+            rr = make_plan(true, S, Hq, Hkv, D, causal, head_chunk, T, &b, err, errlen);
+            if (rr) return rr;
+            if (b.total > n) n = b.total;
+        }
+        *bytes = n;
+        return 0;
+    };
+    auto fits = [&](size_t bytes) { return budget == 0 || bytes <= budget; };
+    size_t bytes = 0;
+    if (!kv_on_host) {
+        if ((r = need(0, &bytes))) return r;
+        if (fits(bytes)) { *out = 0; return 0; }
+    }
+    int64_t best_fit = -1, pick = -1;
+    for (int64_t T = kTrunkGranule; T < S; T *= 2) {
+        if ((r = need(T, &bytes))) return r;
+        if (!fits(bytes)) break;  // the workspaces grow with T
+        best_fit = T;
+        const bool balanced =
+            !kv_on_host || (double)T >= (double)p.kvc * flops / ((double)p.hc * link);
+        const bool fills = (T + 127) / 128 * p.hc >= 4 * (int64_t)num_cus;
+        if (balanced && fills) { pick = T; break; }
+    }
+    if (pick < 0) pick = best_fit;
+    if (pick < 0) {
+        if (kv_on_host && S <= kTrunkGranule) {
+            snprintf(err, errlen, "S = %lld is too short to trunk (host K/V need S > %lld)",
+                     (long long)S, (long long)kTrunkGranule);
+            return -1;
+        }
+        snprintf(err, errlen, "no key/value trunk fits a workspace budget of %zu bytes", budget);
+        return -3;
+    }
+    *out = pick;
+    return 0;
+}
+
 }  // namespace hc

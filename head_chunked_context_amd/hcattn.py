@@ -47,6 +47,10 @@ def lib():
     L.attn_fwd.restype = ctypes.c_int
     L.attn_bwd.argtypes = [vp] * 9 + shape + [vp, sz, vp]
     L.attn_bwd.restype = ctypes.c_int
+    L.attn_pick_kv_trunk.argtypes = shape[:6] + [ctypes.c_int32, ctypes.c_int32, sz,
+                                                  ctypes.c_double, ctypes.c_double,
+                                                  ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]
+    L.attn_pick_kv_trunk.restype = ctypes.c_int
     L.attn_last_error.argtypes = []
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_set_single_stream.argtypes = [ctypes.c_int]
@@ -103,6 +107,17 @@ def bwd_workspace_bytes(S, Hq, Hkv, D, causal=True, head_chunk=0, kv_trunk=0) ->
     if n == 0:
         raise HcAttnError(-1, last_error())
     return n
+
+
+def pick_kv_trunk(S, Hq, Hkv, D, causal=True, head_chunk=0, *, kv_on_host=False,
+                  with_backward=True, budget_bytes=0, link_bytes_per_s=0.0, flops_per_s=0.0,
+                  num_cus=0) -> int:
+    """kv_trunk for a device-memory budget (0 = untrunked); see attn_pick_kv_trunk."""
+    t = ctypes.c_int64(-1)
+    _check(lib().attn_pick_kv_trunk(S, Hq, Hkv, D, int(causal), head_chunk, int(kv_on_host),
+                                    int(with_backward), budget_bytes, float(link_bytes_per_s),
+                                    float(flops_per_s), num_cus, ctypes.byref(t)))
+    return int(t.value)
 
 
 def _stream(device) -> int:

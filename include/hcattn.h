@@ -110,6 +110,30 @@ size_t attn_bwd_workspace_bytes(int64_t S, int32_t Hq, int32_t Hkv, int32_t D, i
                                 int32_t head_chunk, int64_t kv_trunk);
 
 /*
+ * Picks kv_trunk for a device-memory budget, the way the FPDT summary sizes
+ * trunks ("Technical Deep Dive" and the trunk-size Q&A: the copy of the next
+ * trunk should take about as long as computing on the current one; longer
+ * trunks then only cost memory).  Candidates are 256 * 2^k < S.  A candidate
+ * qualifies when (a) the workspace of attn_fwd, and of attn_bwd if
+ * with_backward, fits budget_bytes (0 = no limit); (b) if kv_on_host, copying
+ * one trunk of the chunk's K and V heads over a link of link_bytes_per_s is
+ * no slower than the forward's FLOPs on one query-trunk x key-trunk block at
+ * flops_per_s; (c) one forward launch has at least two rounds of workgroups
+ * on num_cus compute units.  The smallest qualifying candidate is written to
+ * *kv_trunk; device-resident K/V whose untrunked workspaces fit get 0; if
+ * none qualifies, the longest candidate that fits.  Rates and counts <= 0
+ * take the values measured on one MI355X: 57e9 B/s pinned-host copies, 1e15
+ * FLOP/s forward, 256 compute units.  Host-only arithmetic (no HIP call).
+ * Returns ATTN_OK; ATTN_EINVAL / ATTN_EUNSUPPORTED for shapes attn_fwd would
+ * reject (and host K/V with S <= 256); ATTN_EWORKSPACE when no candidate fits
+ * the budget; ATTN_EPOINTER when kv_trunk is NULL.
+ */
+int attn_pick_kv_trunk(int64_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t causal,
+                       int32_t head_chunk, int32_t kv_on_host, int32_t with_backward,
+                       size_t budget_bytes, double link_bytes_per_s, double flops_per_s,
+                       int32_t num_cus, int64_t* kv_trunk);
+
+/*
  * Forward: writes o (bf16, round-to-nearest-even from fp32) and lse (unless
  * lse is NULL).  For each chunk the chunk's query heads and the key/value
  * heads they read are packed head-major into the workspace (the one-device

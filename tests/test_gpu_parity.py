@@ -133,6 +133,24 @@ def test_trunks_non_causal_and_d64(causal, D):
     check_bwd(inp, g, causal)
 
 
+def test_picked_trunk_runs_bitwise_equal_to_untrunked():
+    # the trunk chosen for a workspace budget that the untrunked run exceeds
+    from head_chunked_context_amd import fwd_workspace_bytes, pick_kv_trunk
+    S, Hq, Hkv, D, hc = 3000, 4, 2, 128, 2
+    budget = fwd_workspace_bytes(S, Hq, Hkv, D, True, hc, 0) // 2
+    T = pick_kv_trunk(S, Hq, Hkv, D, True, hc, kv_on_host=True, with_backward=False,
+                      budget_bytes=budget)
+    assert 0 < T < S and fwd_workspace_bytes(S, Hq, Hkv, D, True, hc, T) <= budget
+    inp = inputs_cpu(S, Hq, Hkv, D, 38)
+    d = to_dev(inp)
+    dt = to_dev(inp, kv_host=True)
+    print(f"picked trunk S={S} T={T}", flush=True)
+    ot, lt = gpu_fwd(dt, hc, trunk=T)
+    o, lse = gpu_fwd(d, hc)
+    assert torch.equal(ot, o) and torch.equal(lt, lse)
+    check_fwd(inp, ot, lt)
+
+
 @pytest.mark.parametrize("kv_host", [False, True])
 def test_trunk_merge_schedule_matches_oracle(kv_host):
     # per-trunk partial outputs merged by log-sum-exp: equal to rounding
