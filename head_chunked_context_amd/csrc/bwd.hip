@@ -24,9 +24,10 @@
 // MFMAs.  At the end the upper-half wave hands its dK/dV partial to its
 // partner through LDS, which adds it after its own (fixed order).
 //
-// dq_kernel: workgroup = 4 waves x 32 query rows of one head; Q and dO stay in
-// registers; 64-key tiles of K and V are loaded straight into LDS like the
-// forward:
+// dq_kernel: workgroup = NW waves x 32 query rows of one head (NW = 8 with a
+// 4-slot K/V ring for large launches, NW = 4 double-buffered otherwise, as in
+// the forward); Q and dO stay in registers; 64-key tiles of K and V are loaded
+// straight into LDS:
 //   S^T = K Q^T,  dP^T = V dO^T,  dQ^T[d][q] += K^T dS^T (transposed K reads)
 #include "device_common.h"
 #include "kernels.h"
@@ -314,12 +315,14 @@ __device__ __forceinline__ void dq_ds(const f32x16 (&s)[NB], const f32x16 (&dp)[
     }
 }
 
-template <int HD>
-__global__ __launch_bounds__(256, 2) void dq_kernel(DqParams p) {
-    constexpr int BN = 64, WQ = 32, BM = 128;
+template <int HD, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
+    constexpr int BN = 64, WQ = 32, BM = NW * WQ;
     constexpr int NS = HD / 16, NDB = HD / 32;
     constexpr int TILE = BN * HD * 2;
-    __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [buf][K / V]
+    constexpr int NBUF = NW == 8 ? 4 : 2;  // K/V ring slots (tiles in flight: NBUF - 1)
+    constexpr int NI = (NW == 8 ? 1 : 2) * (64 * HD * 2 / 4 / 1024);  // loads per wave per tile
+    __shared__ __attribute__((aligned(1024))) char smem[NBUF][2][TILE];  // [slot][K / V]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values scalar
@@ -379,10 +382,19 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(DqParams p) {
     const int ntiles = kend > 0 ? (int)((kend + BN - 1) / BN) : 0;
     const int ntiles_w = kend_w > 0 ? (int)((kend_w + BN - 1) / BN) : 0;
 
-    if (ntiles > 0) {
-        direct_tile64<HD>(smem[0][0], kh, p.k_rs, p.nk, wave, lane);
-        direct_tile64<HD>(smem[0][1], vh, p.v_rs, p.nk, wave, lane);
-    }
+    // 8 waves: K tiles by waves 0-3, V tiles by waves 4-7; 4 waves: both
+    const int kv_sel = wave >> 2;
+    const uint16_t* kvh = kv_sel == 0 ? kh : vh;
+    const int64_t kv_rs = kv_sel == 0 ? p.k_rs : p.v_rs;
+    auto issue = [&](int t) {
+        const int64_t nb = (int64_t)t * BN;
+        if constexpr (NW == 8) {
+            direct_tile64<HD>(smem[t % NBUF][kv_sel], kvh + nb * kv_rs, kv_rs, p.nk - nb, wave & 3, lane);
+        } else {
+            direct_tile64<HD>(smem[t % NBUF][0], kh + nb * p.k_rs, p.k_rs, p.nk - nb, wave, lane);
+            direct_tile64<HD>(smem[t % NBUF][1], vh + nb * p.v_rs, p.v_rs, p.nk - nb, wave, lane);
+        }
+    };
     wait_vm_loads();
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -393,16 +405,16 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(DqParams p) {
     settle(dlt);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) settle(acc[db]);
+    const int pre = ntiles < NBUF - 1 ? ntiles : NBUF - 1;
+    for (int t = 0; t < pre; ++t) issue(t);
+    wait_tiles_after<NI>(pre - 1);
     __syncthreads();
 
     const int64_t qrel_base = myq - p.k_pos0;  // query position relative to key 0
     for (int j = 0; j < ntiles; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < ntiles) {
-            const int64_t nb = (int64_t)(j + 1) * BN;
-            direct_tile64<HD>(smem[buf ^ 1][0], kh + nb * p.k_rs, p.k_rs, p.nk - nb, wave, lane);
-            direct_tile64<HD>(smem[buf ^ 1][1], vh + nb * p.v_rs, p.v_rs, p.nk - nb, wave, lane);
-        }
+        const int buf = j % NBUF;
+        // the slot of tile j + NBUF - 1 held tile j - 1, released by the last barrier
+        if (j + NBUF - 1 < ntiles) issue(j + NBUF - 1);
         if (j < ntiles_w) {
             const char* Ks = smem[buf][0];
             const char* Vs = smem[buf][1];
@@ -440,7 +452,11 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(DqParams p) {
                 }
             }
         }
-        wait_vm_loads();
+        // tile j + 1 must have landed; later tiles stay in flight
+        {
+            const int last = j + NBUF - 1 < ntiles ? j + NBUF - 1 : ntiles - 1;
+            wait_tiles_after<NI>(last - (j + 1));
+        }
         __syncthreads();
     }
 
@@ -494,15 +510,22 @@ hipError_t launch_dkdv_reduce(const DkdvReduceParams& p, hipStream_t st) {
 
 hipError_t launch_dq(const DqParams& p, int D, hipStream_t st) {
     if (p.nq <= p.q_begin || p.nh <= 0) return hipSuccess;
-    const int64_t qtb = p.q_begin / kDqBlockM;
-    const int64_t blocks = ((p.nq + kDqBlockM - 1) / kDqBlockM - qtb) * p.nh;
+    if (D != 128 && D != 64) return hipErrorInvalidValue;
+    // 256-row workgroups when they fill the chip; 128-row ones otherwise (the
+    // first row must start a workgroup: trunk starts are multiples of 256)
+    const bool wide = ((p.nq + 255) / 256 - p.q_begin / 256) * p.nh >= kWideMinBlocks;
+    const int bm = wide ? 256 : 128;
+    if (p.q_begin % bm != 0) return hipErrorInvalidValue;
+    const int64_t blocks = ((p.nq + bm - 1) / bm - p.q_begin / bm) * p.nh;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (D == 128)
-        hipLaunchKernelGGL(dq_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, st, p);
-    else if (D == 64)
-        hipLaunchKernelGGL(dq_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, st, p);
-    else
-        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)blocks), block(wide ? 512 : 256);
+    if (D == 128) {
+        if (wide) hipLaunchKernelGGL((dq_kernel<128, 8>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((dq_kernel<128, 4>), grid, block, 0, st, p);
+    } else {
+        if (wide) hipLaunchKernelGGL((dq_kernel<64, 8>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((dq_kernel<64, 4>), grid, block, 0, st, p);
+    }
     return hipGetLastError();
 }
 

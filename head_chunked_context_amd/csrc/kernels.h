@@ -142,10 +142,12 @@ hipError_t launch_dkdv(const DkdvParams& p, int D, hipStream_t st);
 hipError_t launch_dkdv_reduce(const DkdvReduceParams& p, hipStream_t st);
 hipError_t launch_dq(const DqParams& p, int D, hipStream_t st);
 
-// Tile sizes the host planner relies on (query rows per forward/dQ workgroup,
-// keys per dK/dV workgroup).
-constexpr int kFwdBlockM = 128;
-constexpr int kDqBlockM = 128;
+// Launch shapes.  The forward and dQ kernels take 256-row workgroups (8
+// waves, one per compute unit) once a launch has at least kWideMinBlocks of
+// them, else 128-row workgroups (4 waves, two per compute unit); the rows of
+// each query are computed the same way in both, bit for bit.  dK/dV
+// workgroups take 128 keys.
+constexpr int kWideMinBlocks = 256;
 constexpr int kDkdvBlockN = 128;
 
 }  // namespace hc

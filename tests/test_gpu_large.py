@@ -2,7 +2,9 @@
 by one, plus properties that hold at any size.
 
 * Workload 2 (S=32768, 32/8/128; head_chunk 4 and 32, the configuration the
-  benchmark times) runs in the default GPU suite.
+  benchmark times) runs in the default GPU suite, and so does a ragged
+  S=16484 case whose head_chunk 4 and 1 runs take the 256-row and the 128-row
+  workgroup shapes of the forward and dQ kernels.
 * Workloads 3, 4 and 5 (S=262144 / 524288 / 5242880) take from tens of
   seconds to several minutes of GPU time; they run when HCATTN_SLOW_TESTS=1.
 
@@ -112,6 +114,24 @@ def test_workload2_full_size_head_chunks_and_samples():
     check_rows(d, o, lse, dq, sample_rows(w.S))
     check_last_keys(d, dk, dv, n=32)
     check_sum_identities(d, dk, dv, w.Hq // w.Hkv)
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_wide_and_narrow_workgroups_give_the_same_bits(D):
+    # head_chunk 4 launches 65 x 4 = 260 forward / dQ workgroups of 256 rows
+    # (8 waves, deep K/V ring); head_chunk 1 launches fewer than 256 and takes
+    # the 128-row shape: every row must come out bit for bit the same
+    S, Hq, Hkv = 16484, 4, 1
+    d = attention_inputs(S, Hq, Hkv, D, 7, device=DEV)
+    print(f"wide/narrow S={S} D={D} hc=4", flush=True)
+    a = run(d, 4)
+    print(f"wide/narrow S={S} D={D} hc=1", flush=True)
+    b = run(d, 1)
+    for x, y, n in zip(a, b, ("o", "lse", "dq", "dk", "dv")):
+        assert torch.equal(x, y), f"{n} differs between the wide and narrow launches"
+    o, lse, dq, dk, dv = a
+    check_rows(d, o, lse, dq, sample_rows(S, n_random=4))
+    check_last_keys(d, dk, dv, n=16)
 
 
 @slow
