@@ -147,6 +147,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
     wait_vm_loads();
     __syncthreads();
 
+    const OperandOffsets<HD> off(lane);  // K / V / Q / dO operand reads
     // positions relative to this wave's first key, in 32-bit
     const int64_t wkpos = p.k_pos0 + wj0;
     const int krel = l32;
@@ -162,8 +163,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
             f32x16 sacc[1], dpacc[1];
 #pragma unroll
             for (int st = 0; st < NS; ++st) {
-                const int ko = lds_off<HD>(kw * 32 + l32, st * 16 + hi * 8);
-                const int qo = lds_off<HD>(rh * 32 + l32, st * 16 + hi * 8);
+                const int ko = off.row[st] + kw * 32 * HD * 2;
+                const int qo = off.row[st] + rh * 32 * HD * 2;
                 const bf16x8 kf = lds_read_b128(skv[0], ko);
                 const bf16x8 vf = lds_read_b128(skv[1], ko);
                 const bf16x8 aq = lds_read_b128(Qs, qo);
@@ -192,9 +193,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
             for (int db = 0; db < NDB; ++db) {
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
-                    bf16x8 ao = lds_read_tr_operand<HD>(Os, rh * 32 + h2 * 16, db * 32, lane);
+                    bf16x8 ao = lds_read_tr_at<HD>(Os, off, rh * 32 + h2 * 16, db);
                     dv[db] = mfma32(ao, pb[0][h2], dv[db]);
-                    bf16x8 aq = lds_read_tr_operand<HD>(Qs, rh * 32 + h2 * 16, db * 32, lane);
+                    bf16x8 aq = lds_read_tr_at<HD>(Qs, off, rh * 32 + h2 * 16, db);
                     dk[db] = mfma32(aq, dsb[0][h2], dk[db]);
                 }
             }
@@ -410,6 +411,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
     wait_tiles_after<NI>(pre - 1);
     __syncthreads();
 
+    const OperandOffsets<HD> off(lane);         // K / V operand reads
     const int64_t qrel_base = myq - p.k_pos0;  // query position relative to key 0
     for (int j = 0; j < ntiles; ++j) {
         const int buf = j % NBUF;
@@ -427,7 +429,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
                 f32x16 s[1], dp[1];
 #pragma unroll
                 for (int st = 0; st < NS; ++st) {
-                    const int o = lds_off<HD>(b * 32 + l32, st * 16 + hi * 8);
+                    const int o = off.row[st] + b * 32 * HD * 2;
                     const bf16x8 ak = lds_read_b128(Ks, o);
                     const bf16x8 av = lds_read_b128(Vs, o);
                     s[0] = mfma32(ak, qf[st], st == 0 ? f32x16{} : s[0]);
@@ -446,7 +448,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
                 for (int db = 0; db < NDB; ++db) {
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) {
-                        bf16x8 ak = lds_read_tr_operand<HD>(Ks, b * 32 + h2 * 16, db * 32, lane);
+                        bf16x8 ak = lds_read_tr_at<HD>(Ks, off, b * 32 + h2 * 16, db);
                         acc[db] = mfma32(ak, dsb[0][h2], acc[db]);
                     }
                 }

@@ -64,18 +64,41 @@ __device__ __forceinline__ s16x4 lds_read_tr(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
-// Transposed A/B operand for 16 reduction indices k0 + {c*4 + 0..3, 8 + c*4 +
-// 0..3} (c = lane / 32) of the 32 columns col0..col0+31 of a row-major tile
-// (reduction index = tile row).  Lane l receives column col0 + l % 32.
+// Per-lane byte offsets of the MFMA operand reads in a [rows][HD] tile,
+// computed once per kernel: row-major 16-byte reads of row (lane % 32) at
+// reduction step st, and the two halves (rows +0..7 and +8..15) of the
+// transposed read of d block db.  The swizzle depends on row % 16 only, so
+// reads 16 * n rows further down are the same offsets plus n * 16 rows of
+// bytes (an immediate), and the loops need no address arithmetic per tile.
 template <int HD>
-__device__ __forceinline__ bf16x8 lds_read_tr_operand(const char* tile, int k0, int col0, int lane) {
-    const int j = lane & 15;
-    const int row = k0 + ((lane >> 5) << 2) + (j >> 2);
-    const int col = col0 + (((lane >> 4) & 1) << 4) + ((j & 3) << 2);
-    s16x4 a = lds_read_tr(tile + lds_off<HD>(row, col));
-    s16x4 b = lds_read_tr(tile + lds_off<HD>(row + 8, col));
-    s16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, ab);
+struct OperandOffsets {
+    int row[HD / 16];
+    int tr[HD / 32][2];
+    __device__ __forceinline__ explicit OperandOffsets(int lane) {
+        const int hi = lane >> 5, l32 = lane & 31;
+#pragma unroll
+        for (int st = 0; st < HD / 16; ++st) row[st] = lds_off<HD>(l32, st * 16 + hi * 8);
+        const int j = lane & 15;
+        const int r = ((lane >> 5) << 2) + (j >> 2);
+        const int c = (((lane >> 4) & 1) << 4) + ((j & 3) << 2);
+#pragma unroll
+        for (int db = 0; db < HD / 32; ++db) {
+            tr[db][0] = lds_off<HD>(r, db * 32 + c);
+            tr[db][1] = lds_off<HD>(r + 8, db * 32 + c);
+        }
+    }
+};
+
+// Transposed A/B operand for the 16 reduction indices k0 + {c*4 + 0..3,
+// 8 + c*4 + 0..3} (c = lane / 32, k0 a multiple of 16) of the 32 columns
+// db*32 .. db*32+31 of a row-major tile (reduction index = tile row): lane l
+// receives column db*32 + l % 32.
+template <int HD>
+__device__ __forceinline__ bf16x8 lds_read_tr_at(const char* tile, const OperandOffsets<HD>& off,
+                                                 int k0, int db) {
+    const s16x4 a = lds_read_tr(tile + off.tr[db][0] + k0 * HD * 2);
+    const s16x4 b = lds_read_tr(tile + off.tr[db][1] + k0 * HD * 2);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // max / sum of x over lanes l and l ^ 32; the same bits land in both lanes

@@ -183,6 +183,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(FwdParams p) {
     wait_tiles_after<NI>(pre - 1);
     __syncthreads();
 
+    // per-lane offsets of the K (row-major) and V (transposed) operand reads
+    const OperandOffsets<HD> off(lane);
     // this lane's query position relative to the key positions of tile 0
     const int64_t qrel_base = p.q_pos0 + myq - p.k_pos0;
     for (int j = 0; j < ntiles; ++j) {
@@ -196,12 +198,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(FwdParams p) {
             f32x16 s[2];
 #pragma unroll
             for (int b = 0; b < 2; ++b)
-                s[b] = mfma32(lds_read_b128(Ks, lds_off<HD>(b * 32 + l32, hi * 8)), qf[0], f32x16{});
+                s[b] = mfma32(lds_read_b128(Ks, off.row[0] + b * 32 * HD * 2), qf[0], f32x16{});
 #pragma unroll
             for (int st = 1; st < NS; ++st) {
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
-                    bf16x8 a = lds_read_b128(Ks, lds_off<HD>(b * 32 + l32, st * 16 + hi * 8));
+                    bf16x8 a = lds_read_b128(Ks, off.row[st] + b * 32 * HD * 2);
                     s[b] = mfma32(a, qf[st], s[b]);
                 }
             }
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(FwdParams p) {
                 for (int b = 0; b < 2; ++b) {
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) {
-                        bf16x8 a = lds_read_tr_operand<HD>(Vs, b * 32 + h2 * 16, db * 32, lane);
+                        const bf16x8 a = lds_read_tr_at<HD>(Vs, off, b * 32 + h2 * 16, db);
                         o[db] = mfma32(a, pb[b][h2], o[db]);
                     }
                 }
