@@ -25,9 +25,9 @@
 // partner through LDS, which adds it after its own (fixed order).
 //
 // dq_kernel: workgroup = NW waves x 32 query rows of one head (NW = 8 with a
-// 4-slot K/V ring for large launches, NW = 4 double-buffered otherwise, as in
-// the forward); Q and dO stay in registers; 64-key tiles of K and V are loaded
-// straight into LDS:
+// 4-slot K/V ring and two tiles per barrier for large launches, NW = 4
+// double-buffered otherwise, as in the forward); Q and dO stay in registers;
+// 64-key tiles of K and V are loaded straight into LDS:
 //   S^T = K Q^T,  dP^T = V dO^T,  dQ^T[d][q] += K^T dS^T (transposed K reads)
 #include "device_common.h"
 #include "kernels.h"
@@ -321,8 +321,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
     constexpr int BN = 64, WQ = 32, BM = NW * WQ;
     constexpr int NS = HD / 16, NDB = HD / 32;
     constexpr int TILE = BN * HD * 2;
-    constexpr int NBUF = NW == 8 ? 4 : 2;  // K/V ring slots (tiles in flight: NBUF - 1)
-    constexpr int NI = (NW == 8 ? 1 : 2) * (64 * HD * 2 / 4 / 1024);  // loads per wave per tile
+    // K/V ring slots: 8 waves work on two tiles per barrier while the next
+    // two load; 4 waves double-buffer single tiles
+    constexpr int NBUF = NW == 8 ? 4 : 2;
     __shared__ __attribute__((aligned(1024))) char smem[NBUF][2][TILE];  // [slot][K / V]
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -406,17 +407,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
     settle(dlt);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) settle(acc[db]);
-    const int pre = ntiles < NBUF - 1 ? ntiles : NBUF - 1;
+    const int pre = ntiles < NBUF / 2 ? ntiles : NBUF / 2;
     for (int t = 0; t < pre; ++t) issue(t);
-    wait_tiles_after<NI>(pre - 1);
+    wait_vm_loads();
     __syncthreads();
 
     const OperandOffsets<HD> off(lane);         // K / V operand reads
     const int64_t qrel_base = myq - p.k_pos0;  // query position relative to key 0
-    for (int j = 0; j < ntiles; ++j) {
-        const int buf = j % NBUF;
-        // the slot of tile j + NBUF - 1 held tile j - 1, released by the last barrier
-        if (j + NBUF - 1 < ntiles) issue(j + NBUF - 1);
+    auto tile = [&](int j, int buf) {
         if (j < ntiles_w) {
             const char* Ks = smem[buf][0];
             const char* Vs = smem[buf][1];
@@ -454,12 +452,24 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
                 }
             }
         }
-        // tile j + 1 must have landed; later tiles stay in flight
-        {
-            const int last = j + NBUF - 1 < ntiles ? j + NBUF - 1 : ntiles - 1;
-            wait_tiles_after<NI>(last - (j + 1));
+    };
+    if constexpr (NW == 8) {
+        for (int j = 0; j < ntiles; j += 2) {
+            // slots of tiles j - 2 and j - 1 were released by the last barrier
+            if (j + 2 < ntiles) issue(j + 2);
+            if (j + 3 < ntiles) issue(j + 3);
+            tile(j, j % NBUF);
+            if (j + 1 < ntiles) tile(j + 1, (j + 1) % NBUF);
+            wait_vm_loads();  // tiles j + 2 and j + 3
+            __syncthreads();
         }
-        __syncthreads();
+    } else {
+        for (int j = 0; j < ntiles; ++j) {
+            if (j + 1 < ntiles) issue(j + 1);
+            tile(j, j % NBUF);
+            wait_vm_loads();
+            __syncthreads();
+        }
     }
 
     if (!row_ok) return;

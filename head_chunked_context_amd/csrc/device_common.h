@@ -123,16 +123,6 @@ __device__ __forceinline__ bf16x2 to_bf16x2(float a, float b) {
 // direct global -> LDS loads below, which do not pass through registers).
 __device__ __forceinline__ void wait_vm_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Wait until this wave's tile loads have landed except those of the last
-// `after` tiles it issued (NI load instructions per tile, at most two tiles
-// left in flight; vector-memory loads retire in issue order).
-template <int NI>
-__device__ __forceinline__ void wait_tiles_after(int after) {
-    if (after >= 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * NI) : "memory");
-    else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NI) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
 // Direct global -> LDS loads (global_load_lds_dword[x4]): lane l's 4 / 16 bytes
 // from `src` land at LDS byte lds_addr + 4 l / 16 l (M0 holds the wave-uniform
 // base).  Issued as inline assembly on purpose: the compiler then does not

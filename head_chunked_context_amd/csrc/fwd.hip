@@ -8,13 +8,13 @@
 //
 // Workgroup = NW waves x 32 query rows of one head; the key loop walks 64-key
 // tiles of K and V loaded straight from global memory into LDS (global_load_
-// lds) through a ring of slots, one barrier per tile.  Large launches take
-// NW = 8 (256 rows, one workgroup per compute unit, a 4-slot ring with three
-// tiles in flight; waves 0-3 load K, waves 4-7 load V): each tile then serves
-// twice the rows and has three tile-times to arrive, which measured 8% faster
-// than NW = 4 at S = 32768.  Smaller launches take NW = 4 (128 rows, two
-// workgroups per compute unit, double-buffered) so more compute units get
-// work.  Per wave and tile, in the transposed form that keeps one query row
+// lds) through a ring of slots.  Large launches take NW = 8 (256 rows, one
+// workgroup per compute unit, waves 0-3 load K and waves 4-7 load V): each
+// tile then serves twice the rows, and a 4-slot ring lets the workgroup work
+// on two tiles per barrier while the next two load (measured 8% and then
+// another 5% faster than NW = 4 with one barrier per tile, at S = 32768).
+// Smaller launches take NW = 4 (128 rows, two workgroups per compute unit,
+// double-buffered, one barrier per tile) so more compute units get work.  Per wave and tile, in the transposed form that keeps one query row
 // per lane pair:
 //   S^T[key][q] = K Q^T          A = K tile (LDS, 16-byte reads), B = Q (regs)
 //   online softmax on S^T        lane l and l^32 share query l % 32
@@ -90,10 +90,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(FwdParams p) {
     constexpr int NS = HD / 16;  // reduction steps of K Q^T
     constexpr int NDB = HD / 32; // 32-wide d blocks of O
     constexpr int TILE = BN * HD * 2;
-    constexpr int NBUF = NW == 8 ? 4 : 2;  // K/V ring slots (tiles in flight: NBUF - 1)
-    // load instructions per wave per tile: 8 waves split K (waves 0-3) and V
-    // (waves 4-7), 4 waves load 16 rows of both
-    constexpr int NI = (NW == 8 ? 1 : 2) * (64 * HD * 2 / 4 / 1024);
+    // K/V ring slots: 8 waves work on two tiles per barrier while the next
+    // two load; 4 waves double-buffer single tiles
+    constexpr int NBUF = NW == 8 ? 4 : 2;
     __shared__ __attribute__((aligned(1024))) char smem[NBUF][2][TILE];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -178,19 +177,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(FwdParams p) {
     wait_vm_loads();
 #pragma unroll
     for (int s = 0; s < NS; ++s) settle(qf[s]);
-    const int pre = ntiles < NBUF - 1 ? ntiles : NBUF - 1;
+    // 8 waves: tiles go in pairs (one barrier per pair), 0 and 1 first;
+    // 4 waves: tile 0 first, one barrier per tile
+    const int pre = ntiles < NBUF / 2 ? ntiles : NBUF / 2;
     for (int t = 0; t < pre; ++t) issue(t);
-    wait_tiles_after<NI>(pre - 1);
+    wait_vm_loads();
     __syncthreads();
 
     // per-lane offsets of the K (row-major) and V (transposed) operand reads
     const OperandOffsets<HD> off(lane);
     // this lane's query position relative to the key positions of tile 0
     const int64_t qrel_base = p.q_pos0 + myq - p.k_pos0;
-    for (int j = 0; j < ntiles; ++j) {
-        const int buf = j % NBUF;
-        // the slot of tile j + NBUF - 1 held tile j - 1, released by the last barrier
-        if (j + NBUF - 1 < ntiles) issue(j + NBUF - 1);
+    auto tile = [&](int j, int buf) {
         if (j < ntiles_w) {
             const char* Ks = smem[buf][0];
             const char* Vs = smem[buf][1];
@@ -238,12 +236,24 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(FwdParams p) {
                 }
             }
         }
-        // tile j + 1 must have landed; later tiles stay in flight
-        {
-            const int last = j + NBUF - 1 < ntiles ? j + NBUF - 1 : ntiles - 1;
-            wait_tiles_after<NI>(last - (j + 1));
+    };
+    if constexpr (NW == 8) {
+        for (int j = 0; j < ntiles; j += 2) {
+            // slots of tiles j - 2 and j - 1 were released by the last barrier
+            if (j + 2 < ntiles) issue(j + 2);
+            if (j + 3 < ntiles) issue(j + 3);
+            tile(j, j % NBUF);
+            if (j + 1 < ntiles) tile(j + 1, (j + 1) % NBUF);
+            wait_vm_loads();  // tiles j + 2 and j + 3
+            __syncthreads();
         }
-        __syncthreads();
+    } else {
+        for (int j = 0; j < ntiles; ++j) {
+            if (j + 1 < ntiles) issue(j + 1);
+            tile(j, j % NBUF);
+            wait_vm_loads();
+            __syncthreads();
+        }
     }
 
     if (!wave_live || myq >= p.nq) return;
