@@ -102,7 +102,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
             for (int e = 0; e < 8; ++e) acc = fmaf((float)db[e], (float)ob[e], acc);
         }
         for (int off = lpr / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, lpr);
-        if (live && sub == 0) p.delta[h * p.delta_hs + row] = acc;
+        if (live && sub == 0) {
+            p.ndelta[h * p.ndelta_hs + row] = -acc;
+            p.nlse2[h * p.nlse2_hs + row] = -(p.lse[h * p.lse_hs + row] * kLog2e);
+        }
     }
 }
 

@@ -10,9 +10,14 @@
 // output tile, with fixed accumulation orders (dK/dV: the group's query heads
 // ascending, then query tiles ascending; dQ: key tiles ascending).
 //
+// The preprocessing pass stores the two row statistics in the form the loops
+// use: -Delta, which the dK/dV kernel loads as the starting value of the dP
+// accumulator (the MFMA then yields dP - Delta), and -LSE * log2(e), the
+// addend of the exponent's fused multiply-add.
+//
 // dkdv_kernel: workgroup = 8 waves on 128 keys of one query head's kv head;
 // K and V of the 128 keys sit in LDS for the whole kernel.  Each step loads a
-// 64-row query tile of Q and dO (plus LSE and Delta) straight into LDS,
+// 64-row query tile of Q and dO (plus the rows' statistics) straight into LDS,
 // double-buffered.  Waves w and w + 4 share keys 32 (w % 4) .. +31 and take
 // the lower / upper 32 rows of every tile:
 //   S[q][key]   = Q K^T        A = Q rows (LDS),   B = K (LDS)
@@ -34,30 +39,28 @@
 
 namespace hc {
 
-constexpr float kLog2e = 1.4426950408889634f;
 
 // P and dS of one 64-row query tile against this lane's key, as bf16 MFMA
 // operands.  MASK adds the causal / ragged-edge test; the common interior
 // tiles skip it entirely.
 template <int NQB, bool MASK>
 __device__ __forceinline__ void dkdv_p_ds(const f32x16 (&sacc)[NQB], const f32x16 (&dpacc)[NQB],
-                                          const float* s_lse, const float* s_delta, int hi,
-                                          float scale_log2, int qrel0, int krel, int qlim,
-                                          bf16x8 (&pb)[NQB][2], bf16x8 (&dsb)[NQB][2]) {
+                                          const float* s_nlse2, int hi, float scale_log2,
+                                          int qrel0, int krel, int qlim, bf16x8 (&pb)[NQB][2],
+                                          bf16x8 (&dsb)[NQB][2]) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             const int qr = qb * 32 + g4 * 8 + hi * 4;  // tile rows qr..qr+3
-            const f32x4 L = *reinterpret_cast<const f32x4*>(s_lse + qr);
-            const f32x4 Dl = *reinterpret_cast<const f32x4*>(s_delta + qr);
+            const f32x4 L = *reinterpret_cast<const f32x4*>(s_nlse2 + qr);
 #pragma unroll
             for (int e = 0; e < 4; e += 2) {
                 const int r = g4 * 4 + e;
                 float pv[2], dsv[2];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    float x = fast_exp2(sacc[qb][r + u] * scale_log2 - L[e + u] * kLog2e);
+                    float x = fast_exp2(__builtin_fmaf(sacc[qb][r + u], scale_log2, L[e + u]));
                     if constexpr (MASK) {
                         // qrel/krel: row and key relative to the key tile start;
                         // visible iff key <= row (causal) and row < qlim
@@ -65,7 +68,7 @@ __device__ __forceinline__ void dkdv_p_ds(const f32x16 (&sacc)[NQB], const f32x1
                         x = (krel <= qrel && qrel < qlim) ? x : 0.f;
                     }
                     pv[u] = x;
-                    dsv[u] = x * (dpacc[qb][r + u] - Dl[e + u]);
+                    dsv[u] = x * dpacc[qb][r + u];
                 }
                 const bf16x2 pk = to_bf16x2(pv[0], pv[1]);
                 const bf16x2 dk2 = to_bf16x2(dsv[0], dsv[1]);
@@ -85,8 +88,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
     constexpr int TILE = BQ * HD * 2;
     __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [buf][Q / dO]
     __shared__ __attribute__((aligned(1024))) char skv[2][2 * TILE];  // this tile's K, V
-    __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];
-    __shared__ __attribute__((aligned(16))) float s_delta[2][BQ];
+    __shared__ __attribute__((aligned(16))) float s_nlse2[2][BQ];   // -LSE * log2(e)
+    __shared__ __attribute__((aligned(16))) float s_ndelta[2][BQ];  // -Delta
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values scalar
@@ -130,8 +133,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
 
     const uint16_t* qh = p.q + (int64_t)hl * p.q_hs;
     const uint16_t* oh = p.dO + (int64_t)hl * p.do_hs;
-    const float* lseh = p.lse + (int64_t)(p.h0 + hl) * p.lse_hs;
-    const float* delh = p.delta + (int64_t)hl * p.delta_hs;
+    const float* lseh = p.nlse2 + (int64_t)hl * p.nlse2_hs;
+    const float* delh = p.ndelta + (int64_t)hl * p.ndelta_hs;
     // one step = Q (waves 0-3) and dO (waves 4-7) rows [i0, i0 + 64) plus
     // their LSE (wave 0) and Delta (wave 4), straight into LDS buffer b
     auto issue_step = [&](int64_t n, int b) {
@@ -140,8 +143,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
             direct_tile64<HD>(smem[b][0], qh + i0 * p.q_rs, p.q_rs, p.nq - i0, kw, lane);
         else
             direct_tile64<HD>(smem[b][1], oh + i0 * p.do_rs, p.do_rs, p.nq - i0, kw, lane);
-        if (wave == 0) direct_vec64(s_lse[b], lseh + i0, p.nq - i0, lane);
-        if (wave == 4) direct_vec64(s_delta[b], delh + i0, p.nq - i0, lane);
+        if (wave == 0) direct_vec64(s_nlse2[b], lseh + i0, p.nq - i0, lane);
+        if (wave == 4) direct_vec64(s_ndelta[b], delh + i0, p.nq - i0, lane);
     };
     if (nsteps > 0) issue_step(0, 0);
     wait_vm_loads();
@@ -160,7 +163,16 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
         if (live) {
             const char* Qs = smem[buf][0];
             const char* Os = smem[buf][1];
+            const float* sl = s_nlse2[buf] + rh * WQ;
+            // dP accumulates onto -Delta of each register's row, so it comes out
+            // as dP - Delta (register r holds row (r / 4) * 8 + hi * 4 + r % 4)
             f32x16 sacc[1], dpacc[1];
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 nd = *reinterpret_cast<const f32x4*>(s_ndelta[buf] + rh * WQ + g4 * 8 + hi * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dpacc[0][g4 * 4 + e] = nd[e];
+            }
 #pragma unroll
             for (int st = 0; st < NS; ++st) {
                 const int ko = off.row[st] + kw * 32 * HD * 2;
@@ -170,11 +182,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
                 const bf16x8 aq = lds_read_b128(Qs, qo);
                 const bf16x8 ao = lds_read_b128(Os, qo);
                 sacc[0] = mfma32(aq, kf, st == 0 ? f32x16{} : sacc[0]);
-                dpacc[0] = mfma32(ao, vf, st == 0 ? f32x16{} : dpacc[0]);
+                dpacc[0] = mfma32(ao, vf, dpacc[0]);
             }
             bf16x8 pb[1][2], dsb[1][2];
-            const float* sl = s_lse[buf] + rh * WQ;
-            const float* sd = s_delta[buf] + rh * WQ;
             const bool edge_k = wj0 + WK > p.nk;
             const bool edge_q = r0 + WQ > p.nq;
             const bool diag = p.causal && r0 < wkpos + WK - 1;
@@ -184,9 +194,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
                 const int qrel0 = (int)(p.causal ? r0 - wkpos : WK + r0);
                 const int qlim = (int)(p.causal ? p.nq - wkpos : WK + p.nq);
                 const int kr = (myk < p.nk) ? krel : (1 << 30);
-                dkdv_p_ds<1, true>(sacc, dpacc, sl, sd, hi, p.scale_log2, qrel0, kr, qlim, pb, dsb);
+                dkdv_p_ds<1, true>(sacc, dpacc, sl, hi, p.scale_log2, qrel0, kr, qlim, pb, dsb);
             } else {
-                dkdv_p_ds<1, false>(sacc, dpacc, sl, sd, hi, p.scale_log2, 0, 0, 0, pb, dsb);
+                dkdv_p_ds<1, false>(sacc, dpacc, sl, hi, p.scale_log2, 0, 0, 0, pb, dsb);
             }
             // dV^T += dO^T P and dK^T += Q^T dS, reduction over the wave's 32 rows
 #pragma unroll
@@ -293,7 +303,7 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(DkdvReduceParams p) {
 // MASK adds the causal / ragged test with keys relative to the first block.
 template <int NB, bool MASK>
 __device__ __forceinline__ void dq_ds(const f32x16 (&s)[NB], const f32x16 (&dp)[NB], float scale_log2,
-                                      float lse2, float dlt, int hi, int qrel, int klim,
+                                      float nlse2, float ndlt, int hi, int qrel, int klim,
                                       bf16x8 (&dsb)[NB][2]) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -302,12 +312,12 @@ __device__ __forceinline__ void dq_ds(const f32x16 (&s)[NB], const f32x16 (&dp)[
             float dsv[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                float x = fast_exp2(s[b][r + u] * scale_log2 - lse2);
+                float x = fast_exp2(__builtin_fmaf(s[b][r + u], scale_log2, nlse2));
                 if constexpr (MASK) {
                     const int key = b * 32 + ((r + u) >> 2) * 8 + hi * 4 + ((r + u) & 3);
                     x = (key <= qrel && key < klim) ? x : 0.f;
                 }
-                dsv[u] = x * (dp[b][r + u] - dlt);
+                dsv[u] = x * (dp[b][r + u] + ndlt);
             }
             const bf16x2 d2 = to_bf16x2(dsv[0], dsv[1]);
             dsb[b][r >> 3][r & 7] = d2[0];
@@ -355,8 +365,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
             df[s] = bf16x8{};
         }
     }
-    const float lse2 = row_ok ? p.lse[(int64_t)(p.h0 + head) * p.lse_hs + myq] * kLog2e : INFINITY;
-    const float dlt = row_ok ? p.delta[(int64_t)head * p.delta_hs + myq] : 0.f;
+    const float nlse2 = row_ok ? p.nlse2[(int64_t)head * p.nlse2_hs + myq] : -INFINITY;
+    const float ndlt = row_ok ? p.ndelta[(int64_t)head * p.ndelta_hs + myq] : 0.f;
 
     f32x16 acc[NDB];
 #pragma unroll
@@ -403,8 +413,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
         settle(qf[s]);
         settle(df[s]);
     }
-    settle(lse2);
-    settle(dlt);
+    settle(nlse2);
+    settle(ndlt);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) settle(acc[db]);
     const int pre = ntiles < NBUF / 2 ? ntiles : NBUF / 2;
@@ -437,9 +447,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
                 if (need_mask) {
                     const int64_t qr = p.causal ? qrel_base - kb - b * 32 : (int64_t)BN;
                     const int kl = (int)(p.nk - kb - b * 32);
-                    dq_ds<1, true>(s, dp, p.scale_log2, lse2, dlt, hi, (int)qr, kl, dsb);
+                    dq_ds<1, true>(s, dp, p.scale_log2, nlse2, ndlt, hi, (int)qr, kl, dsb);
                 } else {
-                    dq_ds<1, false>(s, dp, p.scale_log2, lse2, dlt, hi, 0, 0, dsb);
+                    dq_ds<1, false>(s, dp, p.scale_log2, nlse2, ndlt, hi, 0, 0, dsb);
                 }
                 // dQ^T += K^T dS^T over the half's 32 keys
 #pragma unroll

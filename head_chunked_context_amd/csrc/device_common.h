@@ -36,6 +36,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __attribute__((address_space(3))) void lds_void;
 

@@ -259,8 +259,8 @@ double moved_bytes(const hc::PackParams& p) {
     return 2.0 * p.nh * (double)p.rows * p.D * 2;  // bf16 in, bf16 out
 }
 double moved_bytes(const hc::PrepParams& p) {
-    // O and dO in, packed dO out (bf16); Delta out (fp32)
-    return (double)p.nh * p.rows * (3.0 * p.D * 2 + 4);
+    // O and dO in, packed dO out (bf16); LSE in, -Delta and -LSE log2(e) out (fp32)
+    return (double)p.nh * p.rows * (3.0 * p.D * 2 + 12);
 }
 double moved_bytes(const hc::MergeParams& p) {
     // running and trunk O (fp32) and LSE in; running O / LSE or bf16 O / LSE out
@@ -402,8 +402,8 @@ hc::DkdvParams dkdv_params(const Common& c, const hc::Chunk& ch, const BwdIO& io
     hc::DkdvParams d{};
     d.q = reinterpret_cast<const uint16_t*>(c.ws + p.q_c); d.q_rs = D; d.q_hs = p.S * D;
     d.dO = reinterpret_cast<const uint16_t*>(c.ws + p.do_c); d.do_rs = D; d.do_hs = p.S * D;
-    d.lse = io.lse; d.lse_hs = p.S;
-    d.delta = reinterpret_cast<const float*>(c.ws + p.delta_c); d.delta_hs = p.S;
+    d.nlse2 = reinterpret_cast<const float*>(c.ws + p.lse2_c); d.nlse2_hs = p.S;
+    d.ndelta = reinterpret_cast<const float*>(c.ws + p.delta_c); d.ndelta_hs = p.S;
     d.k = kk; d.v = vv; d.k_rs = d.v_rs = k_rs; d.k_hs = d.v_hs = k_hs;
     d.nh = ch.nh; d.group = p.g; d.h0 = ch.h0; d.kv_base = ch.kv0;
     d.nq = p.S; d.nk = nk; d.k_pos0 = kr0; d.causal = p.causal;
@@ -452,8 +452,10 @@ int bwd_chunk_prep(Common& c, const hc::Chunk& ch, const BwdIO& io) {
     hc::PrepParams pr{};
     pr.o = io.o + (size_t)ch.h0 * D; pr.o_rs = (int64_t)p.Hq * D; pr.o_hs = D;
     pr.dO = io.dout + (size_t)ch.h0 * D; pr.do_rs = (int64_t)p.Hq * D; pr.do_hs = D;
+    pr.lse = io.lse + (size_t)ch.h0 * S; pr.lse_hs = S;
     pr.dO_c = reinterpret_cast<uint16_t*>(c.ws + p.do_c); pr.c_rs = D; pr.c_hs = S * D;
-    pr.delta = reinterpret_cast<float*>(c.ws + p.delta_c); pr.delta_hs = S;
+    pr.ndelta = reinterpret_cast<float*>(c.ws + p.delta_c); pr.ndelta_hs = S;
+    pr.nlse2 = reinterpret_cast<float*>(c.ws + p.lse2_c); pr.nlse2_hs = S;
     pr.nh = ch.nh; pr.rows = S; pr.D = D;
     LAUNCH_PASS(K_PREP, pr, hc::launch_prep(pr, c.st));
     return ATTN_OK;
@@ -466,8 +468,8 @@ hc::DqParams dq_params(const Common& c, const hc::Chunk& ch, const BwdIO& io, co
     hc::DqParams d{};
     d.q = reinterpret_cast<const uint16_t*>(c.ws + p.q_c); d.q_rs = D; d.q_hs = p.S * D;
     d.dO = reinterpret_cast<const uint16_t*>(c.ws + p.do_c); d.do_rs = D; d.do_hs = p.S * D;
-    d.lse = io.lse; d.lse_hs = p.S;
-    d.delta = reinterpret_cast<const float*>(c.ws + p.delta_c); d.delta_hs = p.S;
+    d.nlse2 = reinterpret_cast<const float*>(c.ws + p.lse2_c); d.nlse2_hs = p.S;
+    d.ndelta = reinterpret_cast<const float*>(c.ws + p.delta_c); d.ndelta_hs = p.S;
     d.k = kk; d.v = vv; d.k_rs = d.v_rs = k_rs; d.k_hs = d.v_hs = k_hs;
     d.nh = ch.nh; d.group = p.g; d.h0 = ch.h0; d.kv_base = ch.kv0;
     d.nq = p.S; d.nk = nk; d.k_pos0 = kr0; d.causal = p.causal;

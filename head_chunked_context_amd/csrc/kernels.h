@@ -68,11 +68,16 @@ struct MergeParams {
 
 // Backward preprocessing: Delta[h][i] = sum_d dO[i,h,d] * O[i,h,d] (fp32,
 // fixed order) and the packed copy of dO.
+// Backward preprocessing of a chunk: packs dO head-major and writes, per
+// (head, row), the two row statistics the backward kernels read, in the form
+// they use them: ndelta = -rowsum(dO * O) and nlse2 = -LSE * log2(e).
 struct PrepParams {
     const uint16_t* o;  int64_t o_rs, o_hs;
     const uint16_t* dO; int64_t do_rs, do_hs;
+    const float* lse;   int64_t lse_hs;      // the chunk's heads, natural log
     uint16_t* dO_c;     int64_t c_rs, c_hs;
-    float* delta;       int64_t delta_hs;
+    float* ndelta;      int64_t ndelta_hs;
+    float* nlse2;       int64_t nlse2_hs;
     int nh;
     int64_t rows;
     int D;
@@ -86,8 +91,8 @@ struct PrepParams {
 struct DkdvParams {
     const uint16_t* q;  int64_t q_rs, q_hs;    // chunk query heads (local 0..nh)
     const uint16_t* dO; int64_t do_rs, do_hs;
-    const float* lse;   int64_t lse_hs;        // natural LSE, [global head][row]
-    const float* delta; int64_t delta_hs;      // [local head][row]
+    const float* nlse2;  int64_t nlse2_hs;     // -LSE * log2(e), [local head][row]
+    const float* ndelta; int64_t ndelta_hs;    // -Delta, [local head][row]
     const uint16_t* k;  int64_t k_rs, k_hs;    // kv heads (local 0..nkv)
     const uint16_t* v;  int64_t v_rs, v_hs;
     int nh, group, h0, kv_base;
@@ -118,8 +123,8 @@ struct DkdvReduceParams {
 struct DqParams {
     const uint16_t* q;  int64_t q_rs, q_hs;
     const uint16_t* dO; int64_t do_rs, do_hs;
-    const float* lse;   int64_t lse_hs;
-    const float* delta; int64_t delta_hs;
+    const float* nlse2;  int64_t nlse2_hs;     // -LSE * log2(e), [local head][row]
+    const float* ndelta; int64_t ndelta_hs;    // -Delta, [local head][row]
     const uint16_t* k;  int64_t k_rs, k_hs;
     const uint16_t* v;  int64_t v_rs, v_hs;
     int nh, group, h0, kv_base;

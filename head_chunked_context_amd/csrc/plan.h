@@ -38,7 +38,7 @@ struct Plan {
     size_t o_run = 0, o_t = 0, l_run = 0, l_t = 0;      // fwd trunk partials / carried state
     size_t st_l = 0;                                    // fwd carried lane-pair row sums
     size_t ring_k[2] = {0, 0}, ring_v[2] = {0, 0};      // trunk ring slots
-    size_t do_c = 0, delta_c = 0, dq_acc = 0;           // bwd chunk buffers
+    size_t do_c = 0, delta_c = 0, lse2_c = 0, dq_acc = 0; // bwd chunk buffers
     size_t part_k = 0, part_v = 0;                      // bwd per-head fp32 dK/dV
     size_t carry_k[2] = {0, 0}, carry_v[2] = {0, 0};    // bwd fp32 carries
     size_t stage_k[2] = {0, 0}, stage_v[2] = {0, 0};    // bwd dK/dV staging
@@ -143,7 +143,8 @@ static inline int make_plan(bool bwd, int64_t S, int Hq, int Hkv, int D, int cau
     } else {
         p.q_c = take(p.hc * E);
         p.do_c = take(p.hc * E);
-        p.delta_c = take((size_t)p.hc * S * 4);
+        p.delta_c = take((size_t)p.hc * S * 4);           // -Delta, fp32 [hc][S]
+        p.lse2_c = take((size_t)p.hc * S * 4);            // -LSE * log2(e), fp32 [hc][S]
         const size_t rows = p.trunked ? Et : E;           // keys per dK/dV launch, bf16 bytes
         p.part_k = take(p.hc * rows * 2);                 // fp32 [hc][rows][D]
         p.part_v = take(p.hc * rows * 2);

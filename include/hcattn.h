@@ -104,8 +104,9 @@ enum attn_status {
 size_t attn_fwd_workspace_bytes(int64_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t causal,
                                 int32_t head_chunk, int64_t kv_trunk);
 
-/* Same for attn_bwd (chunk's packed Q, dO, K, V, Delta, fp32 dQ/dK/dV carries,
- * and with kv_trunk the K/V ring and dK/dV staging). 0 on invalid arguments. */
+/* Same for attn_bwd (chunk's packed Q, dO, K, V, the rows' Delta and scaled
+ * LSE, fp32 dQ/dK/dV carries, and with kv_trunk the K/V ring and dK/dV
+ * staging). 0 on invalid arguments. */
 size_t attn_bwd_workspace_bytes(int64_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t causal,
                                 int32_t head_chunk, int64_t kv_trunk);
 

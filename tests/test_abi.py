@@ -63,8 +63,9 @@ def test_backward_workspace_formula_aligned_chunks():
     S, Hq, Hkv, D = 32768, 32, 8, 128
     for hc_ in (4, 8, 32):
         kvc = hc_ // 4
-        # Q, dO (bf16), Delta, per-head fp32 dK/dV partials, K, V (bf16)
-        want = 2 * A(hc_ * E(S, D)) + A(hc_ * S * 4) + 2 * A(2 * hc_ * E(S, D)) + \
+        # Q, dO (bf16), -Delta and -LSE*log2(e) (fp32 rows), per-head fp32 dK/dV
+        # partials, K, V (bf16)
+        want = 2 * A(hc_ * E(S, D)) + 2 * A(hc_ * S * 4) + 2 * A(2 * hc_ * E(S, D)) + \
             2 * A(kvc * E(S, D))
         assert hc.bwd_workspace_bytes(S, Hq, Hkv, D, True, hc_, 0) == want
 
