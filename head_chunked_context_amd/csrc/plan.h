@@ -180,8 +180,8 @@ static inline int make_plan(bool bwd, int64_t S, int Hq, int Hkv, int D, int cau
 //             V heads (4 T kvc D bytes) takes no longer than one full
 //             query-trunk x key-trunk block of the forward (4 T^2 D hc FLOP):
 //             T >= kvc * flops / (hc * link);
-//   fills:    one forward launch has at least two rounds of workgroups (128
-//             query rows each, two resident per compute unit):
+//   fills:    one forward launch has at least two rounds of workgroups
+//             (128 query rows at two per compute unit, or 256 at one):
 //             ceil(T / 128) * hc >= 4 * num_cus.
 // The smallest qualifying T wins.  Device-resident K/V whose untrunked
 // workspaces fit take T = 0 (no trunks).  When no T qualifies, the longest
