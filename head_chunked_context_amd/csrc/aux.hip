@@ -81,28 +81,26 @@ __global__ __launch_bounds__(256) void merge_stats_kernel(MergeParams p) {
 // 16 lanes per row of D = 128 (8 lanes for D = 64): each lane multiplies 8
 // pairs in order, then a fixed xor-butterfly adds the lane partials, so Delta
 // has one summation order whatever the launch shape.
+// Grid: x over row blocks, y = head; D / 8 lanes per row, a fixed
+// shuffle-tree row sum.
 __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
-    const int lpr = p.D / 8;  // lanes per row
-    const int rows_per_block = 256 / lpr;
-    const int sub = threadIdx.x % lpr;
-    const int64_t total = (int64_t)p.nh * p.rows;
-    for (int64_t base = (int64_t)blockIdx.x * rows_per_block; base < total;
-         base += (int64_t)gridDim.x * rows_per_block) {
-        const int64_t hr = base + threadIdx.x / lpr;
-        const bool live = hr < total;
-        const int64_t row = live ? hr % p.rows : 0, h = live ? hr / p.rows : 0;
+    const int lg = p.D == 128 ? 4 : 3;  // log2 of the lanes per row
+    const int lpr = 1 << lg;
+    const int sub = threadIdx.x & (lpr - 1);
+    const int rpb = 256 >> lg;          // rows per block and pass
+    const int64_t h = blockIdx.y;
+    for (int64_t row = (int64_t)blockIdx.x * rpb + (threadIdx.x >> lg); row < p.rows;
+         row += (int64_t)gridDim.x * rpb) {
+        const uint4 ov = *reinterpret_cast<const uint4*>(p.o + h * p.o_hs + row * p.o_rs + sub * 8);
+        const uint4 dv = *reinterpret_cast<const uint4*>(p.dO + h * p.do_hs + row * p.do_rs + sub * 8);
+        *reinterpret_cast<uint4*>(p.dO_c + h * p.c_hs + row * p.c_rs + sub * 8) = dv;
+        const bf16x8 ob = __builtin_bit_cast(bf16x8, ov);
+        const bf16x8 db = __builtin_bit_cast(bf16x8, dv);
         float acc = 0.f;
-        if (live) {
-            const uint4 ov = *reinterpret_cast<const uint4*>(p.o + h * p.o_hs + row * p.o_rs + sub * 8);
-            const uint4 dv = *reinterpret_cast<const uint4*>(p.dO + h * p.do_hs + row * p.do_rs + sub * 8);
-            *reinterpret_cast<uint4*>(p.dO_c + h * p.c_hs + row * p.c_rs + sub * 8) = dv;
-            const bf16x8 ob = __builtin_bit_cast(bf16x8, ov);
-            const bf16x8 db = __builtin_bit_cast(bf16x8, dv);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc = fmaf((float)db[e], (float)ob[e], acc);
-        }
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)db[e], (float)ob[e], acc);
         for (int off = lpr / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, lpr);
-        if (live && sub == 0) {
+        if (sub == 0) {
             p.ndelta[h * p.ndelta_hs + row] = -acc;
             p.nlse2[h * p.nlse2_hs + row] = -(p.lse[h * p.lse_hs + row] * kLog2e);
         }
@@ -135,9 +133,12 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t st) {
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t st) {
     if (p.nh <= 0 || p.rows <= 0) return hipSuccess;
-    const int rows_per_block = 256 / (p.D / 8);
-    hipLaunchKernelGGL(prep_kernel, dim3(grid_for((int64_t)p.nh * p.rows, rows_per_block)),
-                       dim3(256), 0, st, p);
+    if (p.nh > 65535 || (p.D != 128 && p.D != 64)) return hipErrorInvalidValue;
+    const int64_t rpb = 256 / (p.D / 8);
+    int64_t bx = (p.rows + rpb - 1) / rpb;
+    const int64_t cap = (4096 + p.nh - 1) / p.nh;
+    bx = bx > cap ? cap : bx;
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)bx, (unsigned)p.nh), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
