@@ -47,6 +47,12 @@ def test_gqa_chunks_not_aligned_with_groups():
     _run_case(700, 8, 2, 128, [8, 3, 1, 2], seed=12)
 
 
+def test_wide_group_chunks_of_odd_size():
+    # g = 8 (one kv head): hc = 3 and 5 leave ragged chunks whose group spans
+    # two or three chunks, D = 64, ragged sequence end
+    _run_case(601, 8, 1, 64, [8, 3, 5], seed=17)
+
+
 def test_non_causal():
     _run_case(300, 4, 1, 128, [4, 1], seed=13, causal=False)
 
