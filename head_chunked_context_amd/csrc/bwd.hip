@@ -11,8 +11,8 @@
 // ascending, then query tiles ascending; dQ: key tiles ascending).
 //
 // The preprocessing pass stores the two row statistics in the form the loops
-// use: -Delta, which the dK/dV kernel loads as the starting value of the dP
-// accumulator (the MFMA then yields dP - Delta), and -LSE * log2(e), the
+// use: -Delta, which both kernels take as the starting value of the dP
+// accumulator (the MFMAs then yield dP - Delta), and -LSE * log2(e), the
 // addend of the exponent's fused multiply-add.
 //
 // dkdv_kernel: workgroup = 8 waves on 128 keys of one query head's kv head;
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(DkdvReduceParams p) {
 // MASK adds the causal / ragged test with keys relative to the first block.
 template <int NB, bool MASK>
 __device__ __forceinline__ void dq_ds(const f32x16 (&s)[NB], const f32x16 (&dp)[NB], float scale_log2,
-                                      float nlse2, float ndlt, int hi, int qrel, int klim,
+                                      float nlse2, int hi, int qrel, int klim,
                                       bf16x8 (&dsb)[NB][2]) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -317,7 +317,7 @@ __device__ __forceinline__ void dq_ds(const f32x16 (&s)[NB], const f32x16 (&dp)[
                     const int key = b * 32 + ((r + u) >> 2) * 8 + hi * 4 + ((r + u) & 3);
                     x = (key <= qrel && key < klim) ? x : 0.f;
                 }
-                dsv[u] = x * (dp[b][r + u] + ndlt);
+                dsv[u] = x * dp[b][r + u];
             }
             const bf16x2 d2 = to_bf16x2(dsv[0], dsv[1]);
             dsb[b][r >> 3][r & 7] = d2[0];
@@ -415,6 +415,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
     }
     settle(nlse2);
     settle(ndlt);
+    // every register of the lane's dP accumulator starts at -Delta of its
+    // row, so the MFMAs yield dP - Delta
+    f32x16 ndsplat;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndsplat[r] = ndlt;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) settle(acc[db]);
     const int pre = ntiles < NBUF / 2 ? ntiles : NBUF / 2;
@@ -441,15 +446,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
                     const bf16x8 ak = lds_read_b128(Ks, o);
                     const bf16x8 av = lds_read_b128(Vs, o);
                     s[0] = mfma32(ak, qf[st], st == 0 ? f32x16{} : s[0]);
-                    dp[0] = mfma32(av, df[st], st == 0 ? f32x16{} : dp[0]);
+                    dp[0] = mfma32(av, df[st], st == 0 ? ndsplat : dp[0]);
                 }
                 bf16x8 dsb[1][2];
                 if (need_mask) {
                     const int64_t qr = p.causal ? qrel_base - kb - b * 32 : (int64_t)BN;
                     const int kl = (int)(p.nk - kb - b * 32);
-                    dq_ds<1, true>(s, dp, p.scale_log2, nlse2, ndlt, hi, (int)qr, kl, dsb);
+                    dq_ds<1, true>(s, dp, p.scale_log2, nlse2, hi, (int)qr, kl, dsb);
                 } else {
-                    dq_ds<1, false>(s, dp, p.scale_log2, nlse2, ndlt, hi, 0, 0, dsb);
+                    dq_ds<1, false>(s, dp, p.scale_log2, nlse2, hi, 0, 0, dsb);
                 }
                 // dQ^T += K^T dS^T over the half's 32 keys
 #pragma unroll
