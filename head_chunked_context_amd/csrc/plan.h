@@ -180,9 +180,10 @@ static inline int make_plan(bool bwd, int64_t S, int Hq, int Hkv, int D, int cau
 //             V heads (4 T kvc D bytes) takes no longer than one full
 //             query-trunk x key-trunk block of the forward (4 T^2 D hc FLOP):
 //             T >= kvc * flops / (hc * link);
-//   fills:    one forward launch has at least two rounds of workgroups
-//             (128 query rows at two per compute unit, or 256 at one):
-//             ceil(T / 128) * hc >= 4 * num_cus.
+//   fills:    one forward launch has at least four rounds of workgroups
+//             (128 query rows at two per compute unit, or 256 at one), so
+//             a last partial round costs little: ceil(T / 128) * hc >=
+//             8 * num_cus.
 // The smallest qualifying T wins.  Device-resident K/V whose untrunked
 // workspaces fit take T = 0 (no trunks).  When no T qualifies, the longest
 // one that fits is taken.  Returns 0, -1 (bad arguments or host K/V with
@@ -223,7 +224,7 @@ static inline int pick_kv_trunk(int64_t S, int Hq, int Hkv, int D, int causal, i
         best_fit = T;
         const bool balanced =
             !kv_on_host || (double)T >= (double)p.kvc * flops / ((double)p.hc * link);
-        const bool fills = (T + 127) / 128 * p.hc >= 4 * (int64_t)num_cus;
+        const bool fills = (T + 127) / 128 * p.hc >= 8 * (int64_t)num_cus;
         if (balanced && fills) { pick = T; break; }
     }
     if (pick < 0) pick = best_fit;

@@ -119,8 +119,8 @@ size_t attn_bwd_workspace_bytes(int64_t S, int32_t Hq, int32_t Hkv, int32_t D, i
  * with_backward, fits budget_bytes (0 = no limit); (b) if kv_on_host, copying
  * one trunk of the chunk's K and V heads over a link of link_bytes_per_s is
  * no slower than the forward's FLOPs on one query-trunk x key-trunk block at
- * flops_per_s; (c) one forward launch has at least two rounds of workgroups
- * on num_cus compute units.  The smallest qualifying candidate is written to
+ * flops_per_s; (c) one forward launch has at least four rounds of
+ * workgroups on num_cus compute units.  The smallest qualifying candidate is written to
  * *kv_trunk; device-resident K/V whose untrunked workspaces fit get 0; if
  * none qualifies, the longest candidate that fits.  Rates and counts <= 0
  * take the values measured on one MI355X: 57e9 B/s pinned-host copies, 1e15
