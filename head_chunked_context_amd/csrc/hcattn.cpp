@@ -87,8 +87,16 @@ int device_resources(Device** out) {
     if (!d.ready) {
         // default priority on purpose: every stream here runs at one priority
         HIPCHK(hipStreamCreateWithFlags(&d.copy, hipStreamNonBlocking));
-        for (int i = 0; i < EV_COUNT; ++i)
-            HIPCHK(hipEventCreateWithFlags(&d.ev[i], hipEventDisableTiming));
+        for (int i = 0; i < EV_COUNT; ++i) {
+            const hipError_t e = hipEventCreateWithFlags(&d.ev[i], hipEventDisableTiming);
+            if (e != hipSuccess) {
+                // undo, so that a later call starts over cleanly
+                for (int k = 0; k < i; ++k) (void)hipEventDestroy(d.ev[k]);
+                (void)hipStreamDestroy(d.copy);
+                d.copy = nullptr;
+                return fail(ATTN_EHIP, "hipEventCreateWithFlags failed: %s", hipGetErrorString(e));
+            }
+        }
         d.ready = true;
     }
     *out = &d;
