@@ -63,8 +63,9 @@ def algorithmic_flops(family: str, S: int, Hq: int, D: int, causal: bool) -> flo
     return 0.0 if per_pair is None else per_pair * pairs * Hq
 
 
-# the sources each kernel family is compiled from (traffic figures taken with
-# the profiler are only used while these are unchanged)
+# the sources each kernel family is compiled from, with their code-generation
+# options (traffic figures taken with the profiler are only used while these
+# are unchanged)
 FAMILY_SOURCES = {"fwd": ["fwd.hip"], "dkdv": ["bwd.hip"], "dq": ["bwd.hip"]}
 COMMON_SOURCES = ["device_common.h", "kernels.h"]
 
@@ -77,9 +78,11 @@ PROFILES_DIR = os.path.join(ROOT_DIR, "profiles")
 def kernel_source_hash(family: str) -> str:
     import hashlib
     h = hashlib.sha256()
+    from head_chunked_context_amd.build import FLAGS
     for name in FAMILY_SOURCES.get(family, []) + COMMON_SOURCES:
         with open(os.path.join(CSRC_DIR, name), "rb") as f:
             h.update(f.read())
+        h.update(repr(FLAGS.get(name, [])).encode())
     return h.hexdigest()
 
 
