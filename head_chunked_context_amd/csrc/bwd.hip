@@ -137,12 +137,13 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
     const float* delh = p.ndelta + (int64_t)hl * p.ndelta_hs;
     // one step = Q (waves 0-3) and dO (waves 4-7) rows [i0, i0 + 64) plus
     // their LSE (wave 0) and Delta (wave 4), straight into LDS buffer b
+    const TileDma64<HD> dqo(rh == 0 ? p.q_rs : p.do_rs, kw, lane);
     auto issue_step = [&](int64_t n, int b) {
         const int64_t i0 = (qt0 + n) * BQ;
         if (rh == 0)
-            direct_tile64<HD>(smem[b][0], qh + i0 * p.q_rs, p.q_rs, p.nq - i0, kw, lane);
+            dqo.load(smem[b][0], qh + i0 * p.q_rs, p.q_rs, p.nq - i0, kw, lane);
         else
-            direct_tile64<HD>(smem[b][1], oh + i0 * p.do_rs, p.do_rs, p.nq - i0, kw, lane);
+            dqo.load(smem[b][1], oh + i0 * p.do_rs, p.do_rs, p.nq - i0, kw, lane);
         if (wave == 0) direct_vec64(s_nlse2[b], lseh + i0, p.nq - i0, lane);
         if (wave == 4) direct_vec64(s_ndelta[b], delh + i0, p.nq - i0, lane);
     };
@@ -398,13 +399,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
     const int kv_sel = wave >> 2;
     const uint16_t* kvh = kv_sel == 0 ? kh : vh;
     const int64_t kv_rs = kv_sel == 0 ? p.k_rs : p.v_rs;
+    // per-lane parts of the tile-load addresses (8 waves: K or V; 4 waves: both)
+    const TileDma64<HD> dkv(NW == 8 ? kv_rs : p.k_rs, wave & 3, lane);
+    const TileDma64<HD> dv2(p.v_rs, wave & 3, lane);
     auto issue = [&](int t) {
         const int64_t nb = (int64_t)t * BN;
         if constexpr (NW == 8) {
-            direct_tile64<HD>(smem[t % NBUF][kv_sel], kvh + nb * kv_rs, kv_rs, p.nk - nb, wave & 3, lane);
+            dkv.load(smem[t % NBUF][kv_sel], kvh + nb * kv_rs, kv_rs, p.nk - nb, wave & 3, lane);
         } else {
-            direct_tile64<HD>(smem[t % NBUF][0], kh + nb * p.k_rs, p.k_rs, p.nk - nb, wave, lane);
-            direct_tile64<HD>(smem[t % NBUF][1], vh + nb * p.v_rs, p.v_rs, p.nk - nb, wave, lane);
+            dkv.load(smem[t % NBUF][0], kh + nb * p.k_rs, p.k_rs, p.nk - nb, wave, lane);
+            dv2.load(smem[t % NBUF][1], vh + nb * p.v_rs, p.v_rs, p.nk - nb, wave, lane);
         }
     };
     wait_vm_loads();

@@ -182,11 +182,68 @@ __device__ __forceinline__ void direct_tile64(char* lds_tile, const uint16_t* ba
     }
 }
 
+// The same loads in the scalar-base form: a wave-uniform 64-bit global
+// address in an SGPR pair plus a 32-bit per-lane byte offset, so a load needs
+// no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ uint64_t uniform_addr(const void* p) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ void lds_dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    const uint64_t sb = uniform_addr(sbase);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(sb), "s"(m0) : "memory");
+}
+__device__ __forceinline__ void lds_dma4_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    const uint64_t sb = uniform_addr(sbase);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :: "v"(voff), "s"(sb), "s"(m0) : "memory");
+}
+
+// 64-row tile loads with the per-lane part of the address worked out once.
+// Wave w (of the 4 sharing a tile) issues its instruction i for the 1 KB
+// block 4 i + w; with that assignment the swizzled chunk a lane fetches is
+// the same for every i (for both HD = 128 and HD = 64), so the lane's byte
+// offset is fixed and instruction i only moves the wave-uniform base by
+// 4 i blocks of rows.  The LDS image is the one direct_tile64 writes.  Tiles
+// with fewer than 64 valid rows, or strides too long for a 32-bit offset,
+// take direct_tile64.
+template <int HD>
+struct TileDma64 {
+    static constexpr int ROWB = HD * 2, CPR = ROWB / 16, RPI = 1024 / ROWB, NI = 64 / (4 * RPI);
+    static constexpr int64_t kMaxRs = (int64_t)1 << 24;  // 64 rows x rs x 2 B < 2^31
+    uint32_t voff;
+    __device__ __forceinline__ TileDma64(int64_t rs, int wave, int lane) {
+        const int row = wave * RPI + lane / CPR;  // row of instruction 0
+        const int lc = (lane % CPR) ^ swz<HD>(row);
+        voff = rs < kMaxRs ? (uint32_t)((row * rs + lc * 8) * 2) : 0u;
+    }
+    __device__ __forceinline__ void load(char* lds_tile, const uint16_t* base, int64_t rs,
+                                         int64_t nvalid, int wave, int lane) const {
+        if (nvalid >= 64 && rs < kMaxRs) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+                lds_dma16_sv(base + (int64_t)i * 4 * RPI * rs, voff,
+                             lds_addr(lds_tile + (i * 4 + wave) * 1024));
+        } else {
+            direct_tile64<HD>(lds_tile, base, rs, nvalid, wave, lane);
+        }
+    }
+};
+
 // 64 consecutive fp32 (one per lane of one wave) straight into LDS; entries at
 // or past nvalid (>= 1) repeat entry nvalid - 1.
 __device__ __forceinline__ void direct_vec64(float* lds_vec, const float* src, int64_t nvalid, int lane) {
-    const int64_t i = lane < nvalid ? lane : nvalid - 1;
-    lds_dma4(src + i, lds_addr(lds_vec));
+    if (nvalid >= 64) {
+        lds_dma4_sv(src, (uint32_t)lane * 4u, lds_addr(lds_vec));
+    } else {
+        const int64_t i = lane < nvalid ? lane : nvalid - 1;
+        lds_dma4(src + i, lds_addr(lds_vec));
+    }
 }
 
 // 64-row x HD-column bf16 tile: global -> registers -> swizzled LDS, 256 threads.

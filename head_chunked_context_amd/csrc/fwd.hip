@@ -164,13 +164,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(FwdParams p) {
     const int kv_sel = wave >> 2;
     const uint16_t* kvh = kv_sel == 0 ? kh : vh;
     const int64_t kv_rs = kv_sel == 0 ? p.k_rs : p.v_rs;
+    // per-lane parts of the tile-load addresses (8 waves: K or V; 4 waves: both)
+    const TileDma64<HD> dkv(NW == 8 ? kv_rs : p.k_rs, wave & 3, lane);
+    const TileDma64<HD> dv2(p.v_rs, wave & 3, lane);
     auto issue = [&](int t) {
         const int64_t nb = (int64_t)t * BN;
         if constexpr (NW == 8) {
-            direct_tile64<HD>(smem[t % NBUF][kv_sel], kvh + nb * kv_rs, kv_rs, p.nk - nb, wave & 3, lane);
+            dkv.load(smem[t % NBUF][kv_sel], kvh + nb * kv_rs, kv_rs, p.nk - nb, wave & 3, lane);
         } else {
-            direct_tile64<HD>(smem[t % NBUF][0], kh + nb * p.k_rs, p.k_rs, p.nk - nb, wave, lane);
-            direct_tile64<HD>(smem[t % NBUF][1], vh + nb * p.v_rs, p.v_rs, p.nk - nb, wave, lane);
+            dkv.load(smem[t % NBUF][0], kh + nb * p.k_rs, p.k_rs, p.nk - nb, wave, lane);
+            dv2.load(smem[t % NBUF][1], vh + nb * p.v_rs, p.v_rs, p.nk - nb, wave, lane);
         }
     };
     // registers loaded above settle first; then tiles 0 .. NBUF-2 go in flight
