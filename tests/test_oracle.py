@@ -2,7 +2,8 @@
 
 The pages print no worked numbers for attention, so the oracle is pinned by:
 brute-force central finite differences of L = sum(O * dO), closed forms
-(Q = 0, equal keys, row 0, S = 1, a 3-token worked example), the library
+(Q = 0, equal keys, row 0, S = 1, a 3-token worked example whose forward and
+backward values, derived by hand, are stored in tests/golden/), the library
 routine torch scaled_dot_product_attention (+ autograd) in fp64 on the CPU,
 the structural identities of the gradients, and the invariances the pages
 rely on (head chunks reuse buffers without changing results; key trunks merge
@@ -120,6 +121,56 @@ def test_worked_example_three_tokens():
     e1 = math.exp(1.0)
     assert lse2[0, 0] == pytest.approx(math.log(1 + 2 * e1), abs=1e-14)
     assert o2[0, 0, 0] == pytest.approx((3.0 + e1 * (-1.0 + 5.0)) / (1 + 2 * e1), abs=1e-14)
+
+
+def _closed_form(expr: str, names: dict) -> float:
+    """Evaluate a hand-written closed form: numbers, + - * /, unary minus,
+    exp, log and previously defined names only."""
+    import ast
+    import operator as op
+    bins = {ast.Add: op.add, ast.Sub: op.sub, ast.Mult: op.mul, ast.Div: op.truediv}
+    funcs = {"exp": math.exp, "log": math.log}
+
+    def ev(n):
+        if isinstance(n, ast.Expression):
+            return ev(n.body)
+        if isinstance(n, ast.Constant) and isinstance(n.value, (int, float)):
+            return float(n.value)
+        if isinstance(n, ast.BinOp) and type(n.op) in bins:
+            return bins[type(n.op)](ev(n.left), ev(n.right))
+        if isinstance(n, ast.UnaryOp) and isinstance(n.op, ast.USub):
+            return -ev(n.operand)
+        if isinstance(n, ast.Name) and n.id in names:
+            return names[n.id]
+        if isinstance(n, ast.Call) and isinstance(n.func, ast.Name) and n.func.id in funcs \
+                and len(n.args) == 1:
+            return funcs[n.func.id](ev(n.args[0]))
+        raise ValueError(f"unsupported closed form: {expr}")
+    return ev(ast.parse(expr, mode="eval"))
+
+
+def test_golden_worked_example_forward_and_backward():
+    """tests/golden/worked_example_three_tokens.json: a 3-token example whose
+    outputs and gradients were derived by hand from the definition."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "worked_example_three_tokens.json")
+    with open(path) as f:
+        g = json.load(f)
+    names = {}
+    for n, e in g["names"].items():
+        names[n] = _closed_form(e, names)
+    x = g["inputs"]
+    S = x["S"]
+    q, k, v, do = (np.array(x[n], dtype=np.float64).reshape(S, 1, 1)
+                   for n in ("q", "k", "v", "dout"))
+    o, lse = orc.attn_fwd(q, k, v, x["causal"])
+    grads = orc.attn_bwd(q, k, v, do, x["causal"])
+    got = {"o": o[:, 0, 0], "lse": lse[0], "dq": grads["dq"][:, 0, 0],
+           "dk": grads["dk"][:, 0, 0], "dv": grads["dv"][:, 0, 0]}
+    for n, exprs in g["expected"].items():
+        want = np.array([_closed_form(e, names) for e in exprs])
+        np.testing.assert_allclose(got[n], want, rtol=0, atol=g["tolerance"], err_msg=n)
 
 
 def test_q_zero_closed_form():
