@@ -205,30 +205,41 @@ __device__ __forceinline__ void lds_dma4_sv(const void* sbase, uint32_t voff, ui
 }
 
 // 64-row tile loads with the per-lane part of the address worked out once.
-// Wave w (of the 4 sharing a tile) issues its instruction i for the 1 KB
-// block 4 i + w; with that assignment the swizzled chunk a lane fetches is
-// the same for every i (for both HD = 128 and HD = 64), so the lane's byte
-// offset is fixed and instruction i only moves the wave-uniform base by
-// 4 i blocks of rows.  The LDS image is the one direct_tile64 writes.  Tiles
-// with fewer than 64 valid rows, or strides too long for a 32-bit offset,
-// take direct_tile64.
-template <int HD>
+// INTERLEAVED: wave w (of the 4 sharing a tile) issues its instruction i for
+// the 1 KB block 4 i + w; with that assignment the swizzled chunk a lane
+// fetches is the same for every i (for both HD = 128 and HD = 64), so one
+// per-lane byte offset serves all i and instruction i only moves the
+// wave-uniform base by 4 i blocks of rows.  Otherwise wave w takes the
+// consecutive blocks NI w + i (each wave one contiguous run of rows, the order
+// of direct_tile64) with one offset per instruction.  The LDS image is the one
+// direct_tile64 writes.  Tiles with fewer than 64 valid rows, or strides too
+// long for a 32-bit offset, take direct_tile64.
+template <int HD, bool INTERLEAVED>
 struct TileDma64 {
     static constexpr int ROWB = HD * 2, CPR = ROWB / 16, RPI = 1024 / ROWB, NI = 64 / (4 * RPI);
+    static constexpr int NOFF = INTERLEAVED ? 1 : NI;
     static constexpr int64_t kMaxRs = (int64_t)1 << 24;  // 64 rows x rs x 2 B < 2^31
-    uint32_t voff;
+    uint32_t voff[NOFF];
     __device__ __forceinline__ TileDma64(int64_t rs, int wave, int lane) {
-        const int row = wave * RPI + lane / CPR;  // row of instruction 0
-        const int lc = (lane % CPR) ^ swz<HD>(row);
-        voff = rs < kMaxRs ? (uint32_t)((row * rs + lc * 8) * 2) : 0u;
+#pragma unroll
+        for (int i = 0; i < NOFF; ++i) {
+            const int blk = INTERLEAVED ? wave : wave * NI + i;
+            const int row = blk * RPI + lane / CPR;
+            const int lc = (lane % CPR) ^ swz<HD>(row);
+            voff[i] = rs < kMaxRs ? (uint32_t)((row * rs + lc * 8) * 2) : 0u;
+        }
     }
     __device__ __forceinline__ void load(char* lds_tile, const uint16_t* base, int64_t rs,
                                          int64_t nvalid, int wave, int lane) const {
         if (nvalid >= 64 && rs < kMaxRs) {
 #pragma unroll
-            for (int i = 0; i < NI; ++i)
-                lds_dma16_sv(base + (int64_t)i * 4 * RPI * rs, voff,
-                             lds_addr(lds_tile + (i * 4 + wave) * 1024));
+            for (int i = 0; i < NI; ++i) {
+                if constexpr (INTERLEAVED)
+                    lds_dma16_sv(base + (int64_t)i * 4 * RPI * rs, voff[0],
+                                 lds_addr(lds_tile + (i * 4 + wave) * 1024));
+                else
+                    lds_dma16_sv(base, voff[i], lds_addr(lds_tile + (wave * NI + i) * 1024));
+            }
         } else {
             direct_tile64<HD>(lds_tile, base, rs, nvalid, wave, lane);
         }

@@ -165,8 +165,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(FwdParams p) {
     const uint16_t* kvh = kv_sel == 0 ? kh : vh;
     const int64_t kv_rs = kv_sel == 0 ? p.k_rs : p.v_rs;
     // per-lane parts of the tile-load addresses (8 waves: K or V; 4 waves: both)
-    const TileDma64<HD> dkv(NW == 8 ? kv_rs : p.k_rs, wave & 3, lane);
-    const TileDma64<HD> dv2(p.v_rs, wave & 3, lane);
+    const TileDma64<HD, true> dkv(NW == 8 ? kv_rs : p.k_rs, wave & 3, lane);
+    const TileDma64<HD, true> dv2(p.v_rs, wave & 3, lane);
     auto issue = [&](int t) {
         const int64_t nb = (int64_t)t * BN;
         if constexpr (NW == 8) {
