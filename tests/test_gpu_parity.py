@@ -67,6 +67,14 @@ def test_peaked_softmax():
     _run_case(512, 2, 1, 128, [2, 1], seed=15, q_scale=8.0, rel=True)
 
 
+@pytest.mark.parametrize("S,D", [(319, 128), (320, 128), (321, 64), (384, 64)])
+def test_tile_load_boundaries(S, D):
+    # the last 64-row tile of keys (forward, dQ) and of queries (dK/dV) is
+    # short by one row, exactly full, or holds a single row: full tiles take
+    # the scalar-base loads, short ones the clamping path
+    _run_case(S, 4, 2, D, [4, 1], seed=40 + S)
+
+
 def test_single_token_and_tiny():
     for S in (1, 2, 33):
         _run_case(S, 2, 1, 128, [2, 1], seed=16 + S)
