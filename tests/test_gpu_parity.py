@@ -38,6 +38,26 @@ def test_tiny_exactness_case_all_head_chunks():
     _run_case(256, 4, 2, 64, [4, 1, 2], seed=1)
 
 
+def test_tiny_case_fp32_variant_reports_input_rounding():
+    # the tiny case's fp32 variant: the oracle on the fp32 draws themselves
+    # against the GPU on their bf16 rounding.  The difference is the effect
+    # of rounding the inputs to bf16 (the GPU path takes bf16 only); it is
+    # reported, and only held to a loose bound that catches gross errors.
+    from head_chunked_context_amd.inputs import attention_inputs
+    from oracle import oracle as orc
+    x32 = attention_inputs(256, 4, 2, 64, 1, device="cpu", dtype=torch.float32)
+    d = {n: t.to(torch.bfloat16).to(DEV) for n, t in x32.items()}
+    o, lse = gpu_fwd(d, 2)
+    dq, dk, dv = gpu_bwd(d, o, lse, 2)
+    ro, rl = orc.attn_fwd(x32["q"], x32["k"], x32["v"], True)
+    rg = orc.attn_bwd(x32["q"], x32["k"], x32["v"], x32["dout"], True)
+    errs = {"o": maxabs(f64(o), ro), "lse": maxabs(f64(lse), rl), "dq": maxabs(f64(dq), rg["dq"]),
+            "dk": maxabs(f64(dk), rg["dk"]), "dv": maxabs(f64(dv), rg["dv"])}
+    print("fp32 variant, GPU(bf16(x)) vs oracle(x):",
+          "  ".join(f"{n} {e:.3e}" for n, e in errs.items()), flush=True)
+    assert all(np.isfinite(e) and e < 0.25 for e in errs.values()), errs
+
+
 def test_ragged_tail_d128():
     _run_case(1000, 4, 2, 128, [4, 1, 2], seed=11)
 
