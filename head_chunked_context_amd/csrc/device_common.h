@@ -183,8 +183,10 @@ __device__ __forceinline__ void direct_tile64(char* lds_tile, const uint16_t* ba
 }
 
 // The same loads in the scalar-base form: a wave-uniform 64-bit global
-// address in an SGPR pair plus a 32-bit per-lane byte offset, so a load needs
-// no per-lane 64-bit address arithmetic.
+// address in an SGPR pair plus a 32-bit per-lane byte offset (below 2^31
+// here), so a load needs no per-lane 64-bit address arithmetic.  The base
+// must be the same in every lane: readfirstlane keeps the first active
+// lane's value.
 __device__ __forceinline__ uint64_t uniform_addr(const void* p) {
     const uint64_t a = (uint64_t)(uintptr_t)p;
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
