@@ -100,6 +100,41 @@ def test_single_token_and_tiny():
         _run_case(S, 2, 1, 128, [2, 1], seed=16 + S)
 
 
+def _random_cases(n, seed):
+    # seeded shapes: S across tile and workgroup boundaries, GQA ratios 1-8,
+    # chunks that split groups, D 64/128, causal or not, key/value trunks
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        Hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([1, 2, 4, 8]))
+        Hq = Hkv * g
+        S = int(rng.integers(1, 1600))
+        D = int(rng.choice([64, 128]))
+        causal = bool(rng.random() < 0.75)
+        hcs = sorted({Hq, int(rng.integers(1, Hq + 1))}, reverse=True)
+        T = int(rng.choice([0, 0, 256, 512])) if S > 256 else 0
+        cases.append((S, Hq, Hkv, D, causal, hcs, T))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(10, 2024))
+def test_random_shapes_match_oracle(case):
+    S, Hq, Hkv, D, causal, hcs, T = case
+    inp = inputs_cpu(S, Hq, Hkv, D, 50 + S % 97)
+    d = to_dev(inp)
+    outs = []
+    for hc in hcs:
+        print(f"random case S={S} Hq={Hq} Hkv={Hkv} D={D} causal={causal} hc={hc} T={T}",
+              flush=True)
+        o, lse = gpu_fwd(d, hc, trunk=T, causal=causal)
+        outs.append((o, lse) + tuple(gpu_bwd(d, o, lse, hc, trunk=T, causal=causal)))
+    for x, y in zip(outs[0], outs[-1]):
+        assert torch.equal(x, y), "results differ bitwise across head_chunk"
+    check_fwd(inp, outs[0][0], outs[0][1], causal)
+    check_bwd(inp, outs[0][2:], causal)
+
+
 def test_run_to_run_deterministic():
     inp = inputs_cpu(777, 4, 2, 128, 21)
     d = to_dev(inp)
