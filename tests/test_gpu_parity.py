@@ -344,3 +344,67 @@ def test_hip_graph_capture_replays_bitwise(trunk, kv_host):
         torch.cuda.synchronize()
         for x, y, n in zip((o, lse, dq, dk, dv), (o_e, l_e) + tuple(g_e), ("o", "lse", "dq", "dk", "dv")):
             assert torch.equal(x.cpu(), y.cpu()), f"replay {rep}: {n} differs from the eager result"
+
+
+def _guarded(n, dtype, device, fill, guard_bytes=4096, pin=False):
+    """n elements inside a buffer whose every byte (and guard_bytes more on
+    each side) starts as `fill`; returns (buffer, view of the n elements)."""
+    el = torch.empty((), dtype=dtype).element_size()
+    g = guard_bytes // el
+    buf = torch.empty(n + 2 * g, dtype=dtype, device=device, pin_memory=pin)
+    buf.view(torch.uint8).fill_(fill)
+    return buf, buf[g:g + n]
+
+
+def _guards_intact(buf, view, fill):
+    b = buf.view(torch.uint8)
+    lo = view.data_ptr() - buf.data_ptr()
+    hi = lo + view.numel() * view.element_size()
+    return bool((b[:lo] == fill).all()) and bool((b[hi:] == fill).all())
+
+
+@pytest.mark.parametrize("trunk,kv_host,hc", [(0, False, 4), (0, False, 1), (256, False, 3),
+                                              (256, True, 1)])
+def test_poisoned_workspace_and_guard_bytes(trunk, kv_host, hc):
+    # every workspace byte starts as 0xFF (NaN in bf16 and fp32): results must
+    # equal those of a zeroed workspace bit for bit, so no kernel reads
+    # workspace it has not written; the outputs and the workspace sit between
+    # guard bytes that must come back untouched
+    from head_chunked_context_amd import attn_bwd, attn_fwd
+    from head_chunked_context_amd import hcattn as H
+    S, Hq, Hkv, D = 900, 8, 2, 128  # g = 4: hc = 1 and 3 carry dK/dV across chunks
+    inp = inputs_cpu(S, Hq, Hkv, D, 61)
+    d = to_dev(inp, kv_host=kv_host)
+    print(f"poison S={S} hc={hc} T={trunk} kv_host={kv_host}", flush=True)
+    nf = H.fwd_workspace_bytes(S, Hq, Hkv, D, True, hc, trunk)
+    nb = H.bwd_workspace_bytes(S, Hq, Hkv, D, True, hc, trunk)
+    zf = torch.zeros(nf, dtype=torch.uint8, device=DEV)
+    zb = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    o_ref, l_ref = attn_fwd(d["q"], d["k"], d["v"], head_chunk=hc, kv_trunk=trunk, workspace=zf)
+    g_ref = attn_bwd(d["q"], d["k"], d["v"], o_ref, d["dout"], l_ref, head_chunk=hc,
+                     kv_trunk=trunk, workspace=zb)
+    torch.cuda.synchronize()
+
+    C = 0x5A
+    wfb, wf = _guarded(nf, torch.uint8, DEV, 0xFF)
+    wbb, wb = _guarded(nb, torch.uint8, DEV, 0xFF)
+    ob, o = _guarded(S * Hq * D, torch.bfloat16, DEV, C)
+    lb, lse = _guarded(Hq * S, torch.float32, DEV, C)
+    dqb, dq = _guarded(S * Hq * D, torch.bfloat16, DEV, C)
+    kdev = "cpu" if kv_host else DEV
+    dkb, dk = _guarded(S * Hkv * D, torch.bfloat16, kdev, C, pin=kv_host)
+    dvb, dv = _guarded(S * Hkv * D, torch.bfloat16, kdev, C, pin=kv_host)
+    o, lse = o.view(S, Hq, D), lse.view(Hq, S)
+    dq, dk, dv = dq.view(S, Hq, D), dk.view(S, Hkv, D), dv.view(S, Hkv, D)
+    attn_fwd(d["q"], d["k"], d["v"], head_chunk=hc, kv_trunk=trunk, out=o, lse=lse, workspace=wf)
+    attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, head_chunk=hc, kv_trunk=trunk,
+             dq=dq, dk=dk, dv=dv, workspace=wb)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), "forward depends on workspace contents"
+    for a, b, n in zip((dq, dk, dv), g_ref, ("dq", "dk", "dv")):
+        assert torch.equal(a, b), f"{n} depends on workspace contents"
+    for buf, view, fill, n in ((ob, o, C, "o"), (lb, lse, C, "lse"), (dqb, dq, C, "dq"),
+                               (dkb, dk, C, "dk"), (dvb, dv, C, "dv"),
+                               (wfb, wf, 0xFF, "forward workspace"),
+                               (wbb, wb, 0xFF, "backward workspace")):
+        assert _guards_intact(buf, view, fill), f"bytes next to {n} were written"
