@@ -97,6 +97,13 @@ static inline int make_plan(bool bwd, int64_t S, int Hq, int Hkv, int D, int cau
         snprintf(err, errlen, "S = %lld exceeds 2^30 tokens", (long long)S);
         return -2;
     }
+    // every workspace region is at most a few dozen bytes per (head, token,
+    // channel); refuse shapes whose byte counts could wrap a 64-bit size
+    if ((double)S * ((double)Hq + (double)Hkv) * (double)D * 64.0 > 0x1p62) {
+        snprintf(err, errlen, "S = %lld with %d + %d heads is too large to address",
+                 (long long)S, Hq, Hkv);
+        return -2;
+    }
     Plan p;
     p.bwd = bwd;
     p.S = S; p.Hq = Hq; p.Hkv = Hkv; p.D = D; p.causal = causal;

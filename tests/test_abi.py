@@ -95,6 +95,7 @@ def test_head_chunk_zero_means_all_heads():
     ((4096, 4, 2, 128, 1, 0, 100), -1),  # trunk not a multiple of 256
     ((64, 4, 2, 128, 1, -1, 0), -1),
     (((1 << 30) + 1, 4, 2, 128, 1, 0, 0), -2),  # beyond 2^30 tokens
+    ((1 << 30, 1 << 30, 1, 128, 1, 0, 0), -2),  # workspace bytes would wrap 64 bits
 ])
 def test_invalid_arguments_return_status_before_any_gpu_work(args, code):
     L = lib()
