@@ -555,15 +555,9 @@ int bwd_trunked(Common& c, const BwdIO& io) {
                     (int64_t)p.Hkv * D, D);
             }
             LAUNCH_PASS(K_REDUCE, rd, hc::launch_dkdv_reduce(rd, c.st));
-            hc::DqParams dq = dq_params(c, ch, io, kk, vv, (int64_t)ch.nkv * D, D, kr0, nk);
-            dq.q_begin = p.causal ? kr0 : 0;
-            dq.acc_in = t == 0 ? nullptr : dQacc;
-            dq.ain_rs = D; dq.ain_hs = S * D;
-            dq.acc_out = dQacc; dq.aout_rs = D; dq.aout_hs = S * D;
-            dq.final_before = p.causal ? kr0 + nk : (t == p.N - 1 ? S : 0);
-            LAUNCH(K_DQ, hc::launch_dq(dq, D, c.st));
-            r = ring.release(slot);
-            if (r) return r;
+            // the finished dK/dV rows leave as soon as the reduce has staged
+            // them, so their copy, and the next trunk's load queued behind it
+            // on the copy stream, run while dQ of this trunk computes
             if (io.kv_host && nfin > 0) {
                 Device* d = c.dev;
                 HIPCHK(hipEventRecord(d->ev[EV_STAGED0 + ss], c.st));
@@ -580,6 +574,15 @@ int bwd_trunked(Common& c, const BwdIO& io) {
             } else if (io.kv_host) {
                 ++nstage;
             }
+            hc::DqParams dq = dq_params(c, ch, io, kk, vv, (int64_t)ch.nkv * D, D, kr0, nk);
+            dq.q_begin = p.causal ? kr0 : 0;
+            dq.acc_in = t == 0 ? nullptr : dQacc;
+            dq.ain_rs = D; dq.ain_hs = S * D;
+            dq.acc_out = dQacc; dq.aout_rs = D; dq.aout_hs = S * D;
+            dq.final_before = p.causal ? kr0 + nk : (t == p.N - 1 ? S : 0);
+            LAUNCH(K_DQ, hc::launch_dq(dq, D, c.st));
+            r = ring.release(slot);
+            if (r) return r;
         }
     }
     return ATTN_OK;
