@@ -33,7 +33,8 @@
  *                    scaled scores (output of attn_fwd, input of attn_bwd).
  *                    attn_fwd accepts NULL (forward-only use: no LSE kept).
  *   1 <= S <= 2^30 (longer: ATTN_EUNSUPPORTED); Hq, Hkv >= 1 with
- *   Hq % Hkv == 0; D == 64 or 128;
+ *   Hq % Hkv == 0; D == 64 or 128; S * (Hq + Hkv) * D * 64 <= 2^62 (larger
+ *   shapes could wrap the 64-bit workspace sizes: ATTN_EUNSUPPORTED);
  *   causal 0 or 1 (1 is the measured case; 0 runs the same kernels).
  *   head_chunk     : query heads per chunk, 0 means Hq; 1..Hq.  Chunks are
  *                    consecutive ascending head ranges; the last may be short.
