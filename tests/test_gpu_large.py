@@ -134,6 +134,27 @@ def test_wide_and_narrow_workgroups_give_the_same_bits(D):
     check_last_keys(d, dk, dv, n=16)
 
 
+def test_die_aware_dkdv_order_gives_the_same_bits():
+    # dK/dV launches whose head count is not a multiple of 4 take runs of 32
+    # work items per die in a snake order over windows of 256 workgroups;
+    # S = 66000 has 516 key tiles of 128, so head_chunk 1 (516 workgroups: two
+    # full windows and a partial one) and 2 (1032) take that order while 4
+    # keeps the plain one: every result must come out bit for bit the same
+    S, Hq, Hkv, D = 66000, 4, 1, 128
+    d = attention_inputs(S, Hq, Hkv, D, 9, device=DEV)
+    outs = []
+    for hc in (4, 2, 1):
+        print(f"die-aware order S={S} hc={hc}", flush=True)
+        outs.append(run(d, hc))
+    for b in outs[1:]:
+        for x, y, n in zip(outs[0], b, ("o", "lse", "dq", "dk", "dv")):
+            assert torch.equal(x, y), f"{n} differs between the plain and die-aware orders"
+    o, lse, dq, dk, dv = outs[0]
+    check_rows(d, o, lse, dq, sample_rows(S, n_random=4))
+    check_last_keys(d, dk, dv, n=16)
+    check_sum_identities(d, dk, dv, Hq // Hkv)
+
+
 @slow
 def test_workload3_head_chunk_sweep_bitwise_and_samples():
     w = WORKLOADS[3]
