@@ -134,17 +134,18 @@ def test_wide_and_narrow_workgroups_give_the_same_bits(D):
     check_last_keys(d, dk, dv, n=16)
 
 
-def test_die_aware_dkdv_order_gives_the_same_bits():
+@pytest.mark.parametrize("D", [128, 64])
+def test_die_aware_dkdv_order_gives_the_same_bits(D):
     # dK/dV launches whose head count is not a multiple of 4 take runs of 32
     # work items per die in a snake order over windows of 256 workgroups;
     # S = 66000 has 516 key tiles of 128, so head_chunk 1 (516 workgroups: two
     # full windows and a partial one) and 2 (1032) take that order while 4
     # keeps the plain one: every result must come out bit for bit the same
-    S, Hq, Hkv, D = 66000, 4, 1, 128
+    S, Hq, Hkv = 66000, 4, 1
     d = attention_inputs(S, Hq, Hkv, D, 9, device=DEV)
     outs = []
     for hc in (4, 2, 1):
-        print(f"die-aware order S={S} hc={hc}", flush=True)
+        print(f"die-aware order S={S} D={D} hc={hc}", flush=True)
         outs.append(run(d, hc))
     for b in outs[1:]:
         for x, y, n in zip(outs[0], b, ("o", "lse", "dq", "dk", "dv")):
