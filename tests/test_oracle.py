@@ -10,6 +10,7 @@ rely on (head chunks reuse buffers without changing results; key trunks merge
 by softmax statistics into the untrunked result).
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -149,28 +150,39 @@ def _closed_form(expr: str, names: dict) -> float:
     return ev(ast.parse(expr, mode="eval"))
 
 
-def test_golden_worked_example_forward_and_backward():
-    """tests/golden/worked_example_three_tokens.json: a 3-token example whose
-    outputs and gradients were derived by hand from the definition."""
-    import json
+def _golden_files():
+    import glob
     import os
-    path = os.path.join(os.path.dirname(__file__), "golden", "worked_example_three_tokens.json")
+    return sorted(glob.glob(os.path.join(os.path.dirname(__file__), "golden", "*.json")))
+
+
+def _check_golden(path):
+    import json
     with open(path) as f:
         g = json.load(f)
     names = {}
     for n, e in g["names"].items():
         names[n] = _closed_form(e, names)
     x = g["inputs"]
-    S = x["S"]
-    q, k, v, do = (np.array(x[n], dtype=np.float64).reshape(S, 1, 1)
+    S, Hq, Hkv, D = x["S"], x["Hq"], x["Hkv"], x["D"]
+    shape = {"q": (S, Hq, D), "k": (S, Hkv, D), "v": (S, Hkv, D), "dout": (S, Hq, D)}
+    q, k, v, do = (np.array(x[n], dtype=np.float64).reshape(shape[n])
                    for n in ("q", "k", "v", "dout"))
     o, lse = orc.attn_fwd(q, k, v, x["causal"])
     grads = orc.attn_bwd(q, k, v, do, x["causal"])
-    got = {"o": o[:, 0, 0], "lse": lse[0], "dq": grads["dq"][:, 0, 0],
-           "dk": grads["dk"][:, 0, 0], "dv": grads["dv"][:, 0, 0]}
+    got = {"o": o, "lse": lse, "dq": grads["dq"], "dk": grads["dk"], "dv": grads["dv"]}
+    ev = np.vectorize(lambda e: _closed_form(e, names), otypes=[np.float64])
     for n, exprs in g["expected"].items():
-        want = np.array([_closed_form(e, names) for e in exprs])
+        want = ev(np.array(exprs, dtype=object)).reshape(got[n].shape)
         np.testing.assert_allclose(got[n], want, rtol=0, atol=g["tolerance"], err_msg=n)
+
+
+@pytest.mark.parametrize("name", [os.path.basename(p) for p in _golden_files()])
+def test_golden_worked_examples(name):
+    """tests/golden/*.json: small examples whose outputs and gradients were
+    derived by hand from the definition (a 3-token single head with D = 1;
+    two query heads sharing one key/value head with D = 4)."""
+    _check_golden(os.path.join(os.path.dirname(__file__), "golden", name))
 
 
 def test_q_zero_closed_form():

@@ -64,7 +64,16 @@ def pins():
         ("chunks", lambda: T.test_head_chunks_reuse_buffers_without_changing_results(3)),
         ("trunks", lambda: T.test_key_trunks_merge_to_untrunked(37, 8, True)),
         ("sampled", T.test_sampled_rows_and_columns_match_full),
+        ("golden", lambda: [T._check_golden(p) for p in T._golden_files()]),
     ]
+
+
+# mistakes the hand-derived golden examples alone must catch (they have one
+# key/value head and no trunks or chunks, so GQA-index, merge and chunk
+# mistakes are left to the other pins)
+GOLDEN_CATCHES = [m[0] for m in MUTATIONS if m[0] not in (
+    "GQA maps head h to kv h % Hkv", "trunk merge weights swapped",
+    "chunk buffers read the wrong kv head")]
 
 
 @pytest.fixture(scope="module")
@@ -95,3 +104,22 @@ def test_pins_catch_planted_mistake(workdir, name, old, new, count):
     finally:
         orc.restore_library(prev)
     assert caught, f"no pin caught the planted mistake: {name}"
+
+
+@pytest.mark.parametrize("name", GOLDEN_CATCHES)
+def test_golden_examples_catch_planted_mistake(workdir, name):
+    old, new, count = {m[0]: m[1:] for m in MUTATIONS}[name]
+    src = open(SRC).read()
+    mutated = src.replace(old, new) if count < 0 else src.replace(old, new, count)
+    cpath = os.path.join(workdir, "g.c")
+    lpath = os.path.join(workdir, f"g_{abs(hash(name))}.so")
+    open(cpath, "w").write(mutated)
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-shared", "-fPIC", "-o", lpath, cpath, "-lm"],
+                   check=True)
+    prev = orc.use_library(lpath)
+    try:
+        with pytest.raises(AssertionError):
+            for p in T._golden_files():
+                T._check_golden(p)
+    finally:
+        orc.restore_library(prev)
