@@ -69,11 +69,10 @@ def pins():
 
 
 # mistakes the hand-derived golden examples alone must catch (they have one
-# key/value head and no trunks or chunks, so GQA-index, merge and chunk
-# mistakes are left to the other pins)
+# key/value head, so GQA-index and chunk-buffer mistakes are left to the
+# other pins)
 GOLDEN_CATCHES = [m[0] for m in MUTATIONS if m[0] not in (
-    "GQA maps head h to kv h % Hkv", "trunk merge weights swapped",
-    "chunk buffers read the wrong kv head")]
+    "GQA maps head h to kv h % Hkv", "chunk buffers read the wrong kv head")]
 
 
 @pytest.fixture(scope="module")
