@@ -7,10 +7,17 @@ workload is trunked) over one batch of seeded synthetic bf16 inputs already
 resident in HBM.  Throughput counts the causal FLOPs 2*S^2*D*Hq for the
 forward and 2.5x that for the backward (7*S^2*D*Hq per step).
 
+Default workload: Llama3-8B heads at S=262144 (Hq=32, Hkv=8, D=128) with one
+GQA group per chunk (head_chunk 4), the configuration whose head_chunk sweep
+reports throughput and peak workspace bytes per setting.
+
 Prints one JSON line.  Extra fields: the per-kernel roofline of the dominant
-kernel (HIP events around every launch, on the stream it runs on), workspace
-bytes per head_chunk (peak intermediate device memory), and the fp64 CPU
-oracle timed on a bounded sample of the same workload on the host cores.
+kernel (HIP events around every launch, on the stream it runs on), the
+head_chunk sweep (TFLOP/s and workspace / peak intermediate bytes per
+setting), a forward-only (prefill, no LSE kept) line, the 32B-class shape with
+K/V trunks in pinned host memory (PCIe-inclusive, so never the headline), and
+the fp64 CPU oracle timed on a bounded sample of the same workload on the
+host cores.
 """
 from __future__ import annotations
 
@@ -30,11 +37,18 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
-                    help="attention workload id (2 = Llama3-8B layer, S=32768)")
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5],
+                    help="attention workload id (3 = Llama3-8B heads at S=262144)")
     ap.add_argument("--head-chunk", type=int, default=0,
                     help="query heads per chunk (default: one GQA group for workload 2/3)")
-    ap.add_argument("--no-compare", action="store_true", help="skip the other head_chunk")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the other head_chunk settings of the workload")
+    ap.add_argument("--sweep-steps", type=int, default=2,
+                    help="timed steps per other head_chunk setting")
+    ap.add_argument("--no-forward-only", action="store_true",
+                    help="skip the forward-only (no LSE) line")
+    ap.add_argument("--no-host-trunks", action="store_true",
+                    help="skip the pinned-host-trunk line (workload 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=12288,
                     help="tokens of the CPU-oracle sample (one GQA group)")
@@ -137,6 +151,86 @@ def cpu_oracle_baseline(D: int, g: int, tokens: int) -> dict:
                       f"FLOPs 7*S^2*D*heads"}
 
 
+def run_workload(hcm, torch, w, hc, T, dev, steps, warmup, timing, kv_on_host, trunk_merge=False,
+                 forward_only=False):
+    """Seeded inputs of workload w, then W warm-up and K timed steps at one
+    head_chunk.  Returns the timings, workspace bytes and peak intermediate
+    device memory (torch's peak-allocation delta over the user tensors)."""
+    from head_chunked_context_amd.inputs import attention_inputs
+    S, Hq, Hkv, D = w.S, w.Hq, w.Hkv, w.D
+    causal = True
+    inp = attention_inputs(S, Hq, Hkv, D, w.wid, device=dev, with_dout=not forward_only)
+    if kv_on_host:
+        for n in ("k", "v"):
+            inp[n] = inp[n].cpu().pin_memory()
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp.get("dout")
+    o = torch.empty_like(q)
+    lse = None if forward_only else torch.empty((Hq, S), dtype=torch.float32, device=dev)
+    if not forward_only:
+        dq = torch.empty_like(q)
+        pin = k.device.type == "cpu"
+        dk = torch.empty(k.shape, dtype=k.dtype, device=k.device, pin_memory=pin)
+        dv = torch.empty(v.shape, dtype=v.dtype, device=v.device, pin_memory=pin)
+    fb = hcm.fwd_workspace_bytes(S, Hq, Hkv, D, causal, hc, T)
+    bb = 0 if forward_only else hcm.bwd_workspace_bytes(S, Hq, Hkv, D, causal, hc, T)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    ws = torch.empty(max(fb, bb), dtype=torch.uint8, device=dev)
+
+    def step():
+        hcm.attn_fwd(q, k, v, head_chunk=hc, kv_trunk=T, causal=causal, out=o, lse=lse,
+                     workspace=ws, with_lse=not forward_only)
+        mid = torch.cuda.Event(enable_timing=True)
+        mid.record()
+        if not forward_only:
+            hcm.attn_bwd(q, k, v, o, do, lse, head_chunk=hc, kv_trunk=T, causal=causal, dq=dq,
+                         dk=dk, dv=dv, workspace=ws)
+        return mid
+
+    prev_merge = hcm.set_trunk_merge(trunk_merge)
+    try:
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        print(f"{w.name}: head_chunk={hc}{' forward only' if forward_only else ''}: {warmup} "
+              f"warm-up step(s) done, timing {steps}", file=sys.stderr, flush=True)
+        if timing:
+            hcm.timing_reset()
+            hcm.timing_enable(True)
+        starts, mids = [], []
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t_start.record()
+        for _ in range(steps):
+            s = torch.cuda.Event(enable_timing=True)
+            s.record()
+            starts.append(s)
+            mids.append(step())
+        t_end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+    finally:
+        hcm.set_trunk_merge(prev_merge)
+    kern = moved = None
+    if timing:
+        hcm.timing_enable(False)
+        kern = hcm.timing_read()
+        moved = hcm.timing_bytes()
+        hcm.timing_reset()
+    total_ms = t_start.elapsed_time(t_end)
+    fwd_ms = sum(a.elapsed_time(b) for a, b in zip(starts, mids))
+    peak = torch.cuda.max_memory_allocated(dev) - base
+    del ws
+    print(f"{w.name}: head_chunk={hc}: {total_ms / steps:.1f} ms per step", file=sys.stderr,
+          flush=True)
+    return {"ms": total_ms / steps, "fwd_ms": fwd_ms / steps,
+            "bwd_ms": (total_ms - fwd_ms) / steps, "wall_s": wall, "kern": kern, "moved": moved,
+            "ws_fwd": fb, "ws_bwd": bb, "peak_intermediate": peak}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -149,10 +243,10 @@ def main():
     import torch
 
     import head_chunked_context_amd as hcm
-    from head_chunked_context_amd.inputs import WORKLOADS, attention_inputs
+    from head_chunked_context_amd.inputs import WORKLOADS
 
     w = WORKLOADS[args.workload]
-    hc = args.head_chunk or w.head_chunks[0]
+    hc = args.head_chunk or (w.Hq // w.Hkv if w.Hq // w.Hkv in w.head_chunks else w.head_chunks[0])
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     S, Hq, Hkv, D, T = w.S, w.Hq, w.Hkv, w.D, w.kv_trunk
@@ -163,25 +257,6 @@ def main():
         T = int(args.kv_trunk)
     causal = True
 
-    if args.trunk_merge:
-        hcm.set_trunk_merge(True)
-    inp = attention_inputs(S, Hq, Hkv, D, w.wid, device=dev)
-    if w.kv_on_host:
-        for n in ("k", "v"):
-            inp[n] = inp[n].cpu().pin_memory()
-    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["dout"]
-
-    def alloc_outputs():
-        o = torch.empty_like(q)
-        lse = torch.empty((Hq, S), dtype=torch.float32, device=dev)
-        dq = torch.empty_like(q)
-        pin = k.device.type == "cpu"
-        dk = torch.empty(k.shape, dtype=k.dtype, device=k.device, pin_memory=pin)
-        dv = torch.empty(v.shape, dtype=v.dtype, device=v.device, pin_memory=pin)
-        return o, lse, dq, dk, dv
-
-    o, lse, dq, dk, dv = alloc_outputs()
-    torch.cuda.synchronize()
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         a = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -191,60 +266,8 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    def measure(hc_, steps, warmup, timing):
-        fb = hcm.fwd_workspace_bytes(S, Hq, Hkv, D, causal, hc_, T)
-        bb = hcm.bwd_workspace_bytes(S, Hq, Hkv, D, causal, hc_, T)
-        torch.cuda.synchronize()
-        torch.cuda.reset_peak_memory_stats(dev)
-        base = torch.cuda.memory_allocated(dev)
-        ws = torch.empty(max(fb, bb), dtype=torch.uint8, device=dev)
-
-        def step():
-            hcm.attn_fwd(q, k, v, head_chunk=hc_, kv_trunk=T, causal=causal, out=o, lse=lse,
-                         workspace=ws)
-            mid = torch.cuda.Event(enable_timing=True)
-            mid.record()
-            hcm.attn_bwd(q, k, v, o, do, lse, head_chunk=hc_, kv_trunk=T, causal=causal, dq=dq,
-                         dk=dk, dv=dv, workspace=ws)
-            return mid
-
-        for _ in range(warmup):
-            step()
-        torch.cuda.synchronize()
-        print(f"head_chunk={hc_}: {warmup} warm-up step(s) done, timing {steps}", file=sys.stderr,
-              flush=True)
-        if timing:
-            hcm.timing_reset()
-            hcm.timing_enable(True)
-        starts, mids = [], []
-        t_start = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        wall0 = time.perf_counter()
-        t_start.record()
-        for _ in range(steps):
-            s = torch.cuda.Event(enable_timing=True)
-            s.record()
-            starts.append(s)
-            mids.append(step())
-        t_end.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        kern = moved = None
-        if timing:
-            hcm.timing_enable(False)
-            kern = hcm.timing_read()
-            moved = hcm.timing_bytes()
-            hcm.timing_reset()
-        total_ms = t_start.elapsed_time(t_end)
-        fwd_ms = sum(a.elapsed_time(b) for a, b in zip(starts, mids))
-        peak = torch.cuda.max_memory_allocated(dev) - base
-        del ws
-        return {"ms": total_ms / steps, "fwd_ms": fwd_ms / steps,
-                "bwd_ms": (total_ms - fwd_ms) / steps, "wall_s": wall, "kern": kern,
-                "moved": moved,
-                "ws_fwd": fb, "ws_bwd": bb, "peak_intermediate": peak}
-
-    r = measure(hc, args.steps, args.warmup, timing=True)
+    r = run_workload(hcm, torch, w, hc, T, dev, args.steps, args.warmup, True, w.kv_on_host,
+                     args.trunk_merge)
     flops = 7.0 * S * S * D * Hq
     tflops = flops / (r["ms"] / 1e3) / 1e12
 
@@ -299,19 +322,44 @@ def main():
                            "frac": round(r["moved"][f] / (kern[f][1] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
                        for f in ("pack", "prep", "merge", "reduce") if kern[f][0] and kern[f][1] > 0},
     }
+    # throughput and peak workspace per head_chunk setting of the workload
     others = [h for h in w.head_chunks if h != hc]
     if not args.no_compare and others:
-        other = Hq if Hq in others else others[-1]
-        r2 = measure(other, max(1, min(3, args.steps)), 1, timing=False)
-        line["workspace_bytes"][str(other)] = {"fwd": r2["ws_fwd"], "bwd": r2["ws_bwd"],
-                                               "peak_intermediate": r2["peak_intermediate"]}
-        line["head_chunk_compare"] = {
-            "head_chunk": other,
-            "value": round(flops / (r2["ms"] / 1e3) / 1e12, 2),
-            "ms_per_step": round(r2["ms"], 3),
-            "workspace_ratio": round(max(r["ws_fwd"], r["ws_bwd"]) /
-                                     max(r2["ws_fwd"], r2["ws_bwd"]), 4),
-        }
+        sweep = {str(hc): {"value": line["value"], "ms_per_step": line["ms_per_step"]}}
+        for other in others:
+            r2 = run_workload(hcm, torch, w, other, T, dev, max(1, args.sweep_steps), 1, False,
+                              w.kv_on_host, args.trunk_merge)
+            line["workspace_bytes"][str(other)] = {"fwd": r2["ws_fwd"], "bwd": r2["ws_bwd"],
+                                                   "peak_intermediate": r2["peak_intermediate"]}
+            sweep[str(other)] = {"value": round(flops / (r2["ms"] / 1e3) / 1e12, 2),
+                                 "ms_per_step": round(r2["ms"], 3)}
+        full = str(Hq) if str(Hq) in line["workspace_bytes"] else None
+        if full is not None:
+            wb = line["workspace_bytes"]
+            for h in sweep:
+                sweep[h]["workspace_ratio_vs_unchunked"] = round(
+                    max(wb[h]["fwd"], wb[h]["bwd"]) / max(wb[full]["fwd"], wb[full]["bwd"]), 4)
+        line["head_chunk_sweep"] = sweep
+    # forward-only (prefill) mode: no LSE kept, no backward workspace
+    if not args.no_forward_only:
+        rf = run_workload(hcm, torch, w, hc, T, dev, 3, 1, False, w.kv_on_host, args.trunk_merge,
+                          forward_only=True)
+        line["forward_only"] = {"tflops": round(2.0 * S * S * D * Hq / (rf["ms"] / 1e3) / 1e12, 2),
+                                "ms": round(rf["ms"], 3), "workspace_bytes": rf["ws_fwd"],
+                                "peak_intermediate": rf["peak_intermediate"]}
+    # the 32B-class shape with 65536-token K/V trunks in pinned host memory:
+    # the trunk copies cross PCIe inside the step (PCIe-inclusive rate)
+    if not args.no_host_trunks and args.workload != 4:
+        torch.cuda.empty_cache()
+        w4 = WORKLOADS[4]
+        r4 = run_workload(hcm, torch, w4, w4.head_chunks[0], w4.kv_trunk, dev, 1, 1, False, True)
+        f4 = 7.0 * w4.S * w4.S * w4.D * w4.Hq
+        line["pinned_host_trunks"] = {
+            "workload": w4.name, "head_chunk": w4.head_chunks[0], "kv_trunk": w4.kv_trunk,
+            "tflops": round(f4 / (r4["ms"] / 1e3) / 1e12, 2), "ms_per_step": round(r4["ms"], 1),
+            "pct_bf16_peak": round(100.0 * f4 / (r4["ms"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "workspace_bytes": {"fwd": r4["ws_fwd"], "bwd": r4["ws_bwd"]},
+            "peak_intermediate": r4["peak_intermediate"], "pcie_inclusive": True}
     if args.h2d_probe and T > 0:
         # host-to-device rate of one trunk's K and V (the per-trunk copy)
         hb = torch.empty(2 * T * Hkv * D, dtype=torch.bfloat16, pin_memory=True)

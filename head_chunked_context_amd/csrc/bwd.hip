@@ -130,14 +130,19 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
     const int kvl = (p.h0 + hl) / p.group - p.kv_base;
 
     // the workgroup's 128 keys of K (waves 0-3) and V (waves 4-7) go to LDS
-    // (rows past nk repeat the last key; their P is masked to zero)
+    // (rows past nk repeat the last key; their P is masked to zero).  When
+    // the tile holds 64 keys or fewer, every row of the second half repeats
+    // key nk - 1, so no lane reads past the last key.
     if (j0 < p.nk) {
         const int64_t nv = p.nk - j0;
         const int64_t rs = rh == 0 ? p.k_rs : p.v_rs;
         const uint16_t* src = rh == 0 ? p.k + (int64_t)kvl * p.k_hs + j0 * p.k_rs
                                       : p.v + (int64_t)kvl * p.v_hs + j0 * p.v_rs;
         direct_tile64<HD>(skv[rh], src, rs, nv, kw, lane);
-        direct_tile64<HD>(skv[rh] + TILE, src + 64 * rs, rs, nv > 64 ? nv - 64 : 1, kw, lane);
+        if (nv > 64)
+            direct_tile64<HD>(skv[rh] + TILE, src + 64 * rs, rs, nv - 64, kw, lane);
+        else
+            direct_tile64<HD>(skv[rh] + TILE, src + (nv - 1) * rs, rs, 1, kw, lane);
     }
     f32x16 dk[NDB], dv[NDB];
 #pragma unroll

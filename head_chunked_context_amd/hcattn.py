@@ -91,8 +91,45 @@ def _dims(q, k):
 
 
 def _bf16(name, t):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
     if t.dtype != torch.bfloat16 or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
+
+
+def _validate(specs, kv_names):
+    """Check every tensor the call hands to the C ABI, which sees only
+    pointers: specs are (name, tensor or None, shape, dtype); None (an output
+    the binding allocates itself) is skipped.  Shapes, dtypes and contiguity
+    come first; then placement: the first tensor (q) and every tensor not in
+    kv_names on one GPU, and those in kv_names (k, v, dk, dv) all on that GPU
+    or all in host memory (pinned; the trunked path streams them).  Returns
+    (q's device, the k/v device)."""
+    specs = [x for x in specs if x[1] is not None]
+    for name, t, shape, dtype in specs:
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch tensor")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    dev = specs[0][1].device
+    if dev.type != "cuda":
+        raise ValueError(f"{specs[0][0]} must be on a GPU (is on {dev})")
+    kvdev = None
+    for name, t, _, _ in specs:
+        if name in kv_names:
+            if kvdev is None:
+                kvdev = t.device
+            if t.device != kvdev:
+                raise ValueError(f"{name} is on {t.device}, k on {kvdev}")
+            if t.device != dev and t.device.type != "cpu":
+                raise ValueError(f"{name} is on {t.device}, q on {dev}")
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    return dev, kvdev
 
 
 def fwd_workspace_bytes(S, Hq, Hkv, D, causal=True, head_chunk=0, kv_trunk=0) -> int:
@@ -129,6 +166,9 @@ def _stream(device) -> int:
 def _workspace(nbytes, device, workspace):
     if workspace is None:
         return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != device or \
+            not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
     if workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, "
                          f"needs {nbytes}")
@@ -141,10 +181,14 @@ def attn_fwd(q, k, v, *, head_chunk: int = 0, kv_trunk: int = 0, causal: bool = 
     bf16 on the GPU or, with kv_trunk, in pinned host memory.  Returns
     (o [S,Hq,D] bf16, lse [Hq,S] fp32); with_lse=False (forward-only use)
     keeps no LSE and returns (o, None)."""
-    for n, t in (("q", q), ("k", k), ("v", v)):
+    for n, t in (("q", q), ("k", k)):
         _bf16(n, t)
     S, Hq, Hkv, D = _dims(q, k)
-    dev = q.device
+    bf = torch.bfloat16
+    dev, _ = _validate([("q", q, q.shape, bf), ("k", k, k.shape, bf), ("v", v, k.shape, bf),
+                        ("out", out, q.shape, bf),
+                        ("lse", lse if with_lse else None, (Hq, S), torch.float32)],
+                       ("k", "v"))
     o = torch.empty_like(q) if out is None else out
     l = None
     if with_lse:
@@ -163,17 +207,21 @@ def attn_bwd(q, k, v, o, dout, lse, *, head_chunk: int = 0, kv_trunk: int = 0,
              causal: bool = True, dq=None, dk=None, dv=None, workspace=None):
     """Backward of attn_fwd.  Returns (dq, dk, dv) in bf16; dk/dv are placed
     where k lives (device, or pinned host memory)."""
-    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+    for n, t in (("q", q), ("k", k)):
         _bf16(n, t)
     S, Hq, Hkv, D = _dims(q, k)
-    dev = q.device
+    bf = torch.bfloat16
+    dev, kvdev = _validate([("q", q, q.shape, bf), ("k", k, k.shape, bf), ("v", v, k.shape, bf),
+                            ("o", o, q.shape, bf), ("dout", dout, q.shape, bf),
+                            ("lse", lse, (Hq, S), torch.float32), ("dq", dq, q.shape, bf),
+                            ("dk", dk, k.shape, bf), ("dv", dv, k.shape, bf)],
+                           ("k", "v", "dk", "dv"))
     dq = torch.empty_like(q) if dq is None else dq
+    pin = kvdev.type == "cpu"
     if dk is None:
-        dk = torch.empty(k.shape, dtype=k.dtype, device=k.device,
-                         pin_memory=(k.device.type == "cpu"))
+        dk = torch.empty(k.shape, dtype=k.dtype, device=kvdev, pin_memory=pin)
     if dv is None:
-        dv = torch.empty(v.shape, dtype=v.dtype, device=v.device,
-                         pin_memory=(v.device.type == "cpu"))
+        dv = torch.empty(k.shape, dtype=k.dtype, device=kvdev, pin_memory=pin)
     nb = bwd_workspace_bytes(S, Hq, Hkv, D, causal, head_chunk, kv_trunk)
     ws = _workspace(nb, dev, workspace)
     rc = lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),

@@ -11,11 +11,16 @@ DEV = "cuda"
 TOL = 2e-2       # max-abs, O / dQ / dK / dV (bf16 in, fp32 accumulate)
 TOL_LSE = 1e-3   # max-abs, LSE
 
-# O, dQ, dK and dV are returned in bf16, so even the exact result rounded to
-# bf16 is off by up to half a bf16 ulp of its own value (2^-8 relative at
-# worst): gradients of GQA groups reach |x| ~ 8-30, where that alone exceeds
-# 2e-2.  The bar is therefore applied to the error beyond the output's own
-# representation:  |gpu - oracle| - half_ulp_bf16(oracle) <= TOL.
+# The bar: max-abs error 2e-2 against the fp64 oracle, applied element by
+# element.  O, dQ, dK and dV are returned in bf16, so even the exact result
+# rounded to bf16 is off by up to half a bf16 ulp of its own value (2^-8
+# relative at worst): gradients of GQA groups reach |x| ~ 8-30, where that
+# alone exceeds 2e-2.  Where the exact value is below BIG in magnitude (half
+# a bf16 ulp is at most 2^-7 there) the plain max-abs bar holds; above it the
+# bar applies to the error beyond the output's own representation:
+#     |ref| <  BIG:  |gpu - ref| <= TOL
+#     |ref| >= BIG:  |gpu - ref| - half_ulp_bf16(ref) <= TOL
+BIG = 4.0
 
 
 def inputs_cpu(S, Hq, Hkv, D, seed, q_scale=1.0):
@@ -59,18 +64,25 @@ def half_ulp_bf16(x):
     return np.ldexp(1.0, np.floor(np.log2(a)).astype(np.int64) - 8)
 
 
-def bf16_excess(gpu, ref):
-    """max over elements of |gpu - ref| beyond half a bf16 ulp of ref."""
+def gated_error(gpu, ref):
+    """The gated error: max over elements of |gpu - ref|, less half a bf16
+    ulp of ref where |ref| >= BIG (see above)."""
     ref = np.asarray(ref, dtype=np.float64)
-    return float(np.max(np.abs(np.asarray(gpu, dtype=np.float64) - ref) - half_ulp_bf16(ref)))
+    err = np.abs(np.asarray(gpu, dtype=np.float64) - ref)
+    big = np.abs(ref) >= BIG
+    err = np.where(big, err - half_ulp_bf16(ref), err)
+    return float(np.max(err)) if err.size else 0.0
 
 
 def check_fwd(inp, o, lse, causal=True, tol=TOL):
+    """O (and LSE unless it is None: the forward-only mode keeps none)
+    against the oracle."""
     ro, rl = orc.attn_fwd(inp["q"], inp["k"], inp["v"], causal)
-    eo, el = bf16_excess(f64(o), ro), maxabs(f64(lse), rl)
-    print(f"  O max-abs {maxabs(f64(o), ro):.3e} (beyond bf16 rounding {eo:.3e}), "
+    eo = gated_error(f64(o), ro)
+    el = maxabs(f64(lse), rl) if lse is not None else 0.0
+    print(f"  O max-abs {maxabs(f64(o), ro):.3e} (gated {eo:.3e}), "
           f"LSE max-abs {el:.3e}", flush=True)
-    assert eo <= tol, f"O error beyond bf16 rounding {eo}"
+    assert eo <= tol, f"O gated error {eo}"
     assert el <= TOL_LSE, f"LSE max-abs error {el}"
     return eo, el
 
@@ -79,9 +91,9 @@ def check_bwd(inp, g, causal=True, rel=False):
     ref = orc.attn_bwd(inp["q"], inp["k"], inp["v"], inp["dout"], causal)
     errs = {}
     for name, t in zip(("dq", "dk", "dv"), g):
-        errs[name] = bf16_excess(f64(t), ref[name])
+        errs[name] = gated_error(f64(t), ref[name])
         bound = TOL * max(1.0, float(np.max(np.abs(ref[name])))) if rel else TOL
-        print(f"  {name} max-abs {maxabs(f64(t), ref[name]):.3e} (beyond bf16 rounding "
+        print(f"  {name} max-abs {maxabs(f64(t), ref[name]):.3e} (gated "
               f"{errs[name]:.3e}, bound {bound:.2e})", flush=True)
-        assert errs[name] <= bound, f"{name} error beyond bf16 rounding {errs[name]}"
+        assert errs[name] <= bound, f"{name} gated error {errs[name]}"
     return errs

@@ -240,16 +240,21 @@ def test_trunk_merge_schedule_matches_oracle(kv_host):
     assert maxabs(f64(lt), f64(lse)) <= TOL_LSE
 
 
-@pytest.mark.parametrize("trunk", [0, 256])
-def test_forward_without_lse(trunk):
+@pytest.mark.parametrize("trunk,kv_host", [(0, False), (256, False), (256, True)])
+def test_forward_without_lse(trunk, kv_host):
+    # forward-only (prefill) use: no LSE is kept; O must match the oracle and
+    # the output of the call that keeps the LSE, bit for bit
     from head_chunked_context_amd import attn_fwd
     S, Hq, Hkv, D = 777, 4, 2, 128
     inp = inputs_cpu(S, Hq, Hkv, D, 36)
-    d = to_dev(inp)
-    o, lse = attn_fwd(d["q"], d["k"], d["v"], head_chunk=2, kv_trunk=trunk)
+    d = to_dev(inp, kv_host=kv_host)
+    print(f"forward without LSE S={S} T={trunk} kv_host={kv_host}", flush=True)
     o2, none = attn_fwd(d["q"], d["k"], d["v"], head_chunk=2, kv_trunk=trunk, with_lse=False)
     torch.cuda.synchronize()
     assert none is None
+    check_fwd(inp, o2, None)
+    o, lse = attn_fwd(d["q"], d["k"], d["v"], head_chunk=2, kv_trunk=trunk)
+    torch.cuda.synchronize()
     assert torch.equal(o, o2)
 
 
@@ -285,12 +290,19 @@ def test_single_stream_equals_overlapped():
 
 def test_errors_are_reported_without_work():
     from head_chunked_context_amd import HcAttnError, attn_fwd
+    from head_chunked_context_amd.hcattn import lib
     inp = inputs_cpu(64, 2, 1, 128, 34)
     d = to_dev(inp)
     ws = torch.empty(1 << 24, dtype=torch.uint8, device=DEV)
-    with pytest.raises(HcAttnError) as e:
-        attn_fwd(inp["q"], d["k"], d["v"], workspace=ws)  # q in pageable host memory
-    assert e.value.code == -4
+    with pytest.raises(ValueError):
+        attn_fwd(inp["q"], d["k"], d["v"], workspace=ws)  # q in host memory: the binding refuses
+    # the library's own pointer check, called through the C ABI directly: q in
+    # pageable host memory is refused before any work
+    o = torch.empty_like(d["q"])
+    rc = lib().attn_fwd(inp["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(), o.data_ptr(),
+                        None, 64, 2, 1, 128, 1, 0, 0, ws.data_ptr(), ws.numel(),
+                        torch.cuda.current_stream().cuda_stream)
+    assert rc == -4
     with pytest.raises((HcAttnError, ValueError)):
         attn_fwd(d["q"], d["k"], d["v"], workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
     with pytest.raises(HcAttnError) as e:
