@@ -1,0 +1,551 @@
+// Host-only check of every global-memory access the library's kernels and
+// copies make, built with the address and undefined-behaviour sanitizers by
+// tests/test_extent_check.py.
+//
+// The library's real host pipeline (hcattn.cpp: the C ABI, planner, chunk
+// and trunk loops, ring and staging slots) is linked against a fake HIP
+// runtime defined here.  "Device" buffers are host allocations registered
+// with the fake runtime (pinned host ones likewise, pageable ones not), so
+// attn_fwd / attn_bwd run their argument and pointer checks unchanged.
+// Instead of launching kernels, the launch_* entry points below replay each
+// kernel's addressing: a host replica of the index arithmetic of every load
+// and store in fwd.hip, bwd.hip and aux.hip (per workgroup, wave and lane,
+// including the clamping of ragged tiles), and hipMemcpy2DAsync checks the
+// rows it copies.  Each access must lie inside one checked region: a user
+// tensor of exactly the size the ABI states, or one workspace region of the
+// size the planner carves (so a read that runs from one region into the next,
+// or past the workspace, is reported even though it stays in mapped memory).
+//
+// With --plant-dkdv-overread the dK/dV key-tile load is replayed as it once
+// was written (the second 64-key half of a short last tile loaded from key
+// j0 + 64), which must be reported: evidence that the check sees reads.
+#include <hip/hip_runtime_api.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/hcattn.h"
+#include "kernels.h"
+#include "plan.h"
+
+static bool g_plant = false;
+static long g_fails = 0, g_checks = 0;
+static std::string g_case;
+
+// ------------------------------------------------------------ buffer model
+
+struct Region {
+    uintptr_t lo, hi;
+    std::string name;
+};
+static std::vector<Region> g_regions;  // checked regions (user tensors, workspace regions)
+
+struct Alloc {
+    uintptr_t lo, hi;
+    bool host;  // pinned host (device otherwise)
+};
+static std::vector<Alloc> g_allocs;  // what hipPointerGetAttributes knows
+
+static void fail_msg(const char* fmt, const char* what, uintptr_t a, size_t n) {
+    if (++g_fails <= 20) {
+        fprintf(stderr, "FAIL [%s] %s: ", g_case.c_str(), what);
+        fprintf(stderr, fmt, (unsigned long long)a, (unsigned long long)n);
+        fprintf(stderr, "\n");
+    }
+}
+
+// [p, p + bytes) must lie inside one region
+static void touch(const void* p, int64_t bytes, const char* what) {
+    ++g_checks;
+    const uintptr_t a = (uintptr_t)p;
+    for (const Region& r : g_regions) {
+        if (a >= r.lo && a < r.hi) {
+            if (bytes < 0 || a + (uintptr_t)bytes > r.hi)
+                fail_msg("access at %#llx of %llu bytes runs past its region", what, a,
+                         (size_t)bytes);
+            return;
+        }
+    }
+    fail_msg("access at %#llx (%llu bytes) is in no region", what, a, (size_t)bytes);
+}
+
+// element offset arithmetic on addresses (the replicas may compute addresses
+// outside every buffer; that is what they look for)
+template <class T>
+static const void* at(const T* base, int64_t elems) {
+    return (const void*)((uintptr_t)base + (uintptr_t)(elems * (int64_t)sizeof(T)));
+}
+
+// ------------------------------------------------------------ fake HIP
+
+static uintptr_t g_handle = 0x1000;
+
+extern "C" {
+hipError_t hipGetDevice(int* d) { *d = 0; return hipSuccess; }
+hipError_t hipStreamCreateWithFlags(hipStream_t* s, unsigned int) {
+    *s = reinterpret_cast<hipStream_t>(g_handle += 16);
+    return hipSuccess;
+}
+hipError_t hipStreamDestroy(hipStream_t) { return hipSuccess; }
+hipError_t hipEventCreateWithFlags(hipEvent_t* e, unsigned) {
+    *e = reinterpret_cast<hipEvent_t>(g_handle += 16);
+    return hipSuccess;
+}
+hipError_t hipEventCreate(hipEvent_t* e) { return hipEventCreateWithFlags(e, 0); }
+hipError_t hipEventDestroy(hipEvent_t) { return hipSuccess; }
+hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
+hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t, unsigned int) { return hipSuccess; }
+hipError_t hipEventSynchronize(hipEvent_t) { return hipSuccess; }
+hipError_t hipEventElapsedTime(float* ms, hipEvent_t, hipEvent_t) { *ms = 0.f; return hipSuccess; }
+hipError_t hipGetLastError(void) { return hipSuccess; }
+const char* hipGetErrorString(hipError_t) { return "(fake runtime)"; }
+hipError_t hipPointerGetAttributes(hipPointerAttribute_t* a, const void* p) {
+    const uintptr_t x = (uintptr_t)p;
+    for (const Alloc& al : g_allocs) {
+        if (x >= al.lo && x < al.hi) {
+            memset(a, 0, sizeof(*a));
+            a->type = al.host ? hipMemoryTypeHost : hipMemoryTypeDevice;
+            return hipSuccess;
+        }
+    }
+    return hipErrorInvalidValue;
+}
+hipError_t hipMemcpy2DAsync(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width,
+                            size_t height, hipMemcpyKind, hipStream_t) {
+    for (size_t r = 0; r < height; ++r) {
+        touch((const void*)((uintptr_t)src + r * spitch), (int64_t)width, "copy source row");
+        touch((const void*)((uintptr_t)dst + r * dpitch), (int64_t)width, "copy destination row");
+    }
+    return hipSuccess;
+}
+}  // extern "C"
+
+// ------------------------------------------------------------ kernel replicas
+
+namespace hc {
+
+// Rows a 64-row tile load reads from `base` (stride rs elements): rows at or
+// past nvalid re-read row nvalid - 1 (TileDma64 / direct_tile64).
+static void tile64(const uint16_t* base, int64_t rs, int64_t nvalid, int HD, const char* what) {
+    if (nvalid < 1) {
+        fail_msg("tile load with nvalid < 1 (base %#llx, %llu)", what, (uintptr_t)base, 0);
+        return;
+    }
+    const int64_t n = nvalid >= 64 ? 64 : nvalid;
+    for (int64_t r = 0; r < n; ++r) touch(at(base, r * rs), (int64_t)HD * 2, what);
+}
+// 64 consecutive fp32 (direct_vec64): entries past nvalid repeat nvalid - 1
+static void vec64(const float* src, int64_t nvalid, const char* what) {
+    if (nvalid < 1) {
+        fail_msg("vector load with nvalid < 1 (base %#llx, %llu)", what, (uintptr_t)src, 0);
+        return;
+    }
+    touch(src, (nvalid >= 64 ? 64 : nvalid) * 4, what);
+}
+
+hipError_t launch_pack(const PackParams& p, hipStream_t) {
+    if (p.nh <= 0 || p.rows <= 0) return hipSuccess;
+    for (int64_t h = 0; h < p.nh; ++h)
+        for (int64_t row = 0; row < p.rows; ++row) {
+            touch(at(p.src, h * p.s_hs + row * p.s_rs), (int64_t)p.D * 2, "pack read");
+            touch(at(p.dst, h * p.d_hs + row * p.d_rs), (int64_t)p.D * 2, "pack write");
+        }
+    return hipSuccess;
+}
+
+hipError_t launch_merge(const MergeParams& p, hipStream_t) {
+    if (p.nh <= 0 || p.rows <= 0) return hipSuccess;
+    for (int64_t h = 0; h < p.nh; ++h)
+        for (int64_t row = 0; row < p.rows; ++row) {
+            const int64_t hr = h * p.rows + row;
+            touch(p.l_r + hr, 4, "merge l_r");
+            touch(p.l_t + hr, 4, "merge l_t");
+            touch(at(p.o_r, hr * p.D), (int64_t)p.D * 4, "merge o_r");
+            touch(at(p.o_t, hr * p.D), (int64_t)p.D * 4, "merge o_t");
+            if (p.final_out) {
+                touch(at(p.out, h * p.out_hs + row * p.out_rs), (int64_t)p.D * 2, "merge out");
+                if (p.lse_out) touch(p.lse_out + h * p.lse_hs + row, 4, "merge lse_out");
+            }
+        }
+    return hipSuccess;
+}
+
+hipError_t launch_prep(const PrepParams& p, hipStream_t) {
+    if (p.nh <= 0 || p.rows <= 0) return hipSuccess;
+    for (int64_t h = 0; h < p.nh; ++h)
+        for (int64_t row = 0; row < p.rows; ++row) {
+            touch(at(p.o, h * p.o_hs + row * p.o_rs), (int64_t)p.D * 2, "prep o");
+            touch(at(p.dO, h * p.do_hs + row * p.do_rs), (int64_t)p.D * 2, "prep dO");
+            touch(at(p.dO_c, h * p.c_hs + row * p.c_rs), (int64_t)p.D * 2, "prep dO_c");
+            touch(p.ndelta + h * p.ndelta_hs + row, 4, "prep ndelta");
+            touch(p.nlse2 + h * p.nlse2_hs + row, 4, "prep nlse2");
+            touch(p.lse + h * p.lse_hs + row, 4, "prep lse");
+        }
+    return hipSuccess;
+}
+
+// fwd_kernel<HD, NW> as launched by launch_fwd
+hipError_t launch_fwd(const FwdParams& p, int HD, hipStream_t) {
+    if (p.nq <= 0 || p.nh <= 0) return hipSuccess;
+    const bool wide = (p.nq + 255) / 256 * p.nh >= kWideMinBlocks;
+    const int NW = wide ? 8 : 4, WQ = 32, BM = NW * WQ, BN = 64;
+    const int64_t nqt = (p.nq + BM - 1) / BM;
+    const int64_t blocks = nqt * p.nh;
+    for (int64_t b = 0; b < blocks; ++b) {
+        const int head = (int)(b % p.nh);
+        const int64_t qt = nqt - 1 - b / p.nh;
+        const int64_t q0 = qt * BM;
+        const int kvl = (p.h0 + head) / p.group - p.kv_base;
+        const uint16_t* qh = p.q + (int64_t)head * p.q_hs;
+        const uint16_t* kh = p.k + (int64_t)kvl * p.k_hs;
+        const uint16_t* vh = p.v + (int64_t)kvl * p.v_hs;
+        const int64_t wg_last = (q0 + BM - 1 < p.nq - 1) ? q0 + BM - 1 : p.nq - 1;
+        int64_t kend = p.nk;
+        if (p.causal) {
+            const int64_t a = p.q_pos0 + wg_last - p.k_pos0 + 1;
+            kend = a < kend ? a : kend;
+        }
+        const int ntiles = kend > 0 ? (int)((kend + BN - 1) / BN) : 0;
+        for (int t = 0; t < ntiles; ++t) {
+            const int64_t nb = (int64_t)t * BN;
+            tile64(kh + nb * p.k_rs, p.k_rs, p.nk - nb, HD, "fwd K tile");
+            tile64(vh + nb * p.v_rs, p.v_rs, p.nk - nb, HD, "fwd V tile");
+        }
+        for (int w = 0; w < NW; ++w) {
+            const int64_t wq0 = q0 + w * WQ;
+            const bool wave_live = wq0 < p.nq;
+            for (int l = 0; l < 32; ++l) {
+                const int64_t myq = wq0 + l;
+                if (myq >= p.nq) continue;
+                touch(at(qh, myq * p.q_rs), HD * 2, "fwd Q row");
+                const int64_t sr = (int64_t)head * p.st_hs + myq;
+                if (p.carry_in || p.carry_out) {
+                    touch(p.st_m + sr, 4, "fwd carried m");
+                    touch(p.st_l + 2 * sr, 8, "fwd carried row sums");
+                    touch(at(p.st_o, (int64_t)head * p.st_o_hs + myq * HD), HD * 4, "fwd carried O");
+                }
+                if (!wave_live || p.carry_out) continue;
+                if (p.mode == kFwdFinal) {
+                    touch(at((const uint16_t*)p.o, (int64_t)head * p.o_hs + myq * p.o_rs), HD * 2,
+                          "fwd O (bf16)");
+                    if (p.lse) touch(p.lse + (int64_t)head * p.lse_hs + myq, 4, "fwd LSE");
+                } else {
+                    touch(at((const float*)p.o, (int64_t)head * p.o_hs + myq * p.o_rs), HD * 4,
+                          "fwd O partial (fp32)");
+                    touch(p.lse + (int64_t)head * p.lse_hs + myq, 4, "fwd LSE partial");
+                }
+            }
+        }
+    }
+    return hipSuccess;
+}
+
+// dkdv_kernel<HD, RUNS> as launched by launch_dkdv
+hipError_t launch_dkdv(const DkdvParams& p, int HD, hipStream_t) {
+    if (p.nk <= 0 || p.nh <= 0) return hipSuccess;
+    const int BQ = 64, BNK = 128;
+    const int64_t blocks = (p.nk + BNK - 1) / BNK * p.nh;
+    const bool runs = p.nh % 4 != 0;
+    std::vector<char> seen((size_t)blocks, 0);
+    for (int64_t b = 0; b < blocks; ++b) {
+        int hl;
+        int64_t kt;
+        if (runs) {
+            const unsigned RUN = 32, WIN = 8 * RUN;
+            unsigned item = (unsigned)b;
+            const unsigned w = item / WIN;
+            if ((w + 1) * WIN <= (unsigned)blocks) {
+                const unsigned x = item % 8, o = (item / 8) % RUN;
+                item = w * WIN + ((w & 1) ? 7 - x : x) * RUN + o;
+            }
+            if ((int64_t)item >= blocks || seen[item]) {
+                fail_msg("work item %#llx repeated or out of range (%llu)", "dkdv order", item,
+                         (size_t)blocks);
+                continue;
+            }
+            seen[item] = 1;
+            hl = (int)(item % (unsigned)p.nh);
+            kt = (int64_t)(item / (unsigned)p.nh);
+        } else {
+            hl = (int)(b % p.nh);
+            kt = b / p.nh;
+        }
+        const int64_t j0 = kt * BNK;
+        const int kvl = (p.h0 + hl) / p.group - p.kv_base;
+        if (j0 < p.nk) {
+            const int64_t nv = p.nk - j0;
+            for (int rh = 0; rh < 2; ++rh) {
+                const int64_t rs = rh == 0 ? p.k_rs : p.v_rs;
+                const uint16_t* src = rh == 0 ? p.k + (int64_t)kvl * p.k_hs + j0 * p.k_rs
+                                              : p.v + (int64_t)kvl * p.v_hs + j0 * p.v_rs;
+                const char* what = rh == 0 ? "dkdv K tile" : "dkdv V tile";
+                tile64(src, rs, nv, HD, what);
+                if (g_plant)
+                    tile64(src + 64 * rs, rs, nv > 64 ? nv - 64 : 1, HD, what);
+                else if (nv > 64)
+                    tile64(src + 64 * rs, rs, nv - 64, HD, what);
+                else
+                    tile64(src + (nv - 1) * rs, rs, 1, HD, what);
+            }
+        }
+        const int64_t nqt = (p.nq + BQ - 1) / BQ;
+        int64_t qt0 = 0;
+        if (p.causal) {
+            const int64_t first = p.k_pos0 + j0;
+            qt0 = first >= p.nq ? nqt : first / BQ;
+        }
+        const int64_t nsteps = j0 < p.nk ? nqt - qt0 : 0;
+        const uint16_t* qh = p.q + (int64_t)hl * p.q_hs;
+        const uint16_t* oh = p.dO + (int64_t)hl * p.do_hs;
+        const float* lseh = p.nlse2 + (int64_t)hl * p.nlse2_hs;
+        const float* delh = p.ndelta + (int64_t)hl * p.ndelta_hs;
+        for (int64_t n = 0; n < nsteps; ++n) {
+            const int64_t i0 = (qt0 + n) * BQ;
+            tile64(qh + i0 * p.q_rs, p.q_rs, p.nq - i0, HD, "dkdv Q tile");
+            tile64(oh + i0 * p.do_rs, p.do_rs, p.nq - i0, HD, "dkdv dO tile");
+            vec64(lseh + i0, p.nq - i0, "dkdv -LSE log2e");
+            vec64(delh + i0, p.nq - i0, "dkdv -Delta");
+        }
+        for (int kw = 0; kw < 4; ++kw)
+            for (int l = 0; l < 32; ++l) {
+                const int64_t myk = j0 + kw * 32 + l;
+                if (myk >= p.nk) continue;
+                touch(at(p.part_k, ((int64_t)hl * p.nk + myk) * HD), HD * 4, "dkdv dK partial");
+                touch(at(p.part_v, ((int64_t)hl * p.nk + myk) * HD), HD * 4, "dkdv dV partial");
+            }
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_dkdv_reduce(const DkdvReduceParams& p, hipStream_t) {
+    if (p.nk <= 0 || p.nkv <= 0) return hipSuccess;
+    for (int kvl = 0; kvl < p.nkv; ++kvl) {
+        const int kvg = p.kv_base + kvl;
+        int hb = kvg * p.group - p.h0, he = (kvg + 1) * p.group - p.h0;
+        hb = hb < 0 ? 0 : hb;
+        he = he > p.nh ? p.nh : he;
+        for (int64_t key = 0; key < p.nk; ++key) {
+            if (kvl == p.carry_kv_in) {
+                touch(at(p.carry_in_k, key * p.D), p.D * 4, "reduce carry in dK");
+                touch(at(p.carry_in_v, key * p.D), p.D * 4, "reduce carry in dV");
+            }
+            for (int h = hb; h < he; ++h) {
+                touch(at(p.part_k, ((int64_t)h * p.nk + key) * p.D), p.D * 4, "reduce dK partial");
+                touch(at(p.part_v, ((int64_t)h * p.nk + key) * p.D), p.D * 4, "reduce dV partial");
+            }
+            if (kvl == p.carry_kv_out) {
+                touch(at(p.carry_out_k, key * p.D), p.D * 4, "reduce carry out dK");
+                touch(at(p.carry_out_v, key * p.D), p.D * 4, "reduce carry out dV");
+            } else {
+                touch(at(p.dk, (int64_t)kvl * p.dk_hs + key * p.dk_rs), p.D * 2, "reduce dK out");
+                touch(at(p.dv, (int64_t)kvl * p.dk_hs + key * p.dk_rs), p.D * 2, "reduce dV out");
+            }
+        }
+    }
+    return hipSuccess;
+}
+
+// dq_kernel<HD, NW> as launched by launch_dq
+hipError_t launch_dq(const DqParams& p, int HD, hipStream_t) {
+    if (p.nq <= p.q_begin || p.nh <= 0) return hipSuccess;
+    const bool wide = ((p.nq + 255) / 256 - p.q_begin / 256) * p.nh >= kWideMinBlocks;
+    const int bm = wide ? 256 : 128;
+    if (p.q_begin % bm != 0) return hipErrorInvalidValue;
+    const int NW = wide ? 8 : 4, WQ = 32, BM = NW * WQ, BN = 64;
+    const int64_t qtb = p.q_begin / BM;
+    const int64_t nqt = (p.nq + BM - 1) / BM - qtb;
+    const int64_t blocks = nqt * p.nh;
+    for (int64_t b = 0; b < blocks; ++b) {
+        const int head = (int)(b % p.nh);
+        const int64_t qt = qtb + nqt - 1 - b / p.nh;
+        const int64_t q0 = qt * BM;
+        const int kvl = (p.h0 + head) / p.group - p.kv_base;
+        const uint16_t* kh = p.k + (int64_t)kvl * p.k_hs;
+        const uint16_t* vh = p.v + (int64_t)kvl * p.v_hs;
+        const int64_t wg_last = (q0 + BM - 1 < p.nq - 1) ? q0 + BM - 1 : p.nq - 1;
+        int64_t kend = p.nk;
+        if (p.causal) {
+            const int64_t a = wg_last - p.k_pos0 + 1;
+            kend = a < kend ? a : kend;
+        }
+        const int ntiles = kend > 0 ? (int)((kend + BN - 1) / BN) : 0;
+        for (int t = 0; t < ntiles; ++t) {
+            const int64_t nb = (int64_t)t * BN;
+            tile64(kh + nb * p.k_rs, p.k_rs, p.nk - nb, HD, "dq K tile");
+            tile64(vh + nb * p.v_rs, p.v_rs, p.nk - nb, HD, "dq V tile");
+        }
+        for (int w = 0; w < NW; ++w)
+            for (int l = 0; l < 32; ++l) {
+                const int64_t myq = q0 + w * WQ + l;
+                if (myq >= p.nq) continue;
+                touch(at(p.q, (int64_t)head * p.q_hs + myq * p.q_rs), HD * 2, "dq Q row");
+                touch(at(p.dO, (int64_t)head * p.do_hs + myq * p.do_rs), HD * 2, "dq dO row");
+                touch(p.nlse2 + (int64_t)head * p.nlse2_hs + myq, 4, "dq -LSE log2e");
+                touch(p.ndelta + (int64_t)head * p.ndelta_hs + myq, 4, "dq -Delta");
+                if (p.acc_in)
+                    touch(at(p.acc_in, (int64_t)head * p.ain_hs + myq * p.ain_rs), HD * 4,
+                          "dq fp32 carry in");
+                if (myq < p.final_before || p.acc_out == nullptr)
+                    touch(at(p.dq, (int64_t)head * p.dq_hs + myq * p.dq_rs), HD * 2, "dq out");
+                else
+                    touch(at(p.acc_out, (int64_t)head * p.aout_hs + myq * p.aout_rs), HD * 4,
+                          "dq fp32 carry out");
+            }
+    }
+    return hipSuccess;
+}
+
+}  // namespace hc
+
+// ------------------------------------------------------------ driver
+
+struct Buffer {
+    std::vector<char> mem;
+    void* p() { return mem.data(); }
+};
+
+static void add_region(const void* p, size_t bytes, const std::string& name) {
+    g_regions.push_back({(uintptr_t)p, (uintptr_t)p + bytes, name});
+}
+
+// the workspace regions as the planner carves them (sizes restated here from
+// the layout each kernel reads and writes)
+static void add_workspace(char* ws, const hc::Plan& p) {
+    const size_t E = (size_t)p.S * p.D * 2, Et = (size_t)p.T * p.D * 2;
+    auto R = [&](size_t off, size_t bytes, const char* n) { add_region(ws + off, bytes, n); };
+    if (!p.bwd) {
+        if (!p.trunked) {
+            R(p.q_c, p.hc * E, "ws Q_c");
+            R(p.k_c, p.kvc * E, "ws K_c");
+            R(p.v_c, p.kvc * E, "ws V_c");
+        } else {
+            R(p.q_c, p.hc * Et, "ws Q_m");
+            R(p.o_run, p.hc * Et * 2, "ws O_run");
+            R(p.o_t, p.hc * Et * 2, "ws O_t");
+            R(p.l_run, (size_t)p.hc * p.T * 4, "ws L_run");
+            R(p.l_t, (size_t)p.hc * p.T * 4, "ws L_t");
+            R(p.st_l, (size_t)p.hc * p.T * 8, "ws row sums");
+            for (int s = 0; s < 2; ++s) {
+                R(p.ring_k[s], p.kvc * Et, "ws ring K");
+                R(p.ring_v[s], p.kvc * Et, "ws ring V");
+            }
+        }
+    } else {
+        R(p.q_c, p.hc * E, "ws Q_c");
+        R(p.do_c, p.hc * E, "ws dO_c");
+        R(p.delta_c, (size_t)p.hc * p.S * 4, "ws -Delta");
+        R(p.lse2_c, (size_t)p.hc * p.S * 4, "ws -LSE log2e");
+        const size_t rows = p.trunked ? Et : E;
+        R(p.part_k, p.hc * rows * 2, "ws dK partials");
+        R(p.part_v, p.hc * rows * 2, "ws dV partials");
+        if (!p.trunked) {
+            R(p.k_c, p.kvc * E, "ws K_c");
+            R(p.v_c, p.kvc * E, "ws V_c");
+        } else {
+            R(p.dq_acc, p.hc * E * 2, "ws dQ carry");
+            for (int s = 0; s < 2; ++s) {
+                R(p.ring_k[s], p.kvc * Et, "ws ring K");
+                R(p.ring_v[s], p.kvc * Et, "ws ring V");
+                R(p.stage_k[s], p.kvc * Et, "ws staging dK");
+                R(p.stage_v[s], p.kvc * Et, "ws staging dV");
+            }
+        }
+        for (int s = 0; s < p.carry_slots; ++s) {
+            R(p.carry_k[s], E * 2, "ws dK carry");
+            R(p.carry_v[s], E * 2, "ws dV carry");
+        }
+    }
+}
+
+// one attn_fwd + attn_bwd call pair on exactly sized buffers
+static void run_case(int64_t S, int Hq, int Hkv, int D, int causal, int hc, int64_t T, bool host) {
+    char name[160];
+    snprintf(name, sizeof name, "S=%lld Hq=%d Hkv=%d D=%d causal=%d hc=%d T=%lld host=%d",
+             (long long)S, Hq, Hkv, D, causal, hc, (long long)T, (int)host);
+    g_case = name;
+    const size_t qb = (size_t)S * Hq * D * 2, kb = (size_t)S * Hkv * D * 2, lb = (size_t)Hq * S * 4;
+    Buffer q, k, v, o, lse, dout, dq, dk, dv, wsf, wsb;
+    q.mem.resize(qb); o.mem.resize(qb); dout.mem.resize(qb); dq.mem.resize(qb);
+    k.mem.resize(kb); v.mem.resize(kb); dk.mem.resize(kb); dv.mem.resize(kb);
+    lse.mem.resize(lb);
+    const size_t nf = attn_fwd_workspace_bytes(S, Hq, Hkv, D, causal, hc, T);
+    const size_t nb = attn_bwd_workspace_bytes(S, Hq, Hkv, D, causal, hc, T);
+    if (nf == 0 || nb == 0) {
+        fail_msg("workspace query failed (%llu, %llu)", attn_last_error(), nf, nb);
+        return;
+    }
+    // 256-byte aligned workspaces of exactly the queried size
+    std::vector<char> fbuf(nf + 256), bbuf(nb + 256);
+    char* wf = fbuf.data() + (256 - (uintptr_t)fbuf.data() % 256) % 256;
+    char* wb = bbuf.data() + (256 - (uintptr_t)bbuf.data() % 256) % 256;
+    g_regions.clear();
+    g_allocs.clear();
+    auto reg = [&](Buffer& b, const char* n, bool is_host) {
+        add_region(b.p(), b.mem.size(), n);
+        g_allocs.push_back({(uintptr_t)b.p(), (uintptr_t)b.p() + b.mem.size(), is_host});
+    };
+    reg(q, "q", false); reg(o, "o", false); reg(dout, "dout", false); reg(dq, "dq", false);
+    reg(lse, "lse", false);
+    reg(k, "k", host); reg(v, "v", host); reg(dk, "dk", host); reg(dv, "dv", host);
+    g_allocs.push_back({(uintptr_t)wf, (uintptr_t)wf + nf, false});
+    hc::Plan pf, pb;
+    char msg[256];
+    hc::make_plan(false, S, Hq, Hkv, D, causal, hc, T, &pf, msg, sizeof msg);
+    const size_t keep = g_regions.size();
+    add_workspace(wf, pf);
+    int rc = attn_fwd(q.p(), k.p(), v.p(), o.p(), (float*)lse.p(), S, Hq, Hkv, D, causal, hc, T,
+                      wf, nf, nullptr);
+    if (rc != ATTN_OK) fail_msg("attn_fwd returned %llu (%llu)", attn_last_error(), (size_t)rc, 0);
+    g_regions.resize(keep);
+    g_allocs.pop_back();
+    g_allocs.push_back({(uintptr_t)wb, (uintptr_t)wb + nb, false});
+    hc::make_plan(true, S, Hq, Hkv, D, causal, hc, T, &pb, msg, sizeof msg);
+    add_workspace(wb, pb);
+    rc = attn_bwd(q.p(), k.p(), v.p(), o.p(), dout.p(), (const float*)lse.p(), dq.p(), dk.p(),
+                  dv.p(), S, Hq, Hkv, D, causal, hc, T, wb, nb, nullptr);
+    if (rc != ATTN_OK) fail_msg("attn_bwd returned %llu (%llu)", attn_last_error(), (size_t)rc, 0);
+}
+
+int main(int argc, char** argv) {
+    for (int i = 1; i < argc; ++i)
+        if (strcmp(argv[i], "--plant-dkdv-overread") == 0) g_plant = true;
+    // sequence lengths at and around tile edges (64-row tiles, 128-key dK/dV
+    // tiles, 128/256-row forward and dQ workgroups, 256-token trunks)
+    const int64_t Ss[] = {1, 2, 33, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257,
+                          300, 319, 320, 321, 383, 384, 385, 511, 512, 513, 600, 700, 777, 1100};
+    struct Heads { int Hq, Hkv; };
+    const Heads hs[] = {{1, 1}, {2, 1}, {4, 2}, {8, 2}, {8, 1}, {4, 4}, {6, 2}};
+    long cases = 0;
+    unsigned rng = 12345u;
+    auto pick = [&](int n) { rng = rng * 1103515245u + 12345u; return (int)((rng >> 16) % (unsigned)n); };
+    for (int64_t S : Ss)
+        for (const Heads& h : hs)
+            for (int D : {64, 128}) {
+                // every head_chunk for one causal setting, a sampled one otherwise
+                const int causal = pick(4) != 0;
+                for (int hc = 1; hc <= h.Hq; ++hc) {
+                    if (hc > 1 && hc < h.Hq && pick(2)) continue;
+                    int64_t T = 0;
+                    bool host = false;
+                    const int tsel = S > 256 ? pick(3) : 0;
+                    if (tsel && 256 * tsel < S) {  // a trunk at or past S is untrunked
+                        T = 256 * tsel;
+                        host = pick(2) != 0;
+                    }
+                    run_case(S, h.Hq, h.Hkv, D, causal, hc, T, host);
+                    ++cases;
+                }
+            }
+    // the workload shapes at a short length: 32/8 and 40/8 heads, one-group chunks
+    for (int64_t S : {1000, 1024}) {
+        run_case(S, 32, 8, 128, 1, 4, 0, false); ++cases;
+        run_case(S, 40, 8, 128, 1, 5, 256, true); ++cases;
+        run_case(S, 4, 1, 128, 1, 1, 512, false); ++cases;
+    }
+    printf("cases: %ld  accesses checked: %ld  failures: %ld\n", cases, g_checks, g_fails);
+    return g_fails == 0 ? 0 : 1;
+}
