@@ -711,6 +711,24 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     return r ? r : r2;
 }
 
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t S,
+                     int32_t Hq, int32_t Hkv, int32_t D, int32_t causal, int32_t head_chunk,
+                     int64_t kv_trunk, void* stream) {
+    g_err[0] = 0;
+    hc::Plan pl;
+    int r = plan_or_fail(false, S, Hq, Hkv, D, causal, head_chunk, kv_trunk, &pl);
+    if (r) return r;
+    if (pl.total > hc::kScratchBytes)
+        return fail(ATTN_EWORKSPACE,
+                    "these arguments need %zu bytes of workspace; the built-in one holds %zu "
+                    "(use a smaller head_chunk or kv_trunk, or attn_fwd with a workspace)",
+                    pl.total, hc::kScratchBytes);
+    void* ws = nullptr;
+    HIPCHK(hc::scratch_address(&ws));
+    return attn_fwd(q, k, v, o, lse, S, Hq, Hkv, D, causal, head_chunk, kv_trunk, ws,
+                    hc::kScratchBytes, stream);
+}
+
 const char* attn_last_error(void) { return g_err; }
 
 int attn_set_single_stream(int on) { return g_single_stream.exchange(on ? 1 : 0); }

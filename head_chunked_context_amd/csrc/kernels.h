@@ -155,4 +155,10 @@ hipError_t launch_dq(const DqParams& p, int D, hipStream_t st);
 constexpr int kWideMinBlocks = 256;
 constexpr int kDkdvBlockN = 128;
 
+// The built-in workspace of attn_fwd_noalloc (scratch.hip): 64 MiB per device.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+// Device address of the current device's built-in workspace (looked up once
+// per device with hipGetSymbolAddress, then cached).
+hipError_t scratch_address(void** out);
+
 }  // namespace hc

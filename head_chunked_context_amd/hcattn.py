@@ -51,6 +51,8 @@ def lib():
                                                   ctypes.c_double, ctypes.c_double,
                                                   ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]
     L.attn_pick_kv_trunk.restype = ctypes.c_int
+    L.attn_fwd_noalloc.argtypes = [vp] * 5 + shape + [vp]
+    L.attn_fwd_noalloc.restype = ctypes.c_int
     L.attn_last_error.argtypes = []
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_set_single_stream.argtypes = [ctypes.c_int]
@@ -199,6 +201,30 @@ def attn_fwd(q, k, v, *, head_chunk: int = 0, kv_trunk: int = 0, causal: bool = 
                         l.data_ptr() if l is not None else None,
                         S, Hq, Hkv, D, int(causal), head_chunk, kv_trunk, ws.data_ptr(), nb,
                         _stream(dev))
+    _check(rc)
+    return o, l
+
+
+def attn_fwd_noalloc(q, k, v, *, head_chunk: int = 0, kv_trunk: int = 0, causal: bool = True,
+                     out=None, lse=None, with_lse: bool = True):
+    """attn_fwd on the library's built-in workspace (attn_fwd_noalloc: no
+    device allocation inside the call; ATTN_NOALLOC_WORKSPACE_BYTES per GPU).
+    Pass out (and lse) to allocate nothing at all."""
+    for n, t in (("q", q), ("k", k)):
+        _bf16(n, t)
+    S, Hq, Hkv, D = _dims(q, k)
+    bf = torch.bfloat16
+    dev, _ = _validate([("q", q, q.shape, bf), ("k", k, k.shape, bf), ("v", v, k.shape, bf),
+                        ("out", out, q.shape, bf),
+                        ("lse", lse if with_lse else None, (Hq, S), torch.float32)],
+                       ("k", "v"))
+    o = torch.empty_like(q) if out is None else out
+    l = None
+    if with_lse:
+        l = torch.empty((Hq, S), dtype=torch.float32, device=dev) if lse is None else lse
+    rc = lib().attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                l.data_ptr() if l is not None else None,
+                                S, Hq, Hkv, D, int(causal), head_chunk, kv_trunk, _stream(dev))
     _check(rc)
     return o, l
 

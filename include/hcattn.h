@@ -165,6 +165,25 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int32_t D, int32_t causal, int32_t head_chunk, int64_t kv_trunk, void* workspace,
              size_t workspace_bytes, void* stream);
 
+/*
+ * attn_fwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  It allocates nothing (no hipMalloc, no library
+ * allocation); the workspace is the library's built-in device array of
+ * ATTN_NOALLOC_WORKSPACE_BYTES per GPU, held from the first use on a device
+ * until the process ends.  Arguments, outputs and results are attn_fwd's, bit
+ * for bit.  Returns ATTN_EWORKSPACE, before any work, when
+ * attn_fwd_workspace_bytes(...) exceeds that size (a smaller head_chunk or a
+ * kv_trunk brings any shape under it: the trunked forward's workspace does not
+ * grow with S).  Every call on one GPU uses that GPU's one array: calls that
+ * overlap on a device (several streams or host threads at once) race; order
+ * them.
+ */
+#define ATTN_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t S,
+                     int32_t Hq, int32_t Hkv, int32_t D, int32_t causal, int32_t head_chunk,
+                     int64_t kv_trunk, void* stream);
+
 /* This thread's message for the last non-zero status ("" if none). */
 const char* attn_last_error(void);
 

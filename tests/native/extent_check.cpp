@@ -126,7 +126,20 @@ hipError_t hipMemcpy2DAsync(void* dst, size_t dpitch, const void* src, size_t sp
 
 // ------------------------------------------------------------ kernel replicas
 
+// the built-in workspace of attn_fwd_noalloc: one registered buffer standing
+// in for the device array, its regions added by the driver before each call
+static std::vector<char> g_scratch;
+static char* scratch_base() {
+    if (g_scratch.empty()) g_scratch.resize(hc::kScratchBytes + 256);
+    return g_scratch.data() + (256 - (uintptr_t)g_scratch.data() % 256) % 256;
+}
+
 namespace hc {
+
+hipError_t scratch_address(void** out) {
+    *out = scratch_base();
+    return hipSuccess;
+}
 
 // Rows a 64-row tile load reads from `base` (stride rs elements): rows at or
 // past nvalid re-read row nvalid - 1 (TileDma64 / direct_tile64).
@@ -502,6 +515,18 @@ static void run_case(int64_t S, int Hq, int Hkv, int D, int causal, int hc, int6
     if (rc != ATTN_OK) fail_msg("attn_fwd returned %llu (%llu)", attn_last_error(), (size_t)rc, 0);
     g_regions.resize(keep);
     g_allocs.pop_back();
+    if (nf <= ATTN_NOALLOC_WORKSPACE_BYTES) {
+        // the same forward on the built-in workspace
+        char* sb = scratch_base();
+        g_allocs.push_back({(uintptr_t)sb, (uintptr_t)sb + hc::kScratchBytes, false});
+        add_workspace(sb, pf);
+        rc = attn_fwd_noalloc(q.p(), k.p(), v.p(), o.p(), (float*)lse.p(), S, Hq, Hkv, D, causal,
+                              hc, T, nullptr);
+        if (rc != ATTN_OK)
+            fail_msg("attn_fwd_noalloc returned %llu (%llu)", attn_last_error(), (size_t)rc, 0);
+        g_regions.resize(keep);
+        g_allocs.pop_back();
+    }
     g_allocs.push_back({(uintptr_t)wb, (uintptr_t)wb + nb, false});
     hc::make_plan(true, S, Hq, Hkv, D, causal, hc, T, &pb, msg, sizeof msg);
     add_workspace(wb, pb);
