@@ -69,9 +69,14 @@ def _bind(lib):
     lib.orc_attn_bwd.argtypes = [_dp, _dp, _dp, _dp] + shape + [_dp, _dp, _dp, _dp, _dp]
     lib.orc_attn_dq_rows.argtypes = [_dp, _dp, _lp, _i64, _dp, _dp] + shape + [_dp, _dp]
     lib.orc_attn_dkdv_cols.argtypes = [_dp, _dp, _i64, _dp, _dp] + shape + [_lp, _i64, _dp, _dp]
+    lshape = [_i64, _int, _int, _int, _int, _int]  # S, dm, Hq, Hkv, D, causal
+    lib.orc_layer_fwd.argtypes = [_dp] * 5 + lshape + [_dp, _dp]
+    lib.orc_layer_fwd_chunked.argtypes = [_dp] * 5 + lshape + [_int, _dp]
+    lib.orc_layer_bwd.argtypes = [_dp] * 6 + lshape + [_dp] * 5
     for f in (lib.orc_attn_fwd, lib.orc_attn_fwd_rows, lib.orc_attn_fwd_trunked,
               lib.orc_attn_fwd_chunked, lib.orc_attn_bwd, lib.orc_attn_dq_rows,
-              lib.orc_attn_dkdv_cols):
+              lib.orc_attn_dkdv_cols, lib.orc_layer_fwd, lib.orc_layer_fwd_chunked,
+              lib.orc_layer_bwd):
         f.restype = _int
     return lib
 
@@ -194,3 +199,52 @@ def attn_dkdv_cols(q_tail, dout_tail, i0: int, k, v, cols, causal: bool = True):
                                       Hkv, D, int(causal), cols.ctypes.data_as(_lp), n, _p(dk),
                                       _p(dv)), "orc_attn_dkdv_cols")
     return dk, dv
+
+
+# ------------------------------------------------------------ attention layer
+#
+# x [S, dm]; wq [Hq*D, dm]; wk, wv [Hkv*D, dm]; wo [dm, Hq*D] (weights in the
+# [out][in] convention, y = x W^T); no bias, no rotary embedding, batch 1.
+
+
+def _layer_dims(x, wq, wk, wo, Hq, Hkv, D):
+    if x.ndim != 2 or wq.shape != (Hq * D, x.shape[1]) or wk.shape != (Hkv * D, x.shape[1]) \
+            or wo.shape != (x.shape[1], Hq * D):
+        raise ValueError("layer shapes: x [S,dm], wq [Hq*D,dm], wk/wv [Hkv*D,dm], wo [dm,Hq*D]")
+    return x.shape[0], x.shape[1]
+
+
+def layer_fwd(x, wq, wk, wv, wo, Hq: int, Hkv: int, D: int, causal: bool = True):
+    """y = attention(x Wq^T, x Wk^T, x Wv^T) Wo^T: returns (y [S,dm], lse [Hq,S])."""
+    x, wq, wk, wv, wo = (_f64(t) for t in (x, wq, wk, wv, wo))
+    S, dm = _layer_dims(x, wq, wk, wo, Hq, Hkv, D)
+    y = np.empty((S, dm))
+    lse = np.empty((Hq, S))
+    _check(_load().orc_layer_fwd(_p(x), _p(wq), _p(wk), _p(wv), _p(wo), S, dm, Hq, Hkv, D,
+                                 int(causal), _p(y), _p(lse)), "orc_layer_fwd")
+    return y, lse
+
+
+def layer_fwd_chunked(x, wq, wk, wv, wo, Hq: int, Hkv: int, D: int, head_chunk: int,
+                      causal: bool = True):
+    """The layer walked head chunk by head chunk (projections of the chunk's
+    heads, attention, the chunk's share of the output projection)."""
+    x, wq, wk, wv, wo = (_f64(t) for t in (x, wq, wk, wv, wo))
+    S, dm = _layer_dims(x, wq, wk, wo, Hq, Hkv, D)
+    y = np.empty((S, dm))
+    _check(_load().orc_layer_fwd_chunked(_p(x), _p(wq), _p(wk), _p(wv), _p(wo), S, dm, Hq, Hkv,
+                                         D, int(causal), int(head_chunk), _p(y)),
+           "orc_layer_fwd_chunked")
+    return y
+
+
+def layer_bwd(x, wq, wk, wv, wo, dy, Hq: int, Hkv: int, D: int, causal: bool = True):
+    """Gradients of sum(y * dy): dict with dx, dwq, dwk, dwv, dwo."""
+    x, wq, wk, wv, wo, dy = (_f64(t) for t in (x, wq, wk, wv, wo, dy))
+    S, dm = _layer_dims(x, wq, wk, wo, Hq, Hkv, D)
+    out = {"dx": np.empty((S, dm)), "dwq": np.empty(wq.shape), "dwk": np.empty(wk.shape),
+           "dwv": np.empty(wv.shape), "dwo": np.empty(wo.shape)}
+    _check(_load().orc_layer_bwd(_p(x), _p(wq), _p(wk), _p(wv), _p(wo), _p(dy), S, dm, Hq, Hkv,
+                                 D, int(causal), _p(out["dx"]), _p(out["dwq"]), _p(out["dwk"]),
+                                 _p(out["dwv"]), _p(out["dwo"])), "orc_layer_bwd")
+    return out

@@ -407,3 +407,175 @@ int orc_attn_dkdv_cols(const double* q_tail, const double* dout_tail, i64 i0, co
     free(Dl);
     return 0;
 }
+
+/* ------------------------------------------------- attention layer (NEXT) */
+
+/*
+ * The attention layer around the attention itself, as the U-Pipe paragraph
+ * of the Road to 5 Million Tokens talk describes the chunk loop: for a group
+ * of heads, the heads' projections are (re)computed, attention runs on them,
+ * and the group's partial result is stored before the buffers are reused.
+ * The pages name no projection shapes; the readings here (each listed in the
+ * design notes): weights in the [out][in] convention, no bias, no rotary
+ * embedding, batch 1, d_model = dm:
+ *     q = x Wq^T  [S][Hq*D]     Wq [Hq*D][dm]
+ *     k = x Wk^T  [S][Hkv*D]    Wk [Hkv*D][dm]
+ *     v = x Wv^T  [S][Hkv*D]    Wv [Hkv*D][dm]
+ *     o = attention(q, k, v)    (the definition above, heads as [S][H][D])
+ *     y = o Wo^T  [S][dm]       Wo [dm][Hq*D]
+ * and the gradients of L = sum(y * dy).
+ */
+
+/* out[s][n] = sum_c a[s][c] w[n][c]   (a [S][K], w [N][K]) */
+static void matmul_nt(const double* a, const double* w, i64 S, int K, int N, double* out) {
+#pragma omp parallel for schedule(static)
+    for (i64 s = 0; s < S; ++s)
+        for (int n = 0; n < N; ++n)
+            out[(size_t)s * N + n] = dot(a + (size_t)s * K, w + (size_t)n * K, K);
+}
+
+/* out[s][c] = sum_n g[s][n] w[n][c]   (g [S][N], w [N][K]); accumulate if acc */
+static void matmul_nn(const double* g, const double* w, i64 S, int N, int K, double* out, int acc) {
+#pragma omp parallel for schedule(static)
+    for (i64 s = 0; s < S; ++s)
+        for (int c = 0; c < K; ++c) {
+            double t = 0.0;
+            for (int n = 0; n < N; ++n) t += g[(size_t)s * N + n] * w[(size_t)n * K + c];
+            out[(size_t)s * K + c] = acc ? out[(size_t)s * K + c] + t : t;
+        }
+}
+
+/* out[n][c] = sum_s g[s][n] a[s][c]   (g [S][N], a [S][K]) */
+static void matmul_tn(const double* g, const double* a, i64 S, int N, int K, double* out) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int n = 0; n < N; ++n)
+        for (int c = 0; c < K; ++c) {
+            double t = 0.0;
+            for (i64 s = 0; s < S; ++s) t += g[(size_t)s * N + n] * a[(size_t)s * K + c];
+            out[(size_t)n * K + c] = t;
+        }
+}
+
+int orc_layer_fwd(const double* x, const double* wq, const double* wk, const double* wv,
+                  const double* wo, i64 S, int dm, int Hq, int Hkv, int D, int causal,
+                  double* y, double* lse) {
+    if (bad_shape(S, Hq, Hkv, D, causal) || dm < 1) return -1;
+    const int nq = Hq * D, nk = Hkv * D;
+    double* q = (double*)malloc(sizeof(double) * (size_t)S * nq);
+    double* k = (double*)malloc(sizeof(double) * (size_t)S * nk);
+    double* v = (double*)malloc(sizeof(double) * (size_t)S * nk);
+    double* o = (double*)malloc(sizeof(double) * (size_t)S * nq);
+    double* l = (double*)malloc(sizeof(double) * (size_t)Hq * S);
+    int rc = (q && k && v && o && l) ? 0 : -1;
+    if (rc == 0) {
+        matmul_nt(x, wq, S, dm, nq, q);
+        matmul_nt(x, wk, S, dm, nk, k);
+        matmul_nt(x, wv, S, dm, nk, v);
+        rc = orc_attn_fwd(q, k, v, S, Hq, Hkv, D, causal, o, l);
+    }
+    if (rc == 0) {
+        matmul_nt(o, wo, S, nq, dm, y);
+        if (lse) memcpy(lse, l, sizeof(double) * (size_t)Hq * S);
+    }
+    free(q); free(k); free(v); free(o); free(l);
+    return rc;
+}
+
+/*
+ * The same layer walked a head chunk at a time in the U-Pipe order: for the
+ * chunk's query heads [h0, h0 + nh) and the kv heads they read, project only
+ * those heads from x into one set of chunk buffers (allocated once, reused by
+ * every chunk), run attention on the chunk, and add the chunk's share of the
+ * output projection, o_c Wo[:, chunk columns]^T, into y.
+ */
+int orc_layer_fwd_chunked(const double* x, const double* wq, const double* wk, const double* wv,
+                          const double* wo, i64 S, int dm, int Hq, int Hkv, int D, int causal,
+                          int hc, double* y) {
+    if (bad_shape(S, Hq, Hkv, D, causal) || dm < 1 || hc < 1) return -1;
+    const int g = Hq / Hkv;
+    if (hc > Hq) hc = Hq;
+    int kvmax = (hc + g - 1) / g + 1;
+    if (kvmax > Hkv) kvmax = Hkv;
+    double* qc = (double*)malloc(sizeof(double) * (size_t)S * hc * D);
+    double* kc = (double*)malloc(sizeof(double) * (size_t)S * kvmax * D);
+    double* vc = (double*)malloc(sizeof(double) * (size_t)S * kvmax * D);
+    double* oc = (double*)malloc(sizeof(double) * (size_t)S * hc * D);
+    double* lc = (double*)malloc(sizeof(double) * (size_t)S * hc);
+    double* woc = (double*)malloc(sizeof(double) * (size_t)dm * hc * D);
+    int rc = (qc && kc && vc && oc && lc && woc) ? 0 : -1;
+    for (size_t i = 0; rc == 0 && i < (size_t)S * dm; ++i) y[i] = 0.0;
+    for (int h0 = 0; rc == 0 && h0 < Hq; h0 += hc) {
+        const int nh = (h0 + hc <= Hq) ? hc : Hq - h0;
+        const int kv0 = h0 / g, nkv = (h0 + nh - 1) / g - kv0 + 1;
+        /* the chunk's rows of Wq / Wk / Wv are contiguous: heads h0.. and kv0.. */
+        matmul_nt(x, wq + (size_t)h0 * D * dm, S, dm, nh * D, qc);
+        matmul_nt(x, wk + (size_t)kv0 * D * dm, S, dm, nkv * D, kc);
+        matmul_nt(x, wv + (size_t)kv0 * D * dm, S, dm, nkv * D, vc);
+        /* attention of the chunk: query head hh reads local kv head (h0+hh)/g - kv0 */
+        const double c = 1.0 / sqrt((double)D);
+#pragma omp parallel for collapse(2) schedule(dynamic, 4)
+        for (int hh = 0; hh < nh; ++hh)
+            for (i64 i = 0; i < S; ++i) {
+                const double* qi = qc + ((size_t)i * nh + hh) * D;
+                const int kvl = (h0 + hh) / g - kv0;
+                const i64 j1 = last_key(i, S, causal);
+                const double L = row_lse(qi, kc, 0, j1, kvl, nkv, D, c);
+                lc[(size_t)hh * S + i] = L;
+                row_out(qi, kc, vc, 0, j1, kvl, nkv, D, c, L, oc + ((size_t)i * nh + hh) * D);
+            }
+        /* y += o_c Wo[:, h0*D .. (h0+nh)*D]^T */
+        for (int m = 0; m < dm; ++m)
+            for (int n = 0; n < nh * D; ++n) woc[(size_t)m * nh * D + n] = wo[(size_t)m * Hq * D + (size_t)h0 * D + n];
+#pragma omp parallel for schedule(static)
+        for (i64 s = 0; s < S; ++s)
+            for (int m = 0; m < dm; ++m)
+                y[(size_t)s * dm + m] += dot(oc + (size_t)s * nh * D, woc + (size_t)m * nh * D, nh * D);
+    }
+    free(qc); free(kc); free(vc); free(oc); free(lc); free(woc);
+    return rc;
+}
+
+/*
+ * Backward of L = sum(y * dy) through the layer:
+ *     do  = dy Wo,          dWo = dy^T o
+ *     (dq, dk, dv) = attention backward with do
+ *     dx  = dq Wq + dk Wk + dv Wv
+ *     dWq = dq^T x,  dWk = dk^T x,  dWv = dv^T x
+ */
+int orc_layer_bwd(const double* x, const double* wq, const double* wk, const double* wv,
+                  const double* wo, const double* dy, i64 S, int dm, int Hq, int Hkv, int D,
+                  int causal, double* dx, double* dwq, double* dwk, double* dwv, double* dwo) {
+    if (bad_shape(S, Hq, Hkv, D, causal) || dm < 1) return -1;
+    const int nq = Hq * D, nk = Hkv * D;
+    double* q = (double*)malloc(sizeof(double) * (size_t)S * nq);
+    double* k = (double*)malloc(sizeof(double) * (size_t)S * nk);
+    double* v = (double*)malloc(sizeof(double) * (size_t)S * nk);
+    double* o = (double*)malloc(sizeof(double) * (size_t)S * nq);
+    double* l = (double*)malloc(sizeof(double) * (size_t)Hq * S);
+    double* dov = (double*)malloc(sizeof(double) * (size_t)S * nq);
+    double* dq = (double*)malloc(sizeof(double) * (size_t)S * nq);
+    double* dk = (double*)malloc(sizeof(double) * (size_t)S * nk);
+    double* dv = (double*)malloc(sizeof(double) * (size_t)S * nk);
+    int rc = (q && k && v && o && l && dov && dq && dk && dv) ? 0 : -1;
+    if (rc == 0) {
+        matmul_nt(x, wq, S, dm, nq, q);
+        matmul_nt(x, wk, S, dm, nk, k);
+        matmul_nt(x, wv, S, dm, nk, v);
+        rc = orc_attn_fwd(q, k, v, S, Hq, Hkv, D, causal, o, l);
+    }
+    if (rc == 0) {
+        matmul_nn(dy, wo, S, dm, nq, dov, 0);
+        matmul_tn(dy, o, S, dm, nq, dwo);
+        rc = orc_attn_bwd(q, k, v, dov, S, Hq, Hkv, D, causal, dq, dk, dv, NULL, NULL);
+    }
+    if (rc == 0) {
+        matmul_nn(dq, wq, S, nq, dm, dx, 0);
+        matmul_nn(dk, wk, S, nk, dm, dx, 1);
+        matmul_nn(dv, wv, S, nk, dm, dx, 1);
+        matmul_tn(dq, x, S, nq, dm, dwq);
+        matmul_tn(dk, x, S, nk, dm, dwk);
+        matmul_tn(dv, x, S, nk, dm, dwv);
+    }
+    free(q); free(k); free(v); free(o); free(l); free(dov); free(dq); free(dk); free(dv);
+    return rc;
+}

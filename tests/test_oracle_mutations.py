@@ -122,3 +122,55 @@ def test_golden_examples_catch_planted_mistake(workdir, name):
                 T._check_golden(p)
     finally:
         orc.restore_library(prev)
+
+
+# ------------------------------------------------------------ attention layer
+
+LAYER_MUTATIONS = [
+    ("value projection uses Wk", "matmul_nt(x, wv, S, dm, nk, v);",
+     "matmul_nt(x, wk, S, dm, nk, v);", -1),
+    ("dx drops the key-projection term", "        matmul_nn(dk, wk, S, nk, dm, dx, 1);\n", "", 1),
+    ("dWq taken against dy instead of x", "matmul_tn(dq, x, S, nq, dm, dwq);",
+     "matmul_tn(dq, dy, S, nq, dm, dwq);", 1),
+    ("dO not projected back through Wo", "matmul_nn(dy, wo, S, dm, nq, dov, 0);",
+     "matmul_nt(dy, wo, S, dm, nq, dov);", 1),
+    ("chunked walk keeps only the last chunk's output",
+     "y[(size_t)s * dm + m] += dot(", "y[(size_t)s * dm + m] = dot(", 1),
+    ("chunk projects the wrong kv heads", "matmul_nt(x, wk + (size_t)kv0 * D * dm, S, dm, nkv * D, kc);",
+     "matmul_nt(x, wk, S, dm, nkv * D, kc);", 1),
+]
+
+
+def layer_pins():
+    from tests import test_oracle_layer as L
+    return [
+        ("fd", lambda: L.test_layer_gradients_match_central_differences(3, True)),
+        ("torch", lambda: L.test_layer_matches_torch_fp64(20, 16, 6, 3, 4, True)),
+        ("wq=0", L.test_layer_q_projection_zero_closed_form),
+        ("identity", L.test_identity_projections_reduce_to_the_attention_oracle),
+        ("chunks", lambda: L.test_layer_head_chunks_give_the_unchunked_result(3)),
+        ("linear", L.test_layer_is_linear_in_the_output_projection_and_dy),
+    ]
+
+
+@pytest.mark.parametrize("name,old,new,count", LAYER_MUTATIONS, ids=[m[0] for m in LAYER_MUTATIONS])
+def test_layer_pins_catch_planted_mistake(workdir, name, old, new, count):
+    src = open(SRC).read()
+    assert old in src, f"mutation anchor not found: {name}"
+    mutated = src.replace(old, new) if count < 0 else src.replace(old, new, count)
+    cpath = os.path.join(workdir, "l.c")
+    lpath = os.path.join(workdir, f"l_{abs(hash(name))}.so")
+    open(cpath, "w").write(mutated)
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-shared", "-fPIC", "-o", lpath, cpath, "-lm"],
+                   check=True)
+    prev = orc.use_library(lpath)
+    caught = []
+    try:
+        for pin, fn in layer_pins():
+            try:
+                fn()
+            except (AssertionError, ValueError, IndexError, FloatingPointError):
+                caught.append(pin)
+    finally:
+        orc.restore_library(prev)
+    assert caught, f"no layer pin caught the planted mistake: {name}"
