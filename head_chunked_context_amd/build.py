@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libhcattn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["fwd.hip", "bwd.hip", "aux.hip", "scratch.hip", "hcattn.cpp"]
+SOURCES = ["fwd.hip", "bwd.hip", "aux.hip", "gemm.hip", "scratch.hip", "hcattn.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -1,0 +1,258 @@
+// gemm.hip - bf16 MFMA matrix products of the attention layer around the
+// attention: the Q/K/V projections a head chunk recomputes, the chunk's
+// share of the output projection, and their gradients (Road to 5 Million
+// Tokens talk, the U-Pipe paragraph: a group of heads is recomputed, attended
+// and its partial result stored, then the buffers are reused).
+//
+//   C[m][n] = sum_k A(m, k) B(n, k)        m < M, n < N, k < K, fp32 accumulate
+//
+// Operands are bf16 in "segmented" strided layouts, so one kernel reads the
+// token-major activations ([S][dm]), the [out][in] weights and the head-major
+// chunk buffers ([h][S][D], whose columns h * D + d jump by S * D at every D):
+//   A_KC (k contiguous):  A(m, k) = a[(k / a_seg) a_segs + m a_rs + k % a_seg]
+//   else (m contiguous):  A(m, k) = a[(m / a_seg) a_segs + k a_rs + m % a_seg]
+// and the same for B with n in place of m.  Segments are multiples of 8.
+//
+// Workgroup = 4 waves on a 128 x 128 tile of C, 2 x 2 waves of 64 x 64; K in
+// steps of 32 staged through LDS (registers -> LDS, double-buffered, one
+// barrier per step).  A k-contiguous operand tile is [128][32] with rows
+// padded to 80 bytes (conflict-free 8-byte reads); an m- or n-contiguous one
+// is [32][128] with the XOR-swizzled rows of the attention kernels, read
+// transposed by ds_read_b64_tr_b16.  Both reads deliver the 16 reduction
+// indices of an MFMA step in the same order (k0 + 4c + 0..3, k0 + 8 + 4c +
+// 0..3 for lane half c), so any pair of layouts multiplies consistently.
+// Each wave computes C^T blocks (MFMA rows = n, columns = m): a lane then
+// holds one row m of C with runs of 4 consecutive n, written as 8- or
+// 16-byte stores.
+//
+// Outputs: bf16 (head-major scatter through the segmented C layout), fp32, or
+// fp32 accumulated into C: the accumulators then start from C's values, so a
+// reduction split over several launches (one head chunk each) adds its terms
+// in the same order as a single launch, bit for bit.
+// Split-K: blockIdx.z takes k in [z * k_split, (z + 1) * k_split) and writes
+// fp32 partials at c + z * c_zs; gemm_reduce adds the slices in ascending z.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace hc {
+
+namespace {
+
+constexpr int GBM = 128, GBN = 128, GBK = 32;
+constexpr int KC_PITCH = 40;  // bf16 per padded row of a k-contiguous tile
+
+// 16 reduction indices of one MFMA step from a k-contiguous [rows][KC_PITCH]
+// tile, row `row`, in the transposed-read order
+__device__ __forceinline__ bf16x8 kc_frag(const char* tile, int row, int k0, int c) {
+    const char* p = tile + row * (KC_PITCH * 2) + (k0 + 4 * c) * 2;
+    const s16x4 a = *reinterpret_cast<const s16x4*>(p);
+    const s16x4 b = *reinterpret_cast<const s16x4*>(p + 16);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <bool KC>
+struct OperandTile {
+    // 512 16-byte chunks per 128 x 32 tile, two per thread
+    uint4 r[2];
+
+    // rows (m or n) r0.., reduction indices k0..; zero outside [0, R) x [0, K)
+    __device__ __forceinline__ void load(const uint16_t* base, int64_t rs, int64_t seg,
+                                         int64_t segs, int64_t r0, int64_t R, int64_t k0,
+                                         int64_t K, int tid) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int idx = tid + i * 256;
+            int64_t row, k;
+            if constexpr (KC) {
+                row = r0 + idx / 4;
+                k = k0 + (idx % 4) * 8;
+            } else {
+                k = k0 + idx / 16;
+                row = r0 + (idx % 16) * 8;
+            }
+            if (row < R && k < K) {
+                const int64_t off = KC ? (k / seg) * segs + row * rs + k % seg
+                                       : (row / seg) * segs + k * rs + row % seg;
+                r[i] = *reinterpret_cast<const uint4*>(base + off);
+            } else {
+                r[i] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
+    __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int idx = tid + i * 256;
+            int off;
+            if constexpr (KC) off = (idx / 4) * (KC_PITCH * 2) + (idx % 4) * 16;
+            else off = lds_off<128>(idx / 16, (idx % 16) * 8);
+            *reinterpret_cast<uint4*>(lds + off) = r[i];
+        }
+    }
+};
+
+template <bool KC>
+__device__ __forceinline__ bf16x8 frag(const char* tile, const OperandOffsets<128>& off,
+                                       int blk32, int k0, int lane) {
+    if constexpr (KC) return kc_frag(tile, blk32 * 32 + (lane & 31), k0, lane >> 5);
+    else return lds_read_tr_at<128>(tile, off, k0, blk32);
+}
+
+}  // namespace
+
+template <bool A_KC, bool B_KC>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
+    constexpr int TA = A_KC ? GBM * KC_PITCH * 2 : GBK * 128 * 2;
+    constexpr int TB = B_KC ? GBN * KC_PITCH * 2 : GBK * 128 * 2;
+    __shared__ __attribute__((aligned(1024))) char sa[2][TA];
+    __shared__ __attribute__((aligned(1024))) char sb[2][TB];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1, hi = lane >> 5;
+    const int64_t m0 = (int64_t)blockIdx.x * GBM, n0 = (int64_t)blockIdx.y * GBN;
+    const int64_t kb = p.k_split > 0 ? (int64_t)blockIdx.z * p.k_split : 0;
+    int64_t ke = p.k_split > 0 ? kb + p.k_split : p.K;
+    ke = ke < p.K ? ke : p.K;
+    const int nkt = ke > kb ? (int)((ke - kb + GBK - 1) / GBK) : 0;
+
+    OperandTile<A_KC> ta;
+    OperandTile<B_KC> tb;
+    // lane: row m of C; register group g4 of block nb: columns n .. n + 3
+    char* cz = static_cast<char*>(p.c) +
+               (int64_t)blockIdx.z * p.c_zs * (p.out_mode == kGemmBf16 ? 2 : 4);
+    auto c_off = [&](int mb, int nb, int g4, int64_t* m, int64_t* n) {
+        *m = m0 + wm * 64 + mb * 32 + (lane & 31);
+        *n = n0 + wn * 64 + nb * 32 + g4 * 8 + hi * 4;
+        return (*n / p.c_seg) * p.c_segs + *m * p.c_rs + *n % p.c_seg;
+    };
+    // accumulating products start from C itself, so a product whose reduction
+    // is split over several launches adds in the same order as one launch
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            acc[nb][mb] = f32x16{};
+            if (p.out_mode == kGemmF32Add) {
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    int64_t m, n;
+                    const int64_t o = c_off(mb, nb, g4, &m, &n);
+                    if (m < p.M && n < p.N) {
+                        const f32x4 x = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(cz) + o);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[nb][mb][g4 * 4 + e] = x[e];
+                    }
+                }
+            }
+        }
+
+    const OperandOffsets<128> off(lane);
+    if (nkt > 0) {
+        ta.load(p.a, p.a_rs, p.a_seg, p.a_segs, m0, p.M, kb, ke, tid);
+        tb.load(p.b, p.b_rs, p.b_seg, p.b_segs, n0, p.N, kb, ke, tid);
+        ta.store(sa[0], tid);
+        tb.store(sb[0], tid);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nkt) {
+            const int64_t k1 = kb + (int64_t)(kt + 1) * GBK;
+            ta.load(p.a, p.a_rs, p.a_seg, p.a_segs, m0, p.M, k1, ke, tid);
+            tb.load(p.b, p.b_rs, p.b_seg, p.b_segs, n0, p.N, k1, ke, tid);
+        }
+#pragma unroll
+        for (int ks = 0; ks < GBK / 16; ++ks) {
+            bf16x8 bf[2], af[2];
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) bf[nb] = frag<B_KC>(sb[buf], off, wn * 2 + nb, ks * 16, lane);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) af[mb] = frag<A_KC>(sa[buf], off, wm * 2 + mb, ks * 16, lane);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma32(bf[nb], af[mb], acc[nb][mb]);
+        }
+        if (kt + 1 < nkt) {
+            ta.store(sa[buf ^ 1], tid);
+            tb.store(sb[buf ^ 1], tid);
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                int64_t m, n;
+                const int64_t o = c_off(mb, nb, g4, &m, &n);
+                if (m >= p.M || n >= p.N) continue;
+                const f32x16& a = acc[nb][mb];
+                if (p.out_mode == kGemmBf16) {
+                    const bf16x2 lo = to_bf16x2(a[g4 * 4 + 0], a[g4 * 4 + 1]);
+                    const bf16x2 hi2 = to_bf16x2(a[g4 * 4 + 2], a[g4 * 4 + 3]);
+                    *reinterpret_cast<bf16x4*>(reinterpret_cast<uint16_t*>(cz) + o) =
+                        bf16x4{lo[0], lo[1], hi2[0], hi2[1]};
+                } else {
+                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(cz) + o) =
+                        f32x4{a[g4 * 4 + 0], a[g4 * 4 + 1], a[g4 * 4 + 2], a[g4 * 4 + 3]};
+                }
+            }
+        }
+    }
+}
+
+// out[m][n] (+)= sum_{z ascending} part[z][m][n], 4 fp32 per thread
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmReduceParams p) {
+    const int64_t cpr = p.N / 4;
+    const int64_t total = p.M * cpr;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t m = idx / cpr, n = (idx % cpr) * 4;
+        f32x4 s = *reinterpret_cast<const f32x4*>(p.part + m * p.N + n);
+        for (int z = 1; z < p.splits; ++z) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(p.part + z * p.part_zs + m * p.N + n);
+            s = f32x4{s[0] + x[0], s[1] + x[1], s[2] + x[2], s[3] + x[3]};
+        }
+        f32x4* dst = reinterpret_cast<f32x4*>(p.out + m * p.out_rs + n);
+        if (p.add) {
+            const f32x4 old = *dst;
+            s = f32x4{old[0] + s[0], old[1] + s[1], old[2] + s[2], old[3] + s[3]};
+        }
+        *dst = s;
+    }
+}
+
+hipError_t launch_gemm(const GemmParams& p, bool a_kc, bool b_kc, int splits, hipStream_t st) {
+    if (p.M <= 0 || p.N <= 0) return hipSuccess;
+    // 16-byte operand chunks never straddle a segment, the end of a k-contiguous
+    // row or the end of an r-contiguous one
+    if ((a_kc || b_kc) && p.K % 8 != 0) return hipErrorInvalidValue;
+    if (!a_kc && p.M % 8 != 0) return hipErrorInvalidValue;
+    if (p.N % 8 != 0 || p.a_seg % 8 != 0 || p.b_seg % 8 != 0 || p.c_seg % 4 != 0 ||
+        (p.k_split > 0 && p.k_split % GBK != 0) || splits < 1 || splits > 65535)
+        return hipErrorInvalidValue;
+    const int64_t gx = (p.M + GBM - 1) / GBM, gy = (p.N + GBN - 1) / GBN;
+    if (gx > 0x7fffffffLL || gy > 65535) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)splits), block(256);
+    if (a_kc && b_kc) hipLaunchKernelGGL((gemm_kernel<true, true>), grid, block, 0, st, p);
+    else if (a_kc) hipLaunchKernelGGL((gemm_kernel<true, false>), grid, block, 0, st, p);
+    else if (b_kc) hipLaunchKernelGGL((gemm_kernel<false, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((gemm_kernel<false, false>), grid, block, 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_reduce(const GemmReduceParams& p, hipStream_t st) {
+    if (p.M <= 0 || p.N <= 0) return hipSuccess;
+    if (p.N % 4 != 0 || p.splits < 1) return hipErrorInvalidValue;
+    int64_t b = (p.M * (p.N / 4) + 255) / 256;
+    b = b > 65536 ? 65536 : b;
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)b), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace hc

@@ -211,8 +211,9 @@ int leave(Common& c) {
 
 // ------------------------------------------------------------ kernel timing
 
-enum Kid { K_FWD, K_MERGE, K_PACK, K_PREP, K_DKDV, K_REDUCE, K_DQ, K_COUNT };
-const char* const kKernelNames[K_COUNT] = {"fwd", "merge", "pack", "prep", "dkdv", "reduce", "dq"};
+enum Kid { K_FWD, K_MERGE, K_PACK, K_PREP, K_DKDV, K_REDUCE, K_DQ, K_GEMM, K_COUNT };
+const char* const kKernelNames[K_COUNT] = {"fwd", "merge", "pack", "prep", "dkdv", "reduce", "dq",
+                                           "gemm"};
 
 struct TimingRec {
     int kid;
@@ -588,6 +589,248 @@ int bwd_trunked(Common& c, const BwdIO& io) {
     return ATTN_OK;
 }
 
+// ------------------------------------------------------------ attention layer
+//
+// The layer around the attention, walked a head chunk at a time (Road to 5
+// Million Tokens talk, the U-Pipe paragraph: the chunk's heads are
+// recomputed, attended and their partial result stored, and the buffers are
+// reused).  Weights in the [out][in] convention, y = x W^T:
+//   x [S][dm] bf16; wq [Hq*D][dm], wk, wv [Hkv*D][dm], wo [dm][Hq*D] bf16;
+//   y [S][dm] fp32 = sum over chunks of o_c wo[:, chunk columns]^T.
+// Per chunk: Q_c, K_c, V_c = x W^T of the chunk's rows, written head-major
+// straight by the matrix product; the flash kernel; y += O_c wo_c^T.  The
+// backward recomputes the chunk's projections and attention output, then
+// dO_c = dy wo_c, dWo_c = dy^T O_c, the attention backward, and per GQA group
+// in ascending order dx += dQ_g Wq_g (+ dK Wk + dV Wv once the group's last
+// head is done), dWq = dQ^T x, dWk = dK^T x, dWv = dV^T x.  Every fp32 sum
+// into y and dx continues from the stored value in a fixed group order, so
+// the results do not depend on head_chunk.
+
+struct LayerPlan {
+    hc::Plan at;                 // attention plan of the chunk loop (backward: its regions)
+    int dm;
+    size_t q_c = 0, k_c = 0, v_c = 0, o_c = 0;          // bf16 head-major chunk buffers
+    size_t lse_c = 0, dq_c = 0, dk_c = 0, dv_c = 0;     // backward extras
+    size_t wpart = 0;                                   // split-K partials of weight gradients
+    int splits = 1;
+    int64_t k_split = 0;
+    size_t total = 0;
+};
+
+constexpr int kWgradSplits = 8;
+
+int layer_plan(bool bwd, int64_t S, int dm, int Hq, int Hkv, int D, int causal, int head_chunk,
+               LayerPlan* L) {
+    int r = plan_or_fail(bwd, S, Hq, Hkv, D, causal, head_chunk, 0, &L->at);
+    if (r) return r;
+    if (dm < 64 || dm % 64 != 0) return fail(ATTN_EINVAL, "d_model must be a positive multiple of 64 (got %d)", dm);
+    if ((double)S * dm * 16.0 > 0x1p62) return fail(ATTN_EUNSUPPORTED, "S x d_model too large");
+    const hc::Plan& p = L->at;
+    L->dm = dm;
+    const size_t E = (size_t)S * D * 2;
+    size_t off = p.total;
+    auto take = [&](size_t bytes) { size_t o = off; off = hc::align_up(off + bytes); return o; };
+    if (!bwd) {
+        // the attention plan's own regions (Q_c, K_c, V_c) plus O_c
+        L->q_c = p.q_c; L->k_c = p.k_c; L->v_c = p.v_c;
+        L->o_c = take(p.hc * E);
+    } else {
+        L->q_c = p.q_c; L->k_c = p.k_c; L->v_c = p.v_c;
+        L->o_c = take(p.hc * E);
+        L->lse_c = take((size_t)p.hc * S * 4);
+        L->dq_c = take(p.hc * E);
+        L->dk_c = take(p.kvc * E);
+        L->dv_c = take(p.kvc * E);
+        // split-K of the weight gradients: a function of S only, so that every
+        // weight row sums its terms the same way whatever the chunking
+        L->k_split = (S + 32 * kWgradSplits - 1) / (32 * kWgradSplits) * 32;
+        L->splits = (int)((S + L->k_split - 1) / L->k_split);
+        L->wpart = take((size_t)L->splits * p.hc * D * dm * 4);
+    }
+    L->total = off;
+    return ATTN_OK;
+}
+
+// C = x W^T for `rows` rows of W starting at w (row-major [*][dm]), written
+// bf16 head-major [rows / D][S][D] at dst
+hc::GemmParams proj_params(const uint16_t* x, const uint16_t* w, int rows, int64_t S, int dm,
+                           int D, uint16_t* dst) {
+    hc::GemmParams g{};
+    g.a = x; g.a_rs = dm; g.a_seg = dm; g.a_segs = 0;
+    g.b = w; g.b_rs = dm; g.b_seg = dm; g.b_segs = 0;
+    g.M = S; g.N = rows; g.K = dm;
+    g.c = dst; g.c_rs = D; g.c_seg = D; g.c_segs = S * D;
+    g.out_mode = hc::kGemmBf16;
+    return g;
+}
+
+#define LAUNCH_GEMM(prm, akc, bkc, splits) \
+    KCHK(timed(K_GEMM, c.st, 0.0, [&]() { return hc::launch_gemm((prm), (akc), (bkc), (splits), c.st); }))
+
+// the chunk's projections and attention output into the chunk buffers
+int layer_chunk_forward(Common& c, const LayerPlan& L, const hc::Chunk& ch, const uint16_t* x,
+                        const uint16_t* wq, const uint16_t* wk, const uint16_t* wv, float* lse,
+                        int64_t lse_hs) {
+    const hc::Plan& p = L.at;
+    const int64_t S = p.S;
+    const int D = p.D, dm = L.dm;
+    uint16_t* Qc = reinterpret_cast<uint16_t*>(c.ws + L.q_c);
+    uint16_t* Kc = reinterpret_cast<uint16_t*>(c.ws + L.k_c);
+    uint16_t* Vc = reinterpret_cast<uint16_t*>(c.ws + L.v_c);
+    uint16_t* Oc = reinterpret_cast<uint16_t*>(c.ws + L.o_c);
+    hc::GemmParams g = proj_params(x, wq + (size_t)ch.h0 * D * dm, ch.nh * D, S, dm, D, Qc);
+    LAUNCH_GEMM(g, true, true, 1);
+    g = proj_params(x, wk + (size_t)ch.kv0 * D * dm, ch.nkv * D, S, dm, D, Kc);
+    LAUNCH_GEMM(g, true, true, 1);
+    g = proj_params(x, wv + (size_t)ch.kv0 * D * dm, ch.nkv * D, S, dm, D, Vc);
+    LAUNCH_GEMM(g, true, true, 1);
+    hc::FwdParams f{};
+    f.q = Qc; f.q_rs = D; f.q_hs = S * D;
+    f.k = Kc; f.k_rs = D; f.k_hs = S * D;
+    f.v = Vc; f.v_rs = D; f.v_hs = S * D;
+    f.o = Oc; f.o_rs = D; f.o_hs = S * D;
+    f.lse = lse; f.lse_hs = lse_hs;
+    f.nh = ch.nh; f.group = p.g; f.h0 = ch.h0; f.kv_base = ch.kv0;
+    f.nq = S; f.q_pos0 = 0; f.nk = S; f.k_pos0 = 0;
+    f.causal = p.causal; f.mode = hc::kFwdFinal; f.scale_log2 = c.scale_log2;
+    LAUNCH(K_FWD, hc::launch_fwd(f, D, c.st));
+    return ATTN_OK;
+}
+
+int layer_fwd_run(Common& c, const LayerPlan& L, const uint16_t* x, const uint16_t* wq,
+                  const uint16_t* wk, const uint16_t* wv, const uint16_t* wo, float* y, float* lse) {
+    const hc::Plan& p = L.at;
+    const int64_t S = p.S;
+    const int D = p.D, dm = L.dm;
+    for (int ci = 0; ci < p.nchunks; ++ci) {
+        const hc::Chunk ch = p.chunk(ci);
+        int r = layer_chunk_forward(c, L, ch, x, wq, wk, wv, lse ? lse + (size_t)ch.h0 * S : nullptr, S);
+        if (r) return r;
+        // y += O_c wo[:, h0 D .. (h0 + nh) D]^T
+        hc::GemmParams g{};
+        g.a = reinterpret_cast<const uint16_t*>(c.ws + L.o_c); g.a_rs = D; g.a_seg = D; g.a_segs = S * D;
+        g.b = wo + (size_t)ch.h0 * D; g.b_rs = (int64_t)p.Hq * D; g.b_seg = (int64_t)p.Hq * D; g.b_segs = 0;
+        g.M = S; g.N = dm; g.K = (int64_t)ch.nh * D;
+        g.c = y; g.c_rs = dm; g.c_seg = dm; g.c_segs = 0;
+        g.out_mode = ci == 0 ? hc::kGemmF32 : hc::kGemmF32Add;
+        LAUNCH_GEMM(g, true, true, 1);
+    }
+    return ATTN_OK;
+}
+
+// weight gradient rows: out[m][n] = sum_s A(m, s) B(n, s) over the whole
+// sequence (A, B r-contiguous), split-K into the partial buffer and reduced
+// in ascending split order
+int wgrad(Common& c, const LayerPlan& L, hc::GemmParams g, float* out, int64_t out_rs) {
+    float* part = reinterpret_cast<float*>(c.ws + L.wpart);
+    g.c = part; g.c_rs = g.N; g.c_seg = g.N; g.c_segs = 0;
+    g.out_mode = hc::kGemmF32;
+    g.k_split = L.k_split; g.c_zs = g.M * g.N;
+    LAUNCH_GEMM(g, false, false, L.splits);
+    hc::GemmReduceParams rp{part, g.M * g.N, L.splits, g.M, g.N, out, out_rs, 0};
+    KCHK(timed(K_GEMM, c.st, 0.0, [&]() { return hc::launch_gemm_reduce(rp, c.st); }));
+    return ATTN_OK;
+}
+
+int layer_bwd_run(Common& c, const LayerPlan& L, const uint16_t* x, const uint16_t* wq,
+                  const uint16_t* wk, const uint16_t* wv, const uint16_t* wo, const uint16_t* dy,
+                  float* dx, float* dwq, float* dwk, float* dwv, float* dwo) {
+    const hc::Plan& p = L.at;
+    const int64_t S = p.S;
+    const int D = p.D, dm = L.dm, Hq = p.Hq;
+    uint16_t* Kc = reinterpret_cast<uint16_t*>(c.ws + L.k_c);
+    uint16_t* Vc = reinterpret_cast<uint16_t*>(c.ws + L.v_c);
+    uint16_t* Oc = reinterpret_cast<uint16_t*>(c.ws + L.o_c);
+    uint16_t* dOc = reinterpret_cast<uint16_t*>(c.ws + p.do_c);
+    uint16_t* dQc = reinterpret_cast<uint16_t*>(c.ws + L.dq_c);
+    uint16_t* dKc = reinterpret_cast<uint16_t*>(c.ws + L.dk_c);
+    uint16_t* dVc = reinterpret_cast<uint16_t*>(c.ws + L.dv_c);
+    float* lse_c = reinterpret_cast<float*>(c.ws + L.lse_c);
+    bool dx_started = false;
+    // dx += A(m = s, k) B(n, k) over k < K: A head-major [K / D][S][D] (k
+    // contiguous), B = rows r0.. of a weight [*][dm] read n-contiguous
+    auto dx_add = [&](const uint16_t* a, const uint16_t* w, int64_t K) -> int {
+        hc::GemmParams g{};
+        g.a = a; g.a_rs = D; g.a_seg = D; g.a_segs = S * D;
+        g.b = w; g.b_rs = dm; g.b_seg = dm; g.b_segs = 0;
+        g.M = S; g.N = dm; g.K = K;
+        g.c = dx; g.c_rs = dm; g.c_seg = dm; g.c_segs = 0;
+        g.out_mode = dx_started ? hc::kGemmF32Add : hc::kGemmF32;
+        dx_started = true;
+        LAUNCH_GEMM(g, true, false, 1);
+        return ATTN_OK;
+    };
+    // rows [r0, r0 + K) of a weight gradient: out = A^T x with A head-major
+    auto w_rows = [&](const uint16_t* a, int64_t rows, float* out) -> int {
+        hc::GemmParams g{};
+        g.a = a; g.a_rs = D; g.a_seg = D; g.a_segs = S * D;   // A(m, s) = a[m / D][s][m % D]
+        g.b = x; g.b_rs = dm; g.b_seg = dm; g.b_segs = 0;      // B(n, s) = x[s][n]
+        g.M = rows; g.N = dm; g.K = S;
+        return wgrad(c, L, g, out, dm);
+    };
+    for (int ci = 0; ci < p.nchunks; ++ci) {
+        const hc::Chunk ch = p.chunk(ci);
+        int r = layer_chunk_forward(c, L, ch, x, wq, wk, wv, lse_c, S);
+        if (r) return r;
+        // dO_c = dy wo[:, chunk columns]  (bf16, head-major, where prep reads it)
+        hc::GemmParams g{};
+        g.a = dy; g.a_rs = dm; g.a_seg = dm; g.a_segs = 0;
+        g.b = wo + (size_t)ch.h0 * D; g.b_rs = (int64_t)Hq * D; g.b_seg = (int64_t)Hq * D; g.b_segs = 0;
+        g.M = S; g.N = (int64_t)ch.nh * D; g.K = dm;
+        g.c = dOc; g.c_rs = D; g.c_seg = D; g.c_segs = S * D;
+        g.out_mode = hc::kGemmBf16;
+        LAUNCH_GEMM(g, true, false, 1);
+        // dWo[:, chunk columns] = dy^T O_c
+        g = hc::GemmParams{};
+        g.a = dy; g.a_rs = dm; g.a_seg = dm; g.a_segs = 0;    // A(m, s) = dy[s][m]
+        g.b = Oc; g.b_rs = D; g.b_seg = D; g.b_segs = S * D;  // B(n, s) = O_c[n / D][s][n % D]
+        g.M = dm; g.N = (int64_t)ch.nh * D; g.K = S;
+        if ((r = wgrad(c, L, g, dwo + (size_t)ch.h0 * D, (int64_t)Hq * D))) return r;
+        // attention backward of the chunk (Delta from O_c, dO_c in place)
+        hc::PrepParams pr{};
+        pr.o = Oc; pr.o_rs = D; pr.o_hs = S * D;
+        pr.dO = dOc; pr.do_rs = D; pr.do_hs = S * D;
+        pr.lse = lse_c; pr.lse_hs = S;
+        pr.dO_c = dOc; pr.c_rs = D; pr.c_hs = S * D;
+        pr.ndelta = reinterpret_cast<float*>(c.ws + p.delta_c); pr.ndelta_hs = S;
+        pr.nlse2 = reinterpret_cast<float*>(c.ws + p.lse2_c); pr.nlse2_hs = S;
+        pr.nh = ch.nh; pr.rows = S; pr.D = D;
+        LAUNCH_PASS(K_PREP, pr, hc::launch_prep(pr, c.st));
+        BwdIO io{};
+        io.dq = dQc;
+        hc::DkdvParams dk = dkdv_params(c, ch, io, Kc, Vc, D, S * D, 0, S);
+        LAUNCH(K_DKDV, hc::launch_dkdv(dk, D, c.st));
+        hc::DkdvReduceParams rd = reduce_params(c, ch, ci, 0, S, dKc, dVc, D, S * D);
+        LAUNCH_PASS(K_REDUCE, rd, hc::launch_dkdv_reduce(rd, c.st));
+        hc::DqParams dq = dq_params(c, ch, io, Kc, Vc, D, S * D, 0, S);
+        dq.dq = dQc; dq.dq_rs = D; dq.dq_hs = S * D;
+        LAUNCH(K_DQ, hc::launch_dq(dq, D, c.st));
+        // per GQA group, ascending: dx += dQ_g Wq_g, then dK Wk + dV Wv when the
+        // group's last head is in this chunk; weight-gradient rows
+        const int carry_out = p.carry_out_slot(ci) >= 0 ? 1 : 0;
+        for (int kl = 0; kl < ch.nkv; ++kl) {
+            const int kvg = ch.kv0 + kl;
+            int hb = kvg * p.g, he = hb + p.g;
+            hb = hb < ch.h0 ? ch.h0 : hb;
+            he = he > ch.h0 + ch.nh ? ch.h0 + ch.nh : he;
+            const uint16_t* dq_g = dQc + (size_t)(hb - ch.h0) * S * D;
+            if ((r = dx_add(dq_g, wq + (size_t)hb * D * dm, (int64_t)(he - hb) * D))) return r;
+            const bool done = !(carry_out && kl == ch.nkv - 1);
+            if (done) {
+                if ((r = dx_add(dKc + (size_t)kl * S * D, wk + (size_t)kvg * D * dm, D))) return r;
+                if ((r = dx_add(dVc + (size_t)kl * S * D, wv + (size_t)kvg * D * dm, D))) return r;
+            }
+        }
+        if ((r = w_rows(dQc, (int64_t)ch.nh * D, dwq + (size_t)ch.h0 * D * dm))) return r;
+        const int nfin = ch.nkv - carry_out;
+        if (nfin > 0) {
+            if ((r = w_rows(dKc, (int64_t)nfin * D, dwk + (size_t)ch.kv0 * D * dm))) return r;
+            if ((r = w_rows(dVc, (int64_t)nfin * D, dwv + (size_t)ch.kv0 * D * dm))) return r;
+        }
+    }
+    return ATTN_OK;
+}
+
 int check_ptr(const void* p, const char* name, bool host_ok, bool* is_host) {
     if (p == nullptr) return fail(ATTN_EPOINTER, "%s is NULL", name);
     const Loc l = where(p);
@@ -735,7 +978,82 @@ int attn_set_single_stream(int on) { return g_single_stream.exchange(on ? 1 : 0)
 
 int attn_set_trunk_merge(int on) { return g_trunk_merge.exchange(on ? 1 : 0); }
 
-const char* attn_version(void) { return "0.1.0"; }
+size_t attn_layer_fwd_workspace_bytes(int64_t S, int32_t d_model, int32_t Hq, int32_t Hkv,
+                                      int32_t D, int32_t causal, int32_t head_chunk) {
+    LayerPlan L;
+    if (layer_plan(false, S, d_model, Hq, Hkv, D, causal, head_chunk, &L)) return 0;
+    return L.total;
+}
+
+size_t attn_layer_bwd_workspace_bytes(int64_t S, int32_t d_model, int32_t Hq, int32_t Hkv,
+                                      int32_t D, int32_t causal, int32_t head_chunk) {
+    LayerPlan L;
+    if (layer_plan(true, S, d_model, Hq, Hkv, D, causal, head_chunk, &L)) return 0;
+    return L.total;
+}
+
+int attn_layer_fwd(const void* x, const void* wq, const void* wk, const void* wv, const void* wo,
+                   float* y, float* lse, int64_t S, int32_t d_model, int32_t Hq, int32_t Hkv,
+                   int32_t D, int32_t causal, int32_t head_chunk, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    LayerPlan L;
+    int r = layer_plan(false, S, d_model, Hq, Hkv, D, causal, head_chunk, &L);
+    if (r) return r;
+    if (workspace == nullptr) return fail(ATTN_EWORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % hc::kAlign != 0)
+        return fail(ATTN_EWORKSPACE, "workspace must be %zu-byte aligned", hc::kAlign);
+    if (workspace_bytes < L.total)
+        return fail(ATTN_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+    const void* ins[] = {x, wq, wk, wv, wo, y, workspace};
+    const char* names[] = {"x", "wq", "wk", "wv", "wo", "y", "workspace"};
+    for (int i = 0; i < 7; ++i)
+        if ((r = check_ptr(ins[i], names[i], false, nullptr))) return r;
+    if (lse != nullptr && (r = check_ptr(lse, "lse", false, nullptr))) return r;
+    Common c;
+    init_common(c, L.at, workspace);
+    if ((r = device_resources(&c.dev))) return r;
+    std::lock_guard<std::mutex> lk(c.dev->mu);
+    if ((r = enter(c, static_cast<hipStream_t>(stream)))) return r;
+    r = layer_fwd_run(c, L, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wq),
+                      static_cast<const uint16_t*>(wk), static_cast<const uint16_t*>(wv),
+                      static_cast<const uint16_t*>(wo), y, lse);
+    const int r2 = leave(c);
+    return r ? r : r2;
+}
+
+int attn_layer_bwd(const void* x, const void* wq, const void* wk, const void* wv, const void* wo,
+                   const void* dy, float* dx, float* dwq, float* dwk, float* dwv, float* dwo,
+                   int64_t S, int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D, int32_t causal,
+                   int32_t head_chunk, void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    LayerPlan L;
+    int r = layer_plan(true, S, d_model, Hq, Hkv, D, causal, head_chunk, &L);
+    if (r) return r;
+    if (workspace == nullptr) return fail(ATTN_EWORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % hc::kAlign != 0)
+        return fail(ATTN_EWORKSPACE, "workspace must be %zu-byte aligned", hc::kAlign);
+    if (workspace_bytes < L.total)
+        return fail(ATTN_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+    const void* ins[] = {x, wq, wk, wv, wo, dy, dx, dwq, dwk, dwv, dwo, workspace};
+    const char* names[] = {"x", "wq", "wk", "wv", "wo", "dy", "dx", "dwq", "dwk", "dwv", "dwo",
+                           "workspace"};
+    for (int i = 0; i < 12; ++i)
+        if ((r = check_ptr(ins[i], names[i], false, nullptr))) return r;
+    Common c;
+    init_common(c, L.at, workspace);
+    if ((r = device_resources(&c.dev))) return r;
+    std::lock_guard<std::mutex> lk(c.dev->mu);
+    if ((r = enter(c, static_cast<hipStream_t>(stream)))) return r;
+    r = layer_bwd_run(c, L, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wq),
+                      static_cast<const uint16_t*>(wk), static_cast<const uint16_t*>(wv),
+                      static_cast<const uint16_t*>(wo), static_cast<const uint16_t*>(dy), dx, dwq,
+                      dwk, dwv, dwo);
+    const int r2 = leave(c);
+    return r ? r : r2;
+}
+
+const char* attn_version(void) { return "0.2.0"; }
 
 int attn_timing_enable(int on) { return g_timing.exchange(on ? 1 : 0); }
 

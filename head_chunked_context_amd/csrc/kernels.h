@@ -139,6 +139,36 @@ struct DqParams {
     int64_t final_before; // rows < final_before write bf16 dq, the rest fp32 acc_out
 };
 
+// Matrix product of the attention layer (gemm.hip):
+//   C[m][n] = sum_k A(m, k) B(n, k),  fp32 accumulate over bf16 operands.
+// A k-contiguous operand X(r, k) (r = m for A, n for B) sits at
+//   x[(k / x_seg) * x_segs + r * x_rs + k % x_seg],
+// an r-contiguous one at x[(r / x_seg) * x_segs + k * x_rs + r % x_seg]
+// (which form is a launch argument); C(m, n) at
+//   c[(n / c_seg) * c_segs + m * c_rs + n % c_seg]  (+ z * c_zs for split-K).
+enum GemmOut : int {
+    kGemmBf16 = 0,    // C = bf16(A B)
+    kGemmF32 = 1,     // C = A B in fp32
+    kGemmF32Add = 2,  // C = C + A B in fp32 (accumulators start from C)
+};
+struct GemmParams {
+    const uint16_t* a; int64_t a_rs, a_seg, a_segs;
+    const uint16_t* b; int64_t b_rs, b_seg, b_segs;
+    int64_t M, N, K;
+    void* c;           int64_t c_rs, c_seg, c_segs;
+    int out_mode;
+    int64_t k_split;   // reduction indices per split (multiple of 32); 0 = no split
+    int64_t c_zs;      // elements between the splits' fp32 partial outputs
+};
+// out[m][n] (+ out[m][n] if add) = sum over z ascending of part[z * part_zs + m * N + n]
+struct GemmReduceParams {
+    const float* part; int64_t part_zs;
+    int splits;
+    int64_t M, N;
+    float* out; int64_t out_rs;
+    int add;
+};
+
 hipError_t launch_fwd(const FwdParams& p, int D, hipStream_t st);
 hipError_t launch_pack(const PackParams& p, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, hipStream_t st);
@@ -146,6 +176,8 @@ hipError_t launch_prep(const PrepParams& p, hipStream_t st);
 hipError_t launch_dkdv(const DkdvParams& p, int D, hipStream_t st);
 hipError_t launch_dkdv_reduce(const DkdvReduceParams& p, hipStream_t st);
 hipError_t launch_dq(const DqParams& p, int D, hipStream_t st);
+hipError_t launch_gemm(const GemmParams& p, bool a_kc, bool b_kc, int splits, hipStream_t st);
+hipError_t launch_gemm_reduce(const GemmReduceParams& p, hipStream_t st);
 
 // Launch shapes.  The forward and dQ kernels take 256-row workgroups (8
 // waves, one per compute unit) once a launch has at least kWideMinBlocks of

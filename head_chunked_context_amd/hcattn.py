@@ -53,6 +53,15 @@ def lib():
     L.attn_pick_kv_trunk.restype = ctypes.c_int
     L.attn_fwd_noalloc.argtypes = [vp] * 5 + shape + [vp]
     L.attn_fwd_noalloc.restype = ctypes.c_int
+    lshape = [i64, i32, i32, i32, i32, i32, i32]  # S, d_model, Hq, Hkv, D, causal, head_chunk
+    L.attn_layer_fwd_workspace_bytes.argtypes = lshape
+    L.attn_layer_fwd_workspace_bytes.restype = sz
+    L.attn_layer_bwd_workspace_bytes.argtypes = lshape
+    L.attn_layer_bwd_workspace_bytes.restype = sz
+    L.attn_layer_fwd.argtypes = [vp] * 7 + lshape + [vp, sz, vp]
+    L.attn_layer_fwd.restype = ctypes.c_int
+    L.attn_layer_bwd.argtypes = [vp] * 11 + lshape + [vp, sz, vp]
+    L.attn_layer_bwd.restype = ctypes.c_int
     L.attn_last_error.argtypes = []
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_set_single_stream.argtypes = [ctypes.c_int]
@@ -257,6 +266,76 @@ def attn_bwd(q, k, v, o, dout, lse, *, head_chunk: int = 0, kv_trunk: int = 0,
     return dq, dk, dv
 
 
+def _layer_specs(x, wq, wk, wv, wo, Hq, Hkv, D):
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a [S, d_model] tensor")
+    S, dm = x.shape
+    bf = torch.bfloat16
+    return S, dm, [("x", x, (S, dm), bf), ("wq", wq, (Hq * D, dm), bf),
+                   ("wk", wk, (Hkv * D, dm), bf), ("wv", wv, (Hkv * D, dm), bf),
+                   ("wo", wo, (dm, Hq * D), bf)]
+
+
+def layer_fwd_workspace_bytes(S, d_model, Hq, Hkv, D, causal=True, head_chunk=0) -> int:
+    n = lib().attn_layer_fwd_workspace_bytes(S, d_model, Hq, Hkv, D, int(causal), head_chunk)
+    if n == 0:
+        raise HcAttnError(-1, last_error())
+    return n
+
+
+def layer_bwd_workspace_bytes(S, d_model, Hq, Hkv, D, causal=True, head_chunk=0) -> int:
+    n = lib().attn_layer_bwd_workspace_bytes(S, d_model, Hq, Hkv, D, int(causal), head_chunk)
+    if n == 0:
+        raise HcAttnError(-1, last_error())
+    return n
+
+
+def attn_layer_fwd(x, wq, wk, wv, wo, *, Hq: int, Hkv: int, D: int, head_chunk: int = 0,
+                   causal: bool = True, out=None, lse=None, with_lse: bool = False,
+                   workspace=None):
+    """y = attention(x wq^T, x wk^T, x wv^T) wo^T walked head chunk by head chunk
+    (attn_layer_fwd).  x [S, d_model] bf16; weights [out, in] bf16.  Returns
+    (y [S, d_model] fp32, lse [Hq, S] fp32 or None)."""
+    S, dm, specs = _layer_specs(x, wq, wk, wv, wo, Hq, Hkv, D)
+    specs += [("out", out, (S, dm), torch.float32),
+              ("lse", lse if with_lse else None, (Hq, S), torch.float32)]
+    dev, _ = _validate(specs, ())
+    y = torch.empty((S, dm), dtype=torch.float32, device=dev) if out is None else out
+    l = None
+    if with_lse:
+        l = torch.empty((Hq, S), dtype=torch.float32, device=dev) if lse is None else lse
+    nb = layer_fwd_workspace_bytes(S, dm, Hq, Hkv, D, causal, head_chunk)
+    ws = _workspace(nb, dev, workspace)
+    _check(lib().attn_layer_fwd(x.data_ptr(), wq.data_ptr(), wk.data_ptr(), wv.data_ptr(),
+                                wo.data_ptr(), y.data_ptr(), l.data_ptr() if l is not None else None,
+                                S, dm, Hq, Hkv, D, int(causal), head_chunk, ws.data_ptr(), nb,
+                                _stream(dev)))
+    return y, l
+
+
+def attn_layer_bwd(x, wq, wk, wv, wo, dy, *, Hq: int, Hkv: int, D: int, head_chunk: int = 0,
+                   causal: bool = True, grads=None, workspace=None):
+    """Gradients of sum(y * dy) through attn_layer_fwd (attn_layer_bwd): returns
+    fp32 (dx, dwq, dwk, dwv, dwo).  dy [S, d_model] bf16."""
+    S, dm, specs = _layer_specs(x, wq, wk, wv, wo, Hq, Hkv, D)
+    f32 = torch.float32
+    shapes = [(S, dm), (Hq * D, dm), (Hkv * D, dm), (Hkv * D, dm), (dm, Hq * D)]
+    names = ("dx", "dwq", "dwk", "dwv", "dwo")
+    grads = list(grads) if grads is not None else [None] * 5
+    specs += [("dy", dy, (S, dm), torch.bfloat16)]
+    specs += [(n, g, sh, f32) for n, g, sh in zip(names, grads, shapes)]
+    dev, _ = _validate(specs, ())
+    grads = [torch.empty(sh, dtype=f32, device=dev) if g is None else g
+             for g, sh in zip(grads, shapes)]
+    nb = layer_bwd_workspace_bytes(S, dm, Hq, Hkv, D, causal, head_chunk)
+    ws = _workspace(nb, dev, workspace)
+    _check(lib().attn_layer_bwd(x.data_ptr(), wq.data_ptr(), wk.data_ptr(), wv.data_ptr(),
+                                wo.data_ptr(), dy.data_ptr(), *[g.data_ptr() for g in grads],
+                                S, dm, Hq, Hkv, D, int(causal), head_chunk, ws.data_ptr(), nb,
+                                _stream(dev)))
+    return tuple(grads)
+
+
 def set_single_stream(on: bool) -> bool:
     """Run trunk copies on the caller's stream (race check); returns the old value."""
     return bool(lib().attn_set_single_stream(int(on)))
@@ -272,7 +351,7 @@ def version() -> str:
     return lib().attn_version().decode()
 
 
-KERNEL_FAMILIES = ("fwd", "merge", "pack", "prep", "dkdv", "reduce", "dq")
+KERNEL_FAMILIES = ("fwd", "merge", "pack", "prep", "dkdv", "reduce", "dq", "gemm")
 
 
 def timing_enable(on: bool) -> bool:

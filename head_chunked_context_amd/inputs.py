@@ -69,3 +69,27 @@ def attention_inputs(S: int, Hq: int, Hkv: int, D: int, seed_base: int, device="
     if with_dout:
         out["dout"] = gaussian((S, Hq, D), 1000 * seed_base + TENSOR_IDS["dout"], device, dtype)
     return out
+
+
+LAYER_TENSOR_IDS = {"x": 4, "wq": 5, "wk": 6, "wv": 7, "wo": 8, "dy": 9}
+
+
+def layer_inputs(S: int, d_model: int, Hq: int, Hkv: int, D: int, seed_base: int, device="cpu",
+                 dtype=torch.bfloat16, with_dy: bool = True):
+    """Synthetic inputs of the attention layer around the attention (no trained
+    weights exist here): x [S, d_model] ~ N(0, 1); weights in the [out][in]
+    convention, wq [Hq*D, d_model], wk / wv [Hkv*D, d_model] ~ N(0, 1/d_model)
+    and wo [d_model, Hq*D] ~ N(0, 1/(Hq*D)) (fan-in scaling, so the
+    projected q, k, v are ~N(0, 1) like the attention workloads); dy ~ N(0, 1).
+    Seeds 1000 * seed_base + {x: 4, wq: 5, wk: 6, wv: 7, wo: 8, dy: 9}."""
+    sd = lambda n: 1000 * seed_base + LAYER_TENSOR_IDS[n]
+    out = {
+        "x": gaussian((S, d_model), sd("x"), device, dtype),
+        "wq": gaussian((Hq * D, d_model), sd("wq"), device, dtype, d_model ** -0.5),
+        "wk": gaussian((Hkv * D, d_model), sd("wk"), device, dtype, d_model ** -0.5),
+        "wv": gaussian((Hkv * D, d_model), sd("wv"), device, dtype, d_model ** -0.5),
+        "wo": gaussian((d_model, Hq * D), sd("wo"), device, dtype, (Hq * D) ** -0.5),
+    }
+    if with_dy:
+        out["dy"] = gaussian((S, d_model), sd("dy"), device, dtype)
+    return out

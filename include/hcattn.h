@@ -184,6 +184,51 @@ int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float
                      int32_t Hq, int32_t Hkv, int32_t D, int32_t causal, int32_t head_chunk,
                      int64_t kv_trunk, void* stream);
 
+/*
+ * The attention layer around the attention, walked a head chunk at a time the
+ * way the U-Pipe paragraph of the Road to 5 Million Tokens talk describes it:
+ * for each group of query heads the group's Q/K/V projections are
+ * (re)computed into the reused chunk buffers, attention runs on them, and the
+ * group's share of the output projection is added into the layer output.
+ * Peak intermediate memory (the workspace) grows with head_chunk, not Hq.
+ *   x        : bf16 [S][d_model], device memory.
+ *   wq       : bf16 [Hq*D][d_model]; wk, wv: bf16 [Hkv*D][d_model];
+ *   wo       : bf16 [d_model][Hq*D]  (weights as [out][in]: y = x W^T).
+ *   y        : fp32 [S][d_model] = attention(x wq^T, x wk^T, x wv^T) wo^T,
+ *              accumulated over chunks in fp32 (written, not added to).
+ *   lse      : fp32 [Hq][S] or NULL, as attn_fwd.
+ *   d_model a positive multiple of 64; other shape rules as attn_fwd; no
+ *   key/value trunks; no bias or rotary embedding.
+ * The chunk's projections are written head-major by the library's matrix
+ * kernels and rounded to bf16 (so is the attention output before the output
+ * projection).  Results are bitwise identical for every head_chunk: each fp32
+ * sum into y continues from the stored partial in a fixed order.
+ */
+size_t attn_layer_fwd_workspace_bytes(int64_t S, int32_t d_model, int32_t Hq, int32_t Hkv,
+                                      int32_t D, int32_t causal, int32_t head_chunk);
+int attn_layer_fwd(const void* x, const void* wq, const void* wk, const void* wv, const void* wo,
+                   float* y, float* lse, int64_t S, int32_t d_model, int32_t Hq, int32_t Hkv,
+                   int32_t D, int32_t causal, int32_t head_chunk, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of attn_layer_fwd for L = sum(y * dy): dy bf16 [S][d_model]; writes
+ * fp32 dx [S][d_model], dwq [Hq*D][d_model], dwk, dwv [Hkv*D][d_model], dwo
+ * [d_model][Hq*D].  Per chunk it recomputes the chunk's projections and
+ * attention output (nothing of the forward is kept but x and the weights),
+ * then dO_c = dy wo_c, dWo_c = dy^T O_c, the attention backward (attn_bwd's
+ * kernels and accumulation orders), and per GQA group, ascending,
+ * dx += dQ_g wq_g (+ dK wk + dV wv once the group's last head is done),
+ * dwq = dQ^T x, dwk = dK^T x, dwv = dV^T x.  Bitwise identical for every
+ * head_chunk.
+ */
+size_t attn_layer_bwd_workspace_bytes(int64_t S, int32_t d_model, int32_t Hq, int32_t Hkv,
+                                      int32_t D, int32_t causal, int32_t head_chunk);
+int attn_layer_bwd(const void* x, const void* wq, const void* wk, const void* wv, const void* wo,
+                   const void* dy, float* dx, float* dwq, float* dwk, float* dwv, float* dwo,
+                   int64_t S, int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D, int32_t causal,
+                   int32_t head_chunk, void* workspace, size_t workspace_bytes, void* stream);
+
 /* This thread's message for the last non-zero status ("" if none). */
 const char* attn_last_error(void);
 
@@ -211,7 +256,7 @@ int attn_set_trunk_merge(int on);
  * library launches is bracketed by two HIP timing events recorded on the
  * stream it runs on (the caller's stream); attn_timing_read waits for those
  * events and returns, for the kernel family `name` ("fwd", "merge", "pack",
- * "prep", "dkdv", "reduce", "dq"), the number of launches and their summed
+ * "prep", "dkdv", "reduce", "dq", "gemm"), the number of launches and their summed
  * duration in milliseconds since the last reset.  Events come from a pool the library
  * keeps until unload.  attn_timing_enable returns the previous setting;
  * attn_timing_read returns ATTN_OK or ATTN_EINVAL (unknown name) or ATTN_EHIP.

@@ -9,7 +9,7 @@
 // attn_fwd / attn_bwd run their argument and pointer checks unchanged.
 // Instead of launching kernels, the launch_* entry points below replay each
 // kernel's addressing: a host replica of the index arithmetic of every load
-// and store in fwd.hip, bwd.hip and aux.hip (per workgroup, wave and lane,
+// and store in fwd.hip, bwd.hip, aux.hip and gemm.hip (per workgroup, wave and lane,
 // including the clamping of ragged tiles), and hipMemcpy2DAsync checks the
 // rows it copies.  Each access must lie inside one checked region: a user
 // tensor of exactly the size the ABI states, or one workspace region of the
@@ -412,6 +412,63 @@ hipError_t launch_dq(const DqParams& p, int HD, hipStream_t) {
     return hipSuccess;
 }
 
+// gemm_kernel<A_KC, B_KC> as launched by launch_gemm: every 16-byte operand
+// chunk a 128 x 32 tile load reads, and every C row segment the epilogue (and
+// the accumulating prologue) touches
+static void gemm_operand(const uint16_t* base, int64_t rs, int64_t seg, int64_t segs, bool kc,
+                         int64_t r0, int64_t R, int64_t k0, int64_t K, const char* what) {
+    for (int idx = 0; idx < 512; ++idx) {
+        int64_t row, k;
+        if (kc) { row = r0 + idx / 4; k = k0 + (idx % 4) * 8; }
+        else { k = k0 + idx / 16; row = r0 + (idx % 16) * 8; }
+        if (row >= R || k >= K) continue;
+        const int64_t off = kc ? (k / seg) * segs + row * rs + k % seg
+                               : (row / seg) * segs + k * rs + row % seg;
+        touch(at(base, off), 16, what);
+    }
+}
+
+hipError_t launch_gemm(const GemmParams& p, bool a_kc, bool b_kc, int splits, hipStream_t) {
+    if (p.M <= 0 || p.N <= 0) return hipSuccess;
+    if ((a_kc || b_kc) && p.K % 8 != 0) return hipErrorInvalidValue;
+    if (!a_kc && p.M % 8 != 0) return hipErrorInvalidValue;
+    if (p.N % 8 != 0 || p.a_seg % 8 != 0 || p.b_seg % 8 != 0 || p.c_seg % 4 != 0 ||
+        (p.k_split > 0 && p.k_split % 32 != 0) || splits < 1 || splits > 65535)
+        return hipErrorInvalidValue;
+    const int64_t gx = (p.M + 127) / 128, gy = (p.N + 127) / 128;
+    for (int z = 0; z < splits; ++z)
+        for (int64_t bx = 0; bx < gx; ++bx)
+            for (int64_t by = 0; by < gy; ++by) {
+                const int64_t m0 = bx * 128, n0 = by * 128;
+                const int64_t kb = p.k_split > 0 ? (int64_t)z * p.k_split : 0;
+                int64_t ke = p.k_split > 0 ? kb + p.k_split : p.K;
+                ke = ke < p.K ? ke : p.K;
+                for (int64_t k0 = kb; k0 < ke; k0 += 32) {
+                    gemm_operand(p.a, p.a_rs, p.a_seg, p.a_segs, a_kc, m0, p.M, k0, ke, "gemm A");
+                    gemm_operand(p.b, p.b_rs, p.b_seg, p.b_segs, b_kc, n0, p.N, k0, ke, "gemm B");
+                }
+                const int esz = p.out_mode == kGemmBf16 ? 2 : 4;
+                const char* cz = (const char*)p.c + (int64_t)z * p.c_zs * esz;
+                for (int64_t m = m0; m < m0 + 128 && m < p.M; ++m)
+                    for (int64_t n = n0; n < n0 + 128 && n < p.N; n += 4) {
+                        const int64_t o = (n / p.c_seg) * p.c_segs + m * p.c_rs + n % p.c_seg;
+                        touch(cz + o * esz, 4 * esz, "gemm C");
+                    }
+            }
+    return hipSuccess;
+}
+
+hipError_t launch_gemm_reduce(const GemmReduceParams& p, hipStream_t) {
+    if (p.M <= 0 || p.N <= 0) return hipSuccess;
+    if (p.N % 4 != 0 || p.splits < 1) return hipErrorInvalidValue;
+    for (int64_t m = 0; m < p.M; ++m) {
+        for (int z = 0; z < p.splits; ++z)
+            touch(at(p.part, z * p.part_zs + m * p.N), p.N * 4, "gemm partial");
+        touch(at(p.out, m * p.out_rs), p.N * 4, "gemm reduce out");
+    }
+    return hipSuccess;
+}
+
 }  // namespace hc
 
 // ------------------------------------------------------------ driver
@@ -535,6 +592,83 @@ static void run_case(int64_t S, int Hq, int Hkv, int D, int causal, int hc, int6
     if (rc != ATTN_OK) fail_msg("attn_bwd returned %llu (%llu)", attn_last_error(), (size_t)rc, 0);
 }
 
+// one attn_layer_fwd + attn_layer_bwd pair on exactly sized buffers; the
+// workspace regions restate the layer's carve: the attention plan's regions,
+// then O_c (and for the backward LSE_c, dQ_c, dK_c, dV_c and the split-K
+// partials of the weight gradients)
+static void run_layer_case(int64_t S, int dm, int Hq, int Hkv, int D, int causal, int hc) {
+    char name[160];
+    snprintf(name, sizeof name, "layer S=%lld dm=%d Hq=%d Hkv=%d D=%d causal=%d hc=%d",
+             (long long)S, dm, Hq, Hkv, D, causal, hc);
+    g_case = name;
+    Buffer x, wq, wk, wv, wo, y, lse, dy, dx, dwq, dwk, dwv, dwo;
+    x.mem.resize((size_t)S * dm * 2); dy.mem.resize((size_t)S * dm * 2);
+    wq.mem.resize((size_t)Hq * D * dm * 2); wo.mem.resize((size_t)Hq * D * dm * 2);
+    wk.mem.resize((size_t)Hkv * D * dm * 2); wv.mem.resize((size_t)Hkv * D * dm * 2);
+    y.mem.resize((size_t)S * dm * 4); dx.mem.resize((size_t)S * dm * 4);
+    lse.mem.resize((size_t)Hq * S * 4);
+    dwq.mem.resize((size_t)Hq * D * dm * 4); dwo.mem.resize((size_t)Hq * D * dm * 4);
+    dwk.mem.resize((size_t)Hkv * D * dm * 4); dwv.mem.resize((size_t)Hkv * D * dm * 4);
+    const size_t nf = attn_layer_fwd_workspace_bytes(S, dm, Hq, Hkv, D, causal, hc);
+    const size_t nb = attn_layer_bwd_workspace_bytes(S, dm, Hq, Hkv, D, causal, hc);
+    if (nf == 0 || nb == 0) {
+        fail_msg("layer workspace query failed (%llu, %llu)", attn_last_error(), nf, nb);
+        return;
+    }
+    std::vector<char> fbuf(nf + 256), bbuf(nb + 256);
+    char* wf = fbuf.data() + (256 - (uintptr_t)fbuf.data() % 256) % 256;
+    char* wb = bbuf.data() + (256 - (uintptr_t)bbuf.data() % 256) % 256;
+    g_regions.clear();
+    g_allocs.clear();
+    Buffer* bufs[] = {&x, &wq, &wk, &wv, &wo, &y, &lse, &dy, &dx, &dwq, &dwk, &dwv, &dwo};
+    const char* names[] = {"x", "wq", "wk", "wv", "wo", "y", "lse", "dy", "dx", "dwq", "dwk",
+                           "dwv", "dwo"};
+    for (int i = 0; i < 13; ++i) {
+        add_region(bufs[i]->p(), bufs[i]->mem.size(), names[i]);
+        g_allocs.push_back({(uintptr_t)bufs[i]->p(), (uintptr_t)bufs[i]->p() + bufs[i]->mem.size(),
+                            false});
+    }
+    const size_t keep = g_regions.size();
+    const size_t E = (size_t)S * D * 2;
+    char msg[256];
+    for (int bwd = 0; bwd < 2; ++bwd) {
+        hc::Plan p;
+        hc::make_plan(bwd, S, Hq, Hkv, D, causal, hc, 0, &p, msg, sizeof msg);
+        char* ws = bwd ? wb : wf;
+        add_workspace(ws, p);
+        size_t off = p.total;
+        auto R = [&](size_t bytes, const char* n) {
+            add_region(ws + off, bytes, n);
+            off = hc::align_up(off + bytes);
+        };
+        R(p.hc * E, "ws O_c");
+        if (bwd) {
+            R((size_t)p.hc * S * 4, "ws LSE_c");
+            R(p.hc * E, "ws dQ_c");
+            R(p.kvc * E, "ws dK_c");
+            R(p.kvc * E, "ws dV_c");
+            const int64_t ks = (S + 32 * 8 - 1) / (32 * 8) * 32;
+            const int64_t splits = (S + ks - 1) / ks;
+            R((size_t)splits * p.hc * D * dm * 4, "ws weight-gradient partials");
+        }
+        if (off != (bwd ? nb : nf))
+            fail_msg("layer workspace carve %llu != queried %llu", "layer plan", off, bwd ? nb : nf);
+        g_allocs.push_back({(uintptr_t)ws, (uintptr_t)ws + (bwd ? nb : nf), false});
+        int rc;
+        if (!bwd)
+            rc = attn_layer_fwd(x.p(), wq.p(), wk.p(), wv.p(), wo.p(), (float*)y.p(), (float*)lse.p(),
+                                S, dm, Hq, Hkv, D, causal, hc, wf, nf, nullptr);
+        else
+            rc = attn_layer_bwd(x.p(), wq.p(), wk.p(), wv.p(), wo.p(), dy.p(), (float*)dx.p(),
+                                (float*)dwq.p(), (float*)dwk.p(), (float*)dwv.p(), (float*)dwo.p(),
+                                S, dm, Hq, Hkv, D, causal, hc, wb, nb, nullptr);
+        if (rc != ATTN_OK)
+            fail_msg("attn_layer returned %llu (%llu)", attn_last_error(), (size_t)rc, bwd);
+        g_regions.resize(keep);
+        g_allocs.pop_back();
+    }
+}
+
 int main(int argc, char** argv) {
     for (int i = 1; i < argc; ++i)
         if (strcmp(argv[i], "--plant-dkdv-overread") == 0) g_plant = true;
@@ -571,6 +705,13 @@ int main(int argc, char** argv) {
         run_case(S, 40, 8, 128, 1, 5, 256, true); ++cases;
         run_case(S, 4, 1, 128, 1, 1, 512, false); ++cases;
     }
+    // the attention layer: ragged S, groups split across chunks, D 64 / 128
+    for (int64_t S : {1, 65, 300, 513})
+        for (int hc : {1, 2, 3, 8}) {
+            run_layer_case(S, 128, 8, 2, 64, 1, hc); ++cases;
+        }
+    run_layer_case(200, 192, 4, 1, 128, 0, 2); ++cases;
+    run_layer_case(777, 256, 4, 2, 128, 1, 4); ++cases;
     printf("cases: %ld  accesses checked: %ld  failures: %ld\n", cases, g_checks, g_fails);
     return g_fails == 0 ? 0 : 1;
 }

@@ -1,0 +1,89 @@
+"""GPU parity of the attention layer (attn_layer_fwd / attn_layer_bwd: the
+chunk's Q/K/V projections recomputed per head chunk, attention, the chunk's
+share of the output projection accumulated, and the gradients) against the
+fp64 oracle on the same seeded bf16 inputs, and bitwise equality across
+head_chunk.
+
+Bar: the layer's intermediates (q, k, v, the attention output, dO, dQ, dK,
+dV) are rounded to bf16 where the attention kernels take or give them, so
+each result carries errors of order 2^-8 of its own scale (the weight
+gradients sum S terms and grow like sqrt(S)).  The attention's 2e-2 max-abs
+bar is applied relative to each output's peak magnitude when that exceeds 1:
+max|gpu - oracle| <= 2e-2 * max(1, max|oracle|).
+"""
+import numpy as np
+import pytest
+import torch
+
+from head_chunked_context_amd import attn_layer_bwd, attn_layer_fwd
+from head_chunked_context_amd.inputs import layer_inputs
+from oracle import oracle as orc
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 2e-2
+
+
+def f64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def check(name, gpu, ref):
+    ref = np.asarray(ref)
+    err = float(np.max(np.abs(f64(gpu) - ref)))
+    scale = max(1.0, float(np.max(np.abs(ref))))
+    print(f"  {name}: max-abs {err:.3e}, peak |ref| {np.max(np.abs(ref)):.3e}, "
+          f"ratio {err / scale:.3e}", flush=True)
+    assert err <= TOL * scale, (name, err, scale)
+
+
+@pytest.mark.parametrize("S,dm,Hq,Hkv,D,causal,hcs", [
+    (300, 128, 8, 2, 64, True, [8, 3, 1, 4]),     # groups split across chunks, ragged S
+    (1000, 256, 4, 2, 128, True, [4, 2, 1]),
+    (513, 192, 4, 1, 128, False, [4, 3]),         # non-causal, ragged chunk
+])
+def test_layer_matches_oracle_and_is_bitwise_across_head_chunk(S, dm, Hq, Hkv, D, causal, hcs):
+    inp = layer_inputs(S, dm, Hq, Hkv, D, 80 + S % 17)
+    d = {n: t.to(DEV) for n, t in inp.items()}
+    outs = []
+    for hc in hcs:
+        print(f"layer S={S} dm={dm} Hq={Hq} Hkv={Hkv} D={D} causal={causal} hc={hc}", flush=True)
+        y, lse = attn_layer_fwd(d["x"], d["wq"], d["wk"], d["wv"], d["wo"], Hq=Hq, Hkv=Hkv, D=D,
+                                head_chunk=hc, causal=causal, with_lse=True)
+        g = attn_layer_bwd(d["x"], d["wq"], d["wk"], d["wv"], d["wo"], d["dy"], Hq=Hq, Hkv=Hkv,
+                           D=D, head_chunk=hc, causal=causal)
+        torch.cuda.synchronize()
+        outs.append((y, lse) + tuple(g))
+    names = ("y", "lse", "dx", "dwq", "dwk", "dwv", "dwo")
+    for o in outs[1:]:
+        for a, b, n in zip(outs[0], o, names):
+            assert torch.equal(a, b), f"{n} differs bitwise across head_chunk"
+    ry, rl = orc.layer_fwd(inp["x"], inp["wq"], inp["wk"], inp["wv"], inp["wo"], Hq, Hkv, D, causal)
+    rg = orc.layer_bwd(inp["x"], inp["wq"], inp["wk"], inp["wv"], inp["wo"], inp["dy"], Hq, Hkv, D,
+                       causal)
+    y, lse, dx, dwq, dwk, dwv, dwo = outs[0]
+    check("y", y, ry)
+    lerr = float(np.max(np.abs(f64(lse) - rl)))
+    print(f"  lse: max-abs {lerr:.3e}", flush=True)
+    assert lerr <= 1e-2  # scores from bf16-rounded projections
+    for n, t in (("dx", dx), ("dwq", dwq), ("dwk", dwk), ("dwv", dwv), ("dwo", dwo)):
+        check(n, t, rg[n])
+
+
+def test_layer_projection_of_identity_weights_is_the_attention():
+    # identity projections (d_model = Hq * D, Hq = Hkv): the layer is the
+    # attention itself, so y must equal attn_fwd's output on x (bf16-exact
+    # projections, the same flash kernel) up to the output projection's
+    # bf16 -> fp32 identity product, i.e. exactly the bf16 output
+    from head_chunked_context_amd import attn_fwd
+    S, Hq, D = 640, 2, 128
+    dm = Hq * D
+    g = torch.Generator(device="cpu").manual_seed(5)
+    x = torch.randn((S, dm), generator=g).to(torch.bfloat16).to(DEV)
+    eye = torch.eye(dm, dtype=torch.bfloat16, device=DEV)
+    y, lse = attn_layer_fwd(x, eye, eye, eye, eye, Hq=Hq, Hkv=Hq, D=D, head_chunk=1, with_lse=True)
+    xs = x.view(S, Hq, D).contiguous()
+    o, l = attn_fwd(xs, xs, xs, head_chunk=1)
+    torch.cuda.synchronize()
+    assert torch.equal(y, o.float().view(S, dm))
+    assert torch.equal(lse, l)
