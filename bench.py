@@ -49,6 +49,8 @@ def parse():
                     help="skip the forward-only (no LSE) line")
     ap.add_argument("--no-host-trunks", action="store_true",
                     help="skip the pinned-host-trunk line (workload 4)")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the attention-layer line (projections around attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=12288,
                     help="tokens of the CPU-oracle sample (one GQA group)")
@@ -231,6 +233,51 @@ def run_workload(hcm, torch, w, hc, T, dev, steps, warmup, timing, kv_on_host, t
             "ws_fwd": fb, "ws_bwd": bb, "peak_intermediate": peak}
 
 
+def run_layer(hcm, torch, w, hc, dev, steps, warmup):
+    """The attention layer around the attention at workload w's shape with
+    d_model = Hq * D: forward + backward, head chunk by head chunk.  Returns
+    timings, workspace bytes and the peak intermediate device memory (torch's
+    peak-allocation delta over inputs, weights and outputs)."""
+    from head_chunked_context_amd.inputs import layer_inputs
+    S, Hq, Hkv, D = w.S, w.Hq, w.Hkv, w.D
+    dm = Hq * D
+    inp = layer_inputs(S, dm, Hq, Hkv, D, w.wid, device=dev)
+    y = torch.empty((S, dm), dtype=torch.float32, device=dev)
+    grads = [torch.empty(sh, dtype=torch.float32, device=dev)
+             for sh in ((S, dm), (Hq * D, dm), (Hkv * D, dm), (Hkv * D, dm), (dm, Hq * D))]
+    fb = hcm.layer_fwd_workspace_bytes(S, dm, Hq, Hkv, D, True, hc)
+    bb = hcm.layer_bwd_workspace_bytes(S, dm, Hq, Hkv, D, True, hc)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    ws = torch.empty(max(fb, bb), dtype=torch.uint8, device=dev)
+    a = (inp["x"], inp["wq"], inp["wk"], inp["wv"], inp["wo"])
+
+    def step():
+        hcm.attn_layer_fwd(*a, Hq=Hq, Hkv=Hkv, D=D, head_chunk=hc, out=y, workspace=ws)
+        hcm.attn_layer_bwd(*a, inp["dy"], Hq=Hq, Hkv=Hkv, D=D, head_chunk=hc, grads=grads,
+                           workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    peak = torch.cuda.max_memory_allocated(dev) - base
+    print(f"layer {w.name}: head_chunk={hc}: {ms:.1f} ms per step", file=sys.stderr, flush=True)
+    # counted work: attention 7*S^2*D*Hq, projections 2*S*dm*D*(2 Hq + 2 Hkv) forward and
+    # twice that backward (the backward's recomputation is not counted)
+    flops = 7.0 * S * S * D * Hq + 3 * 2.0 * S * dm * D * (2 * Hq + 2 * Hkv)
+    return {"head_chunk": hc, "ms_per_step": round(ms, 1),
+            "tflops": round(flops / (ms / 1e3) / 1e12, 2),
+            "workspace_bytes": {"fwd": fb, "bwd": bb}, "peak_intermediate": peak}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -360,6 +407,13 @@ def main():
             "pct_bf16_peak": round(100.0 * f4 / (r4["ms"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
             "workspace_bytes": {"fwd": r4["ws_fwd"], "bwd": r4["ws_bwd"]},
             "peak_intermediate": r4["peak_intermediate"], "pcie_inclusive": True}
+    # the attention layer around it (d_model = Hq * D): memory vs head_chunk
+    if not args.no_layer and args.workload in (2, 3):
+        torch.cuda.empty_cache()
+        rows = [run_layer(hcm, torch, w, h, dev, 1, 1) for h in (hc, Hq)]
+        line["layer"] = {"d_model": Hq * D, "settings": rows,
+                         "workspace_ratio": round(max(rows[0]["workspace_bytes"].values()) /
+                                                  max(rows[1]["workspace_bytes"].values()), 4)}
     if args.h2d_probe and T > 0:
         # host-to-device rate of one trunk's K and V (the per-trunk copy)
         hb = torch.empty(2 * T * Hkv * D, dtype=torch.bfloat16, pin_memory=True)

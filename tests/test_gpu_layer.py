@@ -41,7 +41,9 @@ def check(name, gpu, ref):
     (300, 128, 8, 2, 64, True, [8, 3, 1, 4]),     # groups split across chunks, ragged S
     (1000, 256, 4, 2, 128, True, [4, 2, 1]),
     (513, 192, 4, 1, 128, False, [4, 3]),         # non-causal, ragged chunk
+    (4096, 1024, 8, 2, 128, True, [4, 8]),        # many 128 x 128 product tiles, 8 splits
 ])
+@pytest.mark.timeout(600)
 def test_layer_matches_oracle_and_is_bitwise_across_head_chunk(S, dm, Hq, Hkv, D, causal, hcs):
     inp = layer_inputs(S, dm, Hq, Hkv, D, 80 + S % 17)
     d = {n: t.to(DEV) for n, t in inp.items()}
