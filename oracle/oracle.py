@@ -73,10 +73,11 @@ def _bind(lib):
     lib.orc_layer_fwd.argtypes = [_dp] * 5 + lshape + [_dp, _dp]
     lib.orc_layer_fwd_chunked.argtypes = [_dp] * 5 + lshape + [_int, _dp]
     lib.orc_layer_bwd.argtypes = [_dp] * 6 + lshape + [_dp] * 5
+    lib.orc_layer_fwd_rows.argtypes = [_dp] * 5 + lshape + [_lp, _i64, _dp, _dp]
     for f in (lib.orc_attn_fwd, lib.orc_attn_fwd_rows, lib.orc_attn_fwd_trunked,
               lib.orc_attn_fwd_chunked, lib.orc_attn_bwd, lib.orc_attn_dq_rows,
               lib.orc_attn_dkdv_cols, lib.orc_layer_fwd, lib.orc_layer_fwd_chunked,
-              lib.orc_layer_bwd):
+              lib.orc_layer_bwd, lib.orc_layer_fwd_rows):
         f.restype = _int
     return lib
 
@@ -248,3 +249,18 @@ def layer_bwd(x, wq, wk, wv, wo, dy, Hq: int, Hkv: int, D: int, causal: bool = T
                                  D, int(causal), _p(out["dx"]), _p(out["dwq"]), _p(out["dwk"]),
                                  _p(out["dwv"]), _p(out["dwo"])), "orc_layer_bwd")
     return out
+
+
+def layer_fwd_rows(x, wq, wk, wv, wo, rows, Hq: int, Hkv: int, D: int, causal: bool = True):
+    """The layer's output at chosen rows: (y [n, dm], lse [Hq, n]); x, the
+    weights and the whole sequence as for layer_fwd."""
+    x, wq, wk, wv, wo = (_f64(t) for t in (x, wq, wk, wv, wo))
+    rows = _rows(rows)
+    S, dm = _layer_dims(x, wq, wk, wo, Hq, Hkv, D)
+    n = rows.shape[0]
+    y = np.empty((n, dm))
+    lse = np.empty((Hq, n))
+    _check(_load().orc_layer_fwd_rows(_p(x), _p(wq), _p(wk), _p(wv), _p(wo), S, dm, Hq, Hkv, D,
+                                      int(causal), rows.ctypes.data_as(_lp), n, _p(y), _p(lse)),
+           "orc_layer_fwd_rows")
+    return y, lse

@@ -579,3 +579,36 @@ int orc_layer_bwd(const double* x, const double* wq, const double* wk, const dou
     free(q); free(k); free(v); free(o); free(l); free(dov); free(dq); free(dk); free(dv);
     return rc;
 }
+
+/*
+ * The layer's output for chosen rows: y_rows [n][dm] at positions rows[0..n)
+ * (and lse_rows [Hq][n]).  The query projections of those rows and the key /
+ * value projections of every position are taken from x (the whole
+ * sequence); then each row's attention and its output projection, as in
+ * orc_layer_fwd.
+ */
+int orc_layer_fwd_rows(const double* x, const double* wq, const double* wk, const double* wv,
+                       const double* wo, i64 S, int dm, int Hq, int Hkv, int D, int causal,
+                       const i64* rows, i64 n, double* y_rows, double* lse_rows) {
+    if (bad_shape(S, Hq, Hkv, D, causal) || dm < 1 || n < 0) return -1;
+    for (i64 r = 0; r < n; ++r)
+        if (rows[r] < 0 || rows[r] >= S) return -1;
+    const int nq = Hq * D, nk = Hkv * D;
+    double* xr = (double*)malloc(sizeof(double) * (size_t)(n ? n : 1) * dm);
+    double* q = (double*)malloc(sizeof(double) * (size_t)(n ? n : 1) * nq);
+    double* k = (double*)malloc(sizeof(double) * (size_t)S * nk);
+    double* v = (double*)malloc(sizeof(double) * (size_t)S * nk);
+    double* o = (double*)malloc(sizeof(double) * (size_t)(n ? n : 1) * nq);
+    int rc = (xr && q && k && v && o) ? 0 : -1;
+    if (rc == 0) {
+        for (i64 r = 0; r < n; ++r)
+            memcpy(xr + (size_t)r * dm, x + (size_t)rows[r] * dm, sizeof(double) * (size_t)dm);
+        matmul_nt(xr, wq, n, dm, nq, q);
+        matmul_nt(x, wk, S, dm, nk, k);
+        matmul_nt(x, wv, S, dm, nk, v);
+        rc = orc_attn_fwd_rows(q, rows, n, k, v, S, Hq, Hkv, D, causal, o, lse_rows);
+    }
+    if (rc == 0) matmul_nt(o, wo, n, nq, dm, y_rows);
+    free(xr); free(q); free(k); free(v); free(o);
+    return rc;
+}

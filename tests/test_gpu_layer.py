@@ -89,3 +89,35 @@ def test_layer_projection_of_identity_weights_is_the_attention():
     torch.cuda.synchronize()
     assert torch.equal(y, o.float().view(S, dm))
     assert torch.equal(lse, l)
+
+
+@pytest.mark.timeout(900)
+def test_llama3_8b_layer_full_size_sampled_rows_and_head_chunks():
+    # the Llama3-8B attention layer at S = 32768 (d_model 4096, 32/8 heads,
+    # D 128): head_chunk 4 (one GQA group) and 32 give the same bits for y and
+    # every gradient; y and LSE on sampled rows against the oracle (its cost
+    # is the key/value projections of the whole sequence, ~1e12 fp64 FLOP)
+    S, Hq, Hkv, D = 32768, 32, 8, 128
+    dm = Hq * D
+    inp = layer_inputs(S, dm, Hq, Hkv, D, 2, device=DEV)
+    outs = []
+    for hc in (4, 32):
+        print(f"layer S={S} dm={dm} hc={hc}", flush=True)
+        y, lse = attn_layer_fwd(inp["x"], inp["wq"], inp["wk"], inp["wv"], inp["wo"], Hq=Hq,
+                                Hkv=Hkv, D=D, head_chunk=hc, with_lse=True)
+        g = attn_layer_bwd(inp["x"], inp["wq"], inp["wk"], inp["wv"], inp["wo"], inp["dy"], Hq=Hq,
+                           Hkv=Hkv, D=D, head_chunk=hc)
+        torch.cuda.synchronize()
+        outs.append((y, lse) + tuple(g))
+    for a, b, n in zip(outs[0], outs[1], ("y", "lse", "dx", "dwq", "dwk", "dwv", "dwo")):
+        assert torch.equal(a, b), f"{n} differs bitwise between head_chunk 4 and 32"
+        assert torch.isfinite(a).all(), f"{n} has non-finite values"
+    rows = np.array([0, 1, 127, 128, 4095, S // 2, S - 2, S - 1])
+    cpu = {n: t.cpu() for n, t in inp.items()}
+    ry, rl = orc.layer_fwd_rows(cpu["x"], cpu["wq"], cpu["wk"], cpu["wv"], cpu["wo"], rows, Hq, Hkv,
+                                D, True)
+    y, lse = outs[0][0], outs[0][1]
+    check("y rows", y[rows], ry)
+    lerr = float(np.max(np.abs(f64(lse[:, rows]) - rl)))
+    print(f"  lse rows: max-abs {lerr:.3e}", flush=True)
+    assert lerr <= 1e-2

@@ -134,3 +134,15 @@ def test_layer_is_linear_in_the_output_projection_and_dy():
     g2 = orc.layer_bwd(a["x"], a["wq"], a["wk"], a["wv"], a["wo"], -2 * a["dy"], Hq, Hkv, D, True)
     for n in g1:
         assert np.max(np.abs(-2 * g1[n] - g2[n])) <= 1e-11 * max(1.0, np.max(np.abs(g1[n])))
+
+
+def test_layer_rows_match_the_full_layer():
+    S, dm, Hq, Hkv, D = 40, 16, 4, 2, 4
+    a = layer_inputs(S, dm, Hq, Hkv, D, seed=17)
+    rows = np.array([0, 1, 7, 20, 39])
+    for causal in (True, False):
+        y, lse = orc.layer_fwd(a["x"], a["wq"], a["wk"], a["wv"], a["wo"], Hq, Hkv, D, causal)
+        yr, lr = orc.layer_fwd_rows(a["x"], a["wq"], a["wk"], a["wv"], a["wo"], rows, Hq, Hkv, D,
+                                    causal)
+        assert np.max(np.abs(yr - y[rows])) <= 1e-13
+        assert np.max(np.abs(lr - lse[:, rows])) <= 1e-13
