@@ -81,7 +81,7 @@ __device__ __forceinline__ void dkdv_p_ds(const f32x16 (&sacc)[NQB], const f32x1
     }
 }
 
-template <int HD, bool RUNS>
+template <int HD, bool RUNS, bool GLOOP>
 __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
     constexpr int BQ = 64, WQ = 32, WK = 32, BNK = 128;
     constexpr int NS = HD / 16, NDB = HD / 32;
@@ -97,18 +97,22 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
     const int kw = wave & 3;   // key block of the wave (32 keys)
     const int rh = wave >> 2;  // half of every 64-row query tile the wave takes
 
-    // work item = key tile * nh + head, key tiles ascending: heaviest first
-    // (key tile 0 sees every query tile when causal).
+    // work item = key tile * units + unit, key tiles ascending: heaviest
+    // first (key tile 0 sees every query tile when causal).  A unit is a
+    // query head of the chunk (per-head schedule) or a kv head of the chunk
+    // (group loop).
     // Workgroup b runs on die b % 8, and each die's L2 serves its resident
-    // workgroups' Q/dO rows.  When the head count is a multiple of 4, plain
-    // order already gives each die one or two heads at key tiles 2 or 1
-    // apart; otherwise (1, 2, 5 ... heads: RUNS) each die takes runs of 32
+    // workgroups' Q/dO rows.  When the unit count is a multiple of 4, plain
+    // order already gives each die one or two units at key tiles 2 or 1
+    // apart; otherwise (1, 2, 5 ... units: RUNS) each die takes runs of 32
     // consecutive items per window of 8 x 32, in a snake order across
     // windows (a last partial window keeps plain order), so that a die's
     // workgroups stream neighbouring key tiles of few heads.  Measured at
-    // S = 262144: dK/dV 5% faster with 1 head, 3.6% with 2, 4% with 5 (of
-    // 40 / 8 kv heads); 4 and 8 heads are 4% faster in plain order.
-    int hl;
+    // S = 262144 (per-head schedule): dK/dV 5% faster with 1 head, 3.6% with
+    // 2, 4% with 5 (of 40 / 8 kv heads); 4 and 8 heads are 4% faster in
+    // plain order.
+    const int units = GLOOP ? p.nkv : p.nh;
+    int unit;
     int64_t kt;
     if constexpr (RUNS) {
         constexpr unsigned RUN = 32, WIN = 8 * RUN;
@@ -118,16 +122,27 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
             const unsigned x = item % 8, o = (item / 8) % RUN;
             item = w * WIN + ((w & 1) ? 7 - x : x) * RUN + o;
         }
-        hl = (int)(item % (unsigned)p.nh);
-        kt = (int64_t)(item / (unsigned)p.nh);
+        unit = (int)(item % (unsigned)units);
+        kt = (int64_t)(item / (unsigned)units);
     } else {
-        hl = blockIdx.x % p.nh;
-        kt = (int64_t)(blockIdx.x / p.nh);
+        unit = blockIdx.x % units;
+        kt = (int64_t)(blockIdx.x / units);
+    }
+    // the unit's kv head (local) and its query heads [hb, he) (local to the chunk)
+    int kvl, hb, he;
+    if constexpr (GLOOP) {
+        kvl = unit;
+        const int gh0 = (p.kv_base + kvl) * p.group - p.h0;
+        hb = gh0 < 0 ? 0 : gh0;
+        he = gh0 + p.group > p.nh ? p.nh : gh0 + p.group;
+    } else {
+        hb = unit;
+        he = unit + 1;
+        kvl = (p.h0 + unit) / p.group - p.kv_base;
     }
     const int64_t j0 = kt * BNK;                  // first key of the workgroup
     const int64_t wj0 = j0 + kw * WK;             // first key of this wave
     const int64_t myk = wj0 + l32;                // this lane's key
-    const int kvl = (p.h0 + hl) / p.group - p.kv_base;
 
     // the workgroup's 128 keys of K (waves 0-3) and V (waves 4-7) go to LDS
     // (rows past nk repeat the last key; their P is masked to zero).  When
@@ -150,6 +165,24 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
         dk[db] = f32x16{};
         dv[db] = f32x16{};
     }
+    // a group continued from the previous chunk resumes from its row half's sums
+    if (GLOOP && kvl == p.carry_kv_in && myk < p.nk) {
+        const float* ck = p.carry_in_k + rh * p.carry_hs + myk * HD;
+        const float* cv = p.carry_in_v + rh * p.carry_hs + myk * HD;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(ck + db * 32 + g4 * 8 + hi * 4);
+                const f32x4 y = *reinterpret_cast<const f32x4*>(cv + db * 32 + g4 * 8 + hi * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    dk[db][g4 * 4 + e] = x[e];
+                    dv[db][g4 * 4 + e] = y[e];
+                }
+            }
+        }
+    }
 
     // query tiles: causal rows start at the workgroup's first key position
     const int64_t nqt = (p.nq + BQ - 1) / BQ;
@@ -158,28 +191,27 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
         const int64_t first = p.k_pos0 + j0;
         qt0 = first >= p.nq ? nqt : first / BQ;
     }
+    // steps: heads hb..he-1 ascending, each over query tiles qt0..nqt-1 ascending
     const int64_t nsteps = j0 < p.nk ? nqt - qt0 : 0;
+    const int64_t total = nsteps * (he - hb);
 
-    const uint16_t* qh = p.q + (int64_t)hl * p.q_hs;
-    const uint16_t* oh = p.dO + (int64_t)hl * p.do_hs;
-    const float* lseh = p.nlse2 + (int64_t)hl * p.nlse2_hs;
-    const float* delh = p.ndelta + (int64_t)hl * p.ndelta_hs;
-    // one step = Q (waves 0-3) and dO (waves 4-7) rows [i0, i0 + 64) plus
-    // their LSE (wave 0) and Delta (wave 4), straight into LDS buffer b
+    // one step = Q (waves 0-3) and dO (waves 4-7) rows [i0, i0 + 64) of head
+    // h plus their LSE (wave 0) and Delta (wave 4), straight into LDS buffer b
     // each wave loads one contiguous run of the tile's rows: with the
     // interleaved order this kernel ran 7-12% slower at S = 262144 with 32
     // heads per launch (the forward and dQ kernels showed no difference)
     const TileDma64<HD, false> dqo(rh == 0 ? p.q_rs : p.do_rs, kw, lane);
-    auto issue_step = [&](int64_t n, int b) {
-        const int64_t i0 = (qt0 + n) * BQ;
+    auto issue_step = [&](int h, int64_t s, int b) {
+        const int64_t i0 = (qt0 + s) * BQ;
         if (rh == 0)
-            dqo.load(smem[b][0], qh + i0 * p.q_rs, p.q_rs, p.nq - i0, kw, lane);
+            dqo.load(smem[b][0], p.q + (int64_t)h * p.q_hs + i0 * p.q_rs, p.q_rs, p.nq - i0, kw, lane);
         else
-            dqo.load(smem[b][1], oh + i0 * p.do_rs, p.do_rs, p.nq - i0, kw, lane);
-        if (wave == 0) direct_vec64(s_nlse2[b], lseh + i0, p.nq - i0, lane);
-        if (wave == 4) direct_vec64(s_ndelta[b], delh + i0, p.nq - i0, lane);
+            dqo.load(smem[b][1], p.dO + (int64_t)h * p.do_hs + i0 * p.do_rs, p.do_rs, p.nq - i0, kw,
+                     lane);
+        if (wave == 0) direct_vec64(s_nlse2[b], p.nlse2 + (int64_t)h * p.nlse2_hs + i0, p.nq - i0, lane);
+        if (wave == 4) direct_vec64(s_ndelta[b], p.ndelta + (int64_t)h * p.ndelta_hs + i0, p.nq - i0, lane);
     };
-    if (nsteps > 0) issue_step(0, 0);
+    if (total > 0) issue_step(hb, 0, 0);
     wait_vm_loads();
     __syncthreads();
 
@@ -187,10 +219,19 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
     // positions relative to this wave's first key, in 32-bit
     const int64_t wkpos = p.k_pos0 + wj0;
     const int krel = l32;
-    for (int64_t n = 0; n < nsteps; ++n) {
+    // cursor (head, query step) of step n, and of step n + 1
+    int h_cur = hb;
+    int64_t s_cur = 0;
+    for (int64_t n = 0; n < total; ++n) {
         const int buf = (int)(n & 1);
-        if (n + 1 < nsteps) issue_step(n + 1, buf ^ 1);
-        const int64_t r0 = (qt0 + n) * BQ + rh * WQ;  // first row of this wave
+        int h_nxt = h_cur;
+        int64_t s_nxt = s_cur + 1;
+        if (s_nxt == nsteps) {
+            s_nxt = 0;
+            ++h_nxt;
+        }
+        if (n + 1 < total) issue_step(h_nxt, s_nxt, buf ^ 1);
+        const int64_t r0 = (qt0 + s_cur) * BQ + rh * WQ;  // first row of this wave
         // a wave works on the tile only if some of its rows sees one of its keys
         const bool live = wj0 < p.nk && r0 < p.nq && (!p.causal || r0 + WQ - 1 >= wkpos);
         if (live) {
@@ -243,8 +284,32 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
                 }
             }
         }
+        h_cur = h_nxt;
+        s_cur = s_nxt;
         wait_vm_loads();
         __syncthreads();
+    }
+
+    // group continuing in the next chunk: each row half leaves its own sums
+    if (GLOOP && kvl == p.carry_kv_out) {
+        if (myk >= p.nk) return;
+        float* ck = p.carry_out_k + rh * p.carry_hs + myk * HD;
+        float* cv = p.carry_out_v + rh * p.carry_hs + myk * HD;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 x, y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[e] = dk[db][g4 * 4 + e];
+                    y[e] = dv[db][g4 * 4 + e];
+                }
+                *reinterpret_cast<f32x4*>(ck + db * 32 + g4 * 8 + hi * 4) = x;
+                *reinterpret_cast<f32x4*>(cv + db * 32 + g4 * 8 + hi * 4) = y;
+            }
+        }
+        return;
     }
 
     // the two waves of a key block hold partial sums over the two row halves:
@@ -270,22 +335,47 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
     }
     __syncthreads();
     if (rh == 1 || myk >= p.nk) return;
-    float* ak = p.part_k + ((int64_t)hl * p.nk + myk) * HD;
-    float* av = p.part_v + ((int64_t)hl * p.nk + myk) * HD;
+    if constexpr (GLOOP) {
+        // the group is complete: bf16(scale * dK), bf16(dV)
+        uint16_t* ok = p.dk + (int64_t)kvl * p.dk_hs + myk * p.dk_rs;
+        uint16_t* ov = p.dv + (int64_t)kvl * p.dk_hs + myk * p.dk_rs;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+        for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 ok = xk[(db * 4 + g4) * 64 + lane];
-            const f32x4 ov = xv[(db * 4 + g4) * 64 + lane];
-            f32x4 x, y;
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 uk = xk[(db * 4 + g4) * 64 + lane];
+                const f32x4 uv = xv[(db * 4 + g4) * 64 + lane];
+                f32x4 x, y;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x[e] = dk[db][g4 * 4 + e] + ok[e];
-                y[e] = dv[db][g4 * 4 + e] + ov[e];
+                for (int e = 0; e < 4; ++e) {
+                    x[e] = dk[db][g4 * 4 + e] + uk[e];
+                    y[e] = dv[db][g4 * 4 + e] + uv[e];
+                }
+                const bf16x2 k0 = to_bf16x2(x[0] * p.scale, x[1] * p.scale);
+                const bf16x2 k1 = to_bf16x2(x[2] * p.scale, x[3] * p.scale);
+                const bf16x2 v0 = to_bf16x2(y[0], y[1]), v1 = to_bf16x2(y[2], y[3]);
+                *reinterpret_cast<bf16x4*>(ok + db * 32 + g4 * 8 + hi * 4) = bf16x4{k0[0], k0[1], k1[0], k1[1]};
+                *reinterpret_cast<bf16x4*>(ov + db * 32 + g4 * 8 + hi * 4) = bf16x4{v0[0], v0[1], v1[0], v1[1]};
             }
-            *reinterpret_cast<f32x4*>(ak + db * 32 + g4 * 8 + hi * 4) = x;
-            *reinterpret_cast<f32x4*>(av + db * 32 + g4 * 8 + hi * 4) = y;
+        }
+    } else {
+        float* ak = p.part_k + ((int64_t)hb * p.nk + myk) * HD;
+        float* av = p.part_v + ((int64_t)hb * p.nk + myk) * HD;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 ok = xk[(db * 4 + g4) * 64 + lane];
+                const f32x4 ov = xv[(db * 4 + g4) * 64 + lane];
+                f32x4 x, y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[e] = dk[db][g4 * 4 + e] + ok[e];
+                    y[e] = dv[db][g4 * 4 + e] + ov[e];
+                }
+                *reinterpret_cast<f32x4*>(ak + db * 32 + g4 * 8 + hi * 4) = x;
+                *reinterpret_cast<f32x4*>(av + db * 32 + g4 * 8 + hi * 4) = y;
+            }
         }
     }
 }
@@ -551,21 +641,23 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
 }
 
 hipError_t launch_dkdv(const DkdvParams& p, int D, hipStream_t st) {
-    if (p.nk <= 0 || p.nh <= 0) return hipSuccess;
-    const int64_t blocks = (p.nk + kDkdvBlockN - 1) / kDkdvBlockN * p.nh;
+    const int units = p.group_loop ? p.nkv : p.nh;
+    if (p.nk <= 0 || units <= 0) return hipSuccess;
+    const int64_t blocks = (p.nk + kDkdvBlockN - 1) / kDkdvBlockN * units;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    // die-aware runs of work items unless the head count is a multiple of 4
-    const bool runs = p.nh % 4 != 0;
-    if (D == 128 && runs)
-        hipLaunchKernelGGL((dkdv_kernel<128, true>), dim3((unsigned)blocks), dim3(512), 0, st, p);
-    else if (D == 128)
-        hipLaunchKernelGGL((dkdv_kernel<128, false>), dim3((unsigned)blocks), dim3(512), 0, st, p);
-    else if (D == 64 && runs)
-        hipLaunchKernelGGL((dkdv_kernel<64, true>), dim3((unsigned)blocks), dim3(512), 0, st, p);
-    else if (D == 64)
-        hipLaunchKernelGGL((dkdv_kernel<64, false>), dim3((unsigned)blocks), dim3(512), 0, st, p);
-    else
-        return hipErrorInvalidValue;
+    // die-aware runs of work items unless the unit count is a multiple of 4
+    const bool runs = units % 4 != 0;
+    const dim3 grid((unsigned)blocks), block(512);
+#define HC_DKDV(HD, R, G) hipLaunchKernelGGL((dkdv_kernel<HD, R, G>), grid, block, 0, st, p)
+    if (D != 128 && D != 64) return hipErrorInvalidValue;
+    if (p.group_loop) {
+        if (D == 128) { if (runs) HC_DKDV(128, true, true); else HC_DKDV(128, false, true); }
+        else { if (runs) HC_DKDV(64, true, true); else HC_DKDV(64, false, true); }
+    } else {
+        if (D == 128) { if (runs) HC_DKDV(128, true, false); else HC_DKDV(128, false, false); }
+        else { if (runs) HC_DKDV(64, true, false); else HC_DKDV(64, false, false); }
+    }
+#undef HC_DKDV
     return hipGetLastError();
 }
 

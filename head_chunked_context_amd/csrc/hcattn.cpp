@@ -40,6 +40,7 @@ namespace {
 thread_local char g_err[512];
 std::atomic<int> g_single_stream{0};
 std::atomic<int> g_trunk_merge{0};
+std::atomic<int64_t> g_group_loop_min_s{hc::kGroupLoopMinS};
 
 int fail(int code, const char* fmt, ...) {
     va_list ap;
@@ -129,7 +130,8 @@ struct Common {
 int plan_or_fail(bool bwd, int64_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t causal,
                  int32_t head_chunk, int64_t kv_trunk, hc::Plan* pl) {
     char msg[256];
-    const int r = hc::make_plan(bwd, S, Hq, Hkv, D, causal, head_chunk, kv_trunk, pl, msg, sizeof msg);
+    const int r = hc::make_plan(bwd, S, Hq, Hkv, D, causal, head_chunk, kv_trunk, pl, msg,
+                                sizeof msg, g_group_loop_min_s.load());
     if (r == -1) return fail(ATTN_EINVAL, "%s", msg);
     if (r == -2) return fail(ATTN_EUNSUPPORTED, "%s", msg);
     return ATTN_OK;
@@ -419,6 +421,11 @@ hc::DkdvParams dkdv_params(const Common& c, const hc::Chunk& ch, const BwdIO& io
     d.scale_log2 = c.scale_log2;
     d.part_k = reinterpret_cast<float*>(c.ws + p.part_k);
     d.part_v = reinterpret_cast<float*>(c.ws + p.part_v);
+    d.group_loop = p.group_loop ? 1 : 0;
+    d.nkv = ch.nkv;
+    d.carry_kv_in = -1;
+    d.carry_kv_out = -1;
+    d.scale = c.scale;
     return d;
 }
 
@@ -449,6 +456,42 @@ hc::DkdvReduceParams reduce_params(const Common& c, const hc::Chunk& ch, int ci,
     r.dk = dk; r.dv = dv; r.dk_rs = rs; r.dk_hs = hs;
     r.scale = c.scale;
     return r;
+}
+
+// dK/dV of chunk ci over keys [kr0, kr0 + nk) held in (kk, vv): bf16 results
+// of the kv heads whose group ends in this chunk go to (dk, dv) with strides
+// (rs, hs); a group that continues leaves fp32 sums in a carry slot.
+// Group-loop schedule: one launch writes both.  Per-head schedule: per-head
+// partials, then the ordered reduce over the group's heads.
+int dkdv_run(Common& c, const hc::Chunk& ch, int ci, const BwdIO& io, const uint16_t* kk,
+             const uint16_t* vv, int64_t k_rs, int64_t k_hs, int64_t kr0, int64_t nk,
+             uint16_t* dk, uint16_t* dv, int64_t rs, int64_t hs) {
+    const hc::Plan& p = c.pl;
+    const int D = p.D;
+    hc::DkdvParams d = dkdv_params(c, ch, io, kk, vv, k_rs, k_hs, kr0, nk);
+    if (!p.group_loop) {
+        LAUNCH(K_DKDV, hc::launch_dkdv(d, D, c.st));
+        hc::DkdvReduceParams rd = reduce_params(c, ch, ci, kr0, nk, dk, dv, rs, hs);
+        LAUNCH_PASS(K_REDUCE, rd, hc::launch_dkdv_reduce(rd, c.st));
+        return ATTN_OK;
+    }
+    // carries: [2][S][D] fp32 per slot (lower, upper row halves), at this
+    // launch's first key
+    const int in_s = p.carry_in_slot(ci), out_s = p.carry_out_slot(ci);
+    d.carry_hs = p.S * D;
+    if (in_s >= 0) {
+        d.carry_in_k = reinterpret_cast<const float*>(c.ws + p.carry_k[in_s]) + (size_t)kr0 * D;
+        d.carry_in_v = reinterpret_cast<const float*>(c.ws + p.carry_v[in_s]) + (size_t)kr0 * D;
+        d.carry_kv_in = 0;
+    }
+    if (out_s >= 0) {
+        d.carry_out_k = reinterpret_cast<float*>(c.ws + p.carry_k[out_s]) + (size_t)kr0 * D;
+        d.carry_out_v = reinterpret_cast<float*>(c.ws + p.carry_v[out_s]) + (size_t)kr0 * D;
+        d.carry_kv_out = ch.nkv - 1;
+    }
+    d.dk = dk; d.dv = dv; d.dk_rs = rs; d.dk_hs = hs;
+    LAUNCH(K_DKDV, hc::launch_dkdv(d, D, c.st));
+    return ATTN_OK;
 }
 
 int bwd_chunk_prep(Common& c, const hc::Chunk& ch, const BwdIO& io) {
@@ -505,12 +548,10 @@ int bwd_untrunked(Common& c, const BwdIO& io) {
         LAUNCH_PASS(K_PACK, pk, hc::launch_pack(pk, c.st));
         pk = {v + (size_t)ch.kv0 * D, (int64_t)p.Hkv * D, D, Vc, D, S * D, ch.nkv, S, D};
         LAUNCH_PASS(K_PACK, pk, hc::launch_pack(pk, c.st));
-        hc::DkdvParams dk = dkdv_params(c, ch, io, Kc, Vc, D, S * D, 0, S);
-        LAUNCH(K_DKDV, hc::launch_dkdv(dk, D, c.st));
-        hc::DkdvReduceParams rd = reduce_params(
-            c, ch, ci, 0, S, static_cast<uint16_t*>(io.dk) + (size_t)ch.kv0 * D,
-            static_cast<uint16_t*>(io.dv) + (size_t)ch.kv0 * D, (int64_t)p.Hkv * D, D);
-        LAUNCH_PASS(K_REDUCE, rd, hc::launch_dkdv_reduce(rd, c.st));
+        r = dkdv_run(c, ch, ci, io, Kc, Vc, D, S * D, 0, S,
+                     static_cast<uint16_t*>(io.dk) + (size_t)ch.kv0 * D,
+                     static_cast<uint16_t*>(io.dv) + (size_t)ch.kv0 * D, (int64_t)p.Hkv * D, D);
+        if (r) return r;
         hc::DqParams dq = dq_params(c, ch, io, Kc, Vc, D, S * D, 0, S);
         LAUNCH(K_DQ, hc::launch_dq(dq, D, c.st));
     }
@@ -537,28 +578,25 @@ int bwd_trunked(Common& c, const BwdIO& io) {
             if (r) return r;
             const uint16_t* kk = reinterpret_cast<const uint16_t*>(c.ws + p.ring_k[slot]);
             const uint16_t* vv = reinterpret_cast<const uint16_t*>(c.ws + p.ring_v[slot]);
-            hc::DkdvParams dk = dkdv_params(c, ch, io, kk, vv, (int64_t)ch.nkv * D, D, kr0, nk);
-            LAUNCH(K_DKDV, hc::launch_dkdv(dk, D, c.st));
             int ss = -1;
-            hc::DkdvReduceParams rd;
             if (io.kv_host) {
                 ss = nstage & 1;
                 Device* d = c.dev;
                 if (stage_uses[ss] > 0) HIPCHK(hipStreamWaitEvent(c.st, d->ev[EV_SFREE0 + ss], 0));
-                rd = reduce_params(c, ch, ci, kr0, nk, reinterpret_cast<uint16_t*>(c.ws + p.stage_k[ss]),
-                                   reinterpret_cast<uint16_t*>(c.ws + p.stage_v[ss]),
-                                   (int64_t)ch.nkv * D, D);
+                r = dkdv_run(c, ch, ci, io, kk, vv, (int64_t)ch.nkv * D, D, kr0, nk,
+                             reinterpret_cast<uint16_t*>(c.ws + p.stage_k[ss]),
+                             reinterpret_cast<uint16_t*>(c.ws + p.stage_v[ss]),
+                             (int64_t)ch.nkv * D, D);
             } else {
-                rd = reduce_params(
-                    c, ch, ci, kr0, nk,
-                    static_cast<uint16_t*>(io.dk) + ((size_t)kr0 * p.Hkv + ch.kv0) * D,
-                    static_cast<uint16_t*>(io.dv) + ((size_t)kr0 * p.Hkv + ch.kv0) * D,
-                    (int64_t)p.Hkv * D, D);
+                r = dkdv_run(c, ch, ci, io, kk, vv, (int64_t)ch.nkv * D, D, kr0, nk,
+                             static_cast<uint16_t*>(io.dk) + ((size_t)kr0 * p.Hkv + ch.kv0) * D,
+                             static_cast<uint16_t*>(io.dv) + ((size_t)kr0 * p.Hkv + ch.kv0) * D,
+                             (int64_t)p.Hkv * D, D);
             }
-            LAUNCH_PASS(K_REDUCE, rd, hc::launch_dkdv_reduce(rd, c.st));
-            // the finished dK/dV rows leave as soon as the reduce has staged
-            // them, so their copy, and the next trunk's load queued behind it
-            // on the copy stream, run while dQ of this trunk computes
+            if (r) return r;
+            // the finished dK/dV rows leave as soon as they are staged, so
+            // their copy, and the next trunk's load queued behind it on the
+            // copy stream, run while dQ of this trunk computes
             if (io.kv_host && nfin > 0) {
                 Device* d = c.dev;
                 HIPCHK(hipEventRecord(d->ev[EV_STAGED0 + ss], c.st));
@@ -798,10 +836,7 @@ int layer_bwd_run(Common& c, const LayerPlan& L, const uint16_t* x, const uint16
         LAUNCH_PASS(K_PREP, pr, hc::launch_prep(pr, c.st));
         BwdIO io{};
         io.dq = dQc;
-        hc::DkdvParams dk = dkdv_params(c, ch, io, Kc, Vc, D, S * D, 0, S);
-        LAUNCH(K_DKDV, hc::launch_dkdv(dk, D, c.st));
-        hc::DkdvReduceParams rd = reduce_params(c, ch, ci, 0, S, dKc, dVc, D, S * D);
-        LAUNCH_PASS(K_REDUCE, rd, hc::launch_dkdv_reduce(rd, c.st));
+        if ((r = dkdv_run(c, ch, ci, io, Kc, Vc, D, S * D, 0, S, dKc, dVc, D, S * D))) return r;
         hc::DqParams dq = dq_params(c, ch, io, Kc, Vc, D, S * D, 0, S);
         dq.dq = dQc; dq.dq_rs = D; dq.dq_hs = S * D;
         LAUNCH(K_DQ, hc::launch_dq(dq, D, c.st));
@@ -887,7 +922,7 @@ int attn_pick_kv_trunk(int64_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t ca
     int64_t t = 0;
     const int r = hc::pick_kv_trunk(S, Hq, Hkv, D, causal, head_chunk, kv_on_host != 0,
                                     with_backward != 0, budget_bytes, link, flops, cus, &t, msg,
-                                    sizeof msg);
+                                    sizeof msg, g_group_loop_min_s.load());
     if (r == -1) return fail(ATTN_EINVAL, "%s", msg);
     if (r == -2) return fail(ATTN_EUNSUPPORTED, "%s", msg);
     if (r == -3) return fail(ATTN_EWORKSPACE, "%s", msg);
@@ -977,6 +1012,10 @@ const char* attn_last_error(void) { return g_err; }
 int attn_set_single_stream(int on) { return g_single_stream.exchange(on ? 1 : 0); }
 
 int attn_set_trunk_merge(int on) { return g_trunk_merge.exchange(on ? 1 : 0); }
+
+int64_t attn_set_group_loop_min_s(int64_t min_s) {
+    return g_group_loop_min_s.exchange(min_s > 0 ? min_s : hc::kGroupLoopMinS);
+}
 
 size_t attn_layer_fwd_workspace_bytes(int64_t S, int32_t d_model, int32_t Hq, int32_t Hkv,
                                       int32_t D, int32_t causal, int32_t head_chunk) {

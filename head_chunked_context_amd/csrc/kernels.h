@@ -83,11 +83,20 @@ struct PrepParams {
     int D;
 };
 
-// dK/dV partials of one chunk over a key range: one workgroup per (key tile
-// of 128 keys, query head of the chunk).  Each head's contribution over its
-// query tiles (ascending) is written in fp32, unscaled, to part_k/part_v
-// [nh][nk][D]; dkdv_reduce then adds the heads of each group in ascending
-// order.  Rows of part_* are keys of this launch (0..nk).
+// dK/dV of one chunk over a key range, in one of two schedules:
+//  * per head (group_loop = 0): one workgroup per (key tile of 128 keys,
+//    query head of the chunk).  Each head's contribution over its query
+//    tiles (ascending) is written in fp32, unscaled, to part_k/part_v
+//    [nh][nk][D]; dkdv_reduce then adds the heads of each group in ascending
+//    order.  Rows of part_* are keys of this launch (0..nk).
+//  * group loop (group_loop = 1): one workgroup per (key tile, kv head of the
+//    chunk) walks the chunk's heads of that group, ascending, each over its
+//    query tiles, ascending, into the same fp32 registers.  The two row
+//    halves of every key block keep separate sums; a group that continues in
+//    the next chunk leaves both in carry_out ([2][..][D]: lower half, then
+//    upper half carry_hs elements further) and resumes from carry_in; a
+//    finished group writes bf16(scale * (lower + upper)) to dk and
+//    bf16(lower + upper) to dv (strides dk_rs, dk_hs), with no reduce pass.
 struct DkdvParams {
     const uint16_t* q;  int64_t q_rs, q_hs;    // chunk query heads (local 0..nh)
     const uint16_t* dO; int64_t do_rs, do_hs;
@@ -100,7 +109,15 @@ struct DkdvParams {
     int64_t nk, k_pos0;                        // keys of this launch, position of key 0
     int causal;
     float scale_log2;
-    float* part_k; float* part_v;              // [nh][nk][D] fp32
+    float* part_k; float* part_v;              // [nh][nk][D] fp32 (per-head schedule)
+    // group-loop schedule
+    int group_loop;
+    int nkv;                                   // kv heads of the chunk
+    const float* carry_in_k; const float* carry_in_v; int carry_kv_in;  // local kv head or -1
+    float* carry_out_k; float* carry_out_v; int carry_kv_out;
+    int64_t carry_hs;                          // elements from a carry's lower to upper half
+    uint16_t* dk; uint16_t* dv; int64_t dk_rs, dk_hs;
+    float scale;
 };
 
 // Ordered sum over a group's heads: for each kv head of the chunk and key,

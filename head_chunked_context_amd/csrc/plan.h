@@ -18,6 +18,15 @@ namespace hc {
 
 constexpr int64_t kTrunkGranule = 256;  // trunk length must be a multiple
 constexpr size_t kAlign = 256;
+// Sequences at least this long take the group-loop dK/dV schedule: one
+// workgroup per (128-key tile, kv head) walks the chunk's heads of that
+// group itself, keeping dK/dV in registers and writing bf16 dK/dV directly
+// (no per-head fp32 partials, no reduce pass).  Shorter sequences have too
+// few key tiles to spread that longer work over the compute units and keep
+// one workgroup per (key tile, query head) with per-head partials.  The
+// choice depends on S only, so every head_chunk and kv_trunk at one S runs
+// the same arithmetic.
+constexpr int64_t kGroupLoopMinS = 65536;
 
 struct Chunk {
     int h0, nh;    // query heads [h0, h0 + nh)
@@ -32,6 +41,7 @@ struct Plan {
     bool trunked;
     int nchunks, kvc;   // chunks, max kv heads in a chunk
     int carry_slots;    // fp32 dK/dV carries (bwd, group spanning chunks)
+    bool group_loop;    // bwd: group-loop dK/dV schedule (S >= group_loop_min_s)
 
     // workspace regions, byte offsets
     size_t q_c = 0, k_c = 0, v_c = 0;                   // packed chunk buffers
@@ -39,8 +49,8 @@ struct Plan {
     size_t st_l = 0;                                    // fwd carried lane-pair row sums
     size_t ring_k[2] = {0, 0}, ring_v[2] = {0, 0};      // trunk ring slots
     size_t do_c = 0, delta_c = 0, lse2_c = 0, dq_acc = 0; // bwd chunk buffers
-    size_t part_k = 0, part_v = 0;                      // bwd per-head fp32 dK/dV
-    size_t carry_k[2] = {0, 0}, carry_v[2] = {0, 0};    // bwd fp32 carries
+    size_t part_k = 0, part_v = 0;                      // bwd per-head fp32 dK/dV (not group_loop)
+    size_t carry_k[2] = {0, 0}, carry_v[2] = {0, 0};    // bwd fp32 carries ([2][S][D] if group_loop)
     size_t stage_k[2] = {0, 0}, stage_v[2] = {0, 0};    // bwd dK/dV staging
     size_t total = 0;
 
@@ -74,7 +84,8 @@ static inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAl
 
 // Returns 0 and fills *pl, or -1 (invalid) / -2 (unsupported) with a message.
 static inline int make_plan(bool bwd, int64_t S, int Hq, int Hkv, int D, int causal,
-                            int head_chunk, int64_t kv_trunk, Plan* pl, char* err, size_t errlen) {
+                            int head_chunk, int64_t kv_trunk, Plan* pl, char* err, size_t errlen,
+                            int64_t group_loop_min_s = kGroupLoopMinS) {
     if (S < 1) { snprintf(err, errlen, "S must be >= 1 (got %lld)", (long long)S); return -1; }
     if (Hq < 1 || Hkv < 1) { snprintf(err, errlen, "Hq and Hkv must be >= 1"); return -1; }
     if (Hq % Hkv != 0) {
@@ -125,6 +136,7 @@ static inline int make_plan(bool bwd, int64_t S, int Hq, int Hkv, int D, int cau
     }
     p.carry_slots = 0;
     if (bwd && p.hc % p.g != 0) p.carry_slots = (p.g % p.hc == 0) ? 1 : 2;
+    p.group_loop = bwd && S >= group_loop_min_s;
 
     const size_t E = (size_t)S * D * 2;         // one bf16 head slice
     const size_t Et = (size_t)p.T * D * 2;      // one bf16 trunk slice
@@ -152,9 +164,11 @@ static inline int make_plan(bool bwd, int64_t S, int Hq, int Hkv, int D, int cau
         p.do_c = take(p.hc * E);
         p.delta_c = take((size_t)p.hc * S * 4);           // -Delta, fp32 [hc][S]
         p.lse2_c = take((size_t)p.hc * S * 4);            // -LSE * log2(e), fp32 [hc][S]
-        const size_t rows = p.trunked ? Et : E;           // keys per dK/dV launch, bf16 bytes
-        p.part_k = take(p.hc * rows * 2);                 // fp32 [hc][rows][D]
-        p.part_v = take(p.hc * rows * 2);
+        if (!p.group_loop) {
+            const size_t rows = p.trunked ? Et : E;       // keys per dK/dV launch, bf16 bytes
+            p.part_k = take(p.hc * rows * 2);             // fp32 [hc][rows][D]
+            p.part_v = take(p.hc * rows * 2);
+        }
         if (!p.trunked) {
             p.k_c = take(p.kvc * E);
             p.v_c = take(p.kvc * E);
@@ -167,9 +181,12 @@ static inline int make_plan(bool bwd, int64_t S, int Hq, int Hkv, int D, int cau
                 p.stage_v[s] = take(p.kvc * Et);
             }
         }
+        // group loop: the two row halves of every key block keep their own
+        // fp32 sums until the group's last head, so a carry holds both
+        const size_t carry = p.group_loop ? E * 4 : E * 2;
         for (int s = 0; s < p.carry_slots; ++s) {
-            p.carry_k[s] = take(E * 2);                       // fp32 [S][D]
-            p.carry_v[s] = take(E * 2);
+            p.carry_k[s] = take(carry);                       // fp32 [S][D] or [2][S][D]
+            p.carry_v[s] = take(carry);
         }
     }
     p.total = off;
@@ -197,7 +214,8 @@ static inline int make_plan(bool bwd, int64_t S, int Hq, int Hkv, int D, int cau
 // S <= 256, which cannot be trunked) or -3 (nothing fits the budget).
 static inline int pick_kv_trunk(int64_t S, int Hq, int Hkv, int D, int causal, int head_chunk,
                                 bool kv_on_host, bool with_bwd, size_t budget, double link,
-                                double flops, int num_cus, int64_t* out, char* err, size_t errlen) {
+                                double flops, int num_cus, int64_t* out, char* err, size_t errlen,
+                                int64_t group_loop_min_s = kGroupLoopMinS) {
     Plan p;
     int r = make_plan(false, S, Hq, Hkv, D, causal, head_chunk, 0, &p, err, errlen);
     if (r) return r;
@@ -211,7 +229,8 @@ static inline int pick_kv_trunk(int64_t S, int Hq, int Hkv, int D, int causal, i
         if (rr) return rr;
         size_t n = f.total;
         if (with_bwd) {
-            rr = make_plan(true, S, Hq, Hkv, D, causal, head_chunk, T, &b, err, errlen);
+            rr = make_plan(true, S, Hq, Hkv, D, causal, head_chunk, T, &b, err, errlen,
+                           group_loop_min_s);
             if (rr) return rr;
             if (b.total > n) n = b.total;
         }

@@ -68,6 +68,8 @@ def lib():
     L.attn_set_single_stream.restype = ctypes.c_int
     L.attn_set_trunk_merge.argtypes = [ctypes.c_int]
     L.attn_set_trunk_merge.restype = ctypes.c_int
+    L.attn_set_group_loop_min_s.argtypes = [i64]
+    L.attn_set_group_loop_min_s.restype = i64
     L.attn_version.argtypes = []
     L.attn_version.restype = ctypes.c_char_p
     L.attn_timing_enable.argtypes = [ctypes.c_int]
@@ -345,6 +347,12 @@ def set_trunk_merge(on: bool) -> bool:
     """Trunked forward by log-sum-exp merge of per-trunk partials (True) instead
     of the in-kernel carried state (False, default); returns the old value."""
     return bool(lib().attn_set_trunk_merge(int(on)))
+
+
+def set_group_loop_min_s(min_s: int) -> int:
+    """Sequence length from which the backward's dK/dV pass takes the group-loop
+    schedule (0 restores the default, 65536); returns the previous value."""
+    return int(lib().attn_set_group_loop_min_s(int(min_s)))
 
 
 def version() -> str:

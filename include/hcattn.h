@@ -252,6 +252,22 @@ int attn_set_single_stream(int on);
 int attn_set_trunk_merge(int on);
 
 /*
+ * Schedule of the dK/dV pass.  Sequences of at least min_s tokens (default
+ * 65536) take the group-loop schedule: one workgroup per (128-key tile, kv
+ * head) walks the chunk's heads of that group and writes bf16 dK/dV itself
+ * (no per-head fp32 partials in the workspace, no reduce pass; a group that
+ * spans chunks carries fp32 sums of its two row halves).  Shorter sequences
+ * keep one workgroup per (key tile, query head) with per-head partials and
+ * an ordered reduce, which spreads the causal triangle over more
+ * workgroups.  Both are deterministic and bitwise identical across
+ * head_chunk and kv_trunk at one S; they round differently from each other.
+ * Affects attn_bwd, attn_layer_bwd and their workspace queries: change it
+ * before querying sizes.  min_s <= 0 restores the default.  Process-wide;
+ * returns the previous threshold.
+ */
+int64_t attn_set_group_loop_min_s(int64_t min_s);
+
+/*
  * Kernel timing for measurement tools.  While enabled, every kernel the
  * library launches is bracketed by two HIP timing events recorded on the
  * stream it runs on (the caller's stream); attn_timing_read waits for those

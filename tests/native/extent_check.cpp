@@ -33,6 +33,7 @@
 #include "plan.h"
 
 static bool g_plant = false;
+static int64_t g_gl_min_s = hc::kGroupLoopMinS;  // the library's group-loop threshold
 static long g_fails = 0, g_checks = 0;
 static std::string g_case;
 
@@ -257,15 +258,16 @@ hipError_t launch_fwd(const FwdParams& p, int HD, hipStream_t) {
     return hipSuccess;
 }
 
-// dkdv_kernel<HD, RUNS> as launched by launch_dkdv
+// dkdv_kernel<HD, RUNS, GLOOP> as launched by launch_dkdv
 hipError_t launch_dkdv(const DkdvParams& p, int HD, hipStream_t) {
-    if (p.nk <= 0 || p.nh <= 0) return hipSuccess;
+    const int units = p.group_loop ? p.nkv : p.nh;
+    if (p.nk <= 0 || units <= 0) return hipSuccess;
     const int BQ = 64, BNK = 128;
-    const int64_t blocks = (p.nk + BNK - 1) / BNK * p.nh;
-    const bool runs = p.nh % 4 != 0;
+    const int64_t blocks = (p.nk + BNK - 1) / BNK * units;
+    const bool runs = units % 4 != 0;
     std::vector<char> seen((size_t)blocks, 0);
     for (int64_t b = 0; b < blocks; ++b) {
-        int hl;
+        int unit;
         int64_t kt;
         if (runs) {
             const unsigned RUN = 32, WIN = 8 * RUN;
@@ -281,14 +283,28 @@ hipError_t launch_dkdv(const DkdvParams& p, int HD, hipStream_t) {
                 continue;
             }
             seen[item] = 1;
-            hl = (int)(item % (unsigned)p.nh);
-            kt = (int64_t)(item / (unsigned)p.nh);
+            unit = (int)(item % (unsigned)units);
+            kt = (int64_t)(item / (unsigned)units);
         } else {
-            hl = (int)(b % p.nh);
-            kt = b / p.nh;
+            unit = (int)(b % units);
+            kt = b / units;
         }
+        int kvl, hb, he;
+        if (p.group_loop) {
+            kvl = unit;
+            const int gh0 = (p.kv_base + kvl) * p.group - p.h0;
+            hb = gh0 < 0 ? 0 : gh0;
+            he = gh0 + p.group > p.nh ? p.nh : gh0 + p.group;
+            if (hb >= he) fail_msg("kv head %#llx of the chunk has no query head (%llu)",
+                                   "dkdv group", (uintptr_t)kvl, (size_t)hb);
+        } else {
+            hb = unit;
+            he = unit + 1;
+            kvl = (p.h0 + unit) / p.group - p.kv_base;
+        }
+        if (kvl < 0 || kvl >= (p.group_loop ? p.nkv : 1 << 30))
+            fail_msg("kv head %#llx out of range (%llu)", "dkdv kv head", (uintptr_t)kvl, 0);
         const int64_t j0 = kt * BNK;
-        const int kvl = (p.h0 + hl) / p.group - p.kv_base;
         if (j0 < p.nk) {
             const int64_t nv = p.nk - j0;
             for (int rh = 0; rh < 2; ++rh) {
@@ -312,23 +328,38 @@ hipError_t launch_dkdv(const DkdvParams& p, int HD, hipStream_t) {
             qt0 = first >= p.nq ? nqt : first / BQ;
         }
         const int64_t nsteps = j0 < p.nk ? nqt - qt0 : 0;
-        const uint16_t* qh = p.q + (int64_t)hl * p.q_hs;
-        const uint16_t* oh = p.dO + (int64_t)hl * p.do_hs;
-        const float* lseh = p.nlse2 + (int64_t)hl * p.nlse2_hs;
-        const float* delh = p.ndelta + (int64_t)hl * p.ndelta_hs;
-        for (int64_t n = 0; n < nsteps; ++n) {
-            const int64_t i0 = (qt0 + n) * BQ;
-            tile64(qh + i0 * p.q_rs, p.q_rs, p.nq - i0, HD, "dkdv Q tile");
-            tile64(oh + i0 * p.do_rs, p.do_rs, p.nq - i0, HD, "dkdv dO tile");
-            vec64(lseh + i0, p.nq - i0, "dkdv -LSE log2e");
-            vec64(delh + i0, p.nq - i0, "dkdv -Delta");
-        }
+        for (int h = hb; h < he; ++h)
+            for (int64_t n = 0; n < nsteps; ++n) {
+                const int64_t i0 = (qt0 + n) * BQ;
+                tile64(p.q + (int64_t)h * p.q_hs + i0 * p.q_rs, p.q_rs, p.nq - i0, HD, "dkdv Q tile");
+                tile64(p.dO + (int64_t)h * p.do_hs + i0 * p.do_rs, p.do_rs, p.nq - i0, HD,
+                       "dkdv dO tile");
+                vec64(p.nlse2 + (int64_t)h * p.nlse2_hs + i0, p.nq - i0, "dkdv -LSE log2e");
+                vec64(p.ndelta + (int64_t)h * p.ndelta_hs + i0, p.nq - i0, "dkdv -Delta");
+            }
         for (int kw = 0; kw < 4; ++kw)
             for (int l = 0; l < 32; ++l) {
                 const int64_t myk = j0 + kw * 32 + l;
                 if (myk >= p.nk) continue;
-                touch(at(p.part_k, ((int64_t)hl * p.nk + myk) * HD), HD * 4, "dkdv dK partial");
-                touch(at(p.part_v, ((int64_t)hl * p.nk + myk) * HD), HD * 4, "dkdv dV partial");
+                if (!p.group_loop) {
+                    touch(at(p.part_k, ((int64_t)hb * p.nk + myk) * HD), HD * 4, "dkdv dK partial");
+                    touch(at(p.part_v, ((int64_t)hb * p.nk + myk) * HD), HD * 4, "dkdv dV partial");
+                    continue;
+                }
+                for (int rh = 0; rh < 2; ++rh) {
+                    if (kvl == p.carry_kv_in) {
+                        touch(at(p.carry_in_k, rh * p.carry_hs + myk * HD), HD * 4, "dkdv carry in dK");
+                        touch(at(p.carry_in_v, rh * p.carry_hs + myk * HD), HD * 4, "dkdv carry in dV");
+                    }
+                    if (kvl == p.carry_kv_out) {
+                        touch(at(p.carry_out_k, rh * p.carry_hs + myk * HD), HD * 4, "dkdv carry out dK");
+                        touch(at(p.carry_out_v, rh * p.carry_hs + myk * HD), HD * 4, "dkdv carry out dV");
+                    }
+                }
+                if (kvl != p.carry_kv_out) {
+                    touch(at(p.dk, (int64_t)kvl * p.dk_hs + myk * p.dk_rs), HD * 2, "dkdv dK out");
+                    touch(at(p.dv, (int64_t)kvl * p.dk_hs + myk * p.dk_rs), HD * 2, "dkdv dV out");
+                }
             }
     }
     return hipSuccess;
@@ -509,9 +540,11 @@ static void add_workspace(char* ws, const hc::Plan& p) {
         R(p.do_c, p.hc * E, "ws dO_c");
         R(p.delta_c, (size_t)p.hc * p.S * 4, "ws -Delta");
         R(p.lse2_c, (size_t)p.hc * p.S * 4, "ws -LSE log2e");
-        const size_t rows = p.trunked ? Et : E;
-        R(p.part_k, p.hc * rows * 2, "ws dK partials");
-        R(p.part_v, p.hc * rows * 2, "ws dV partials");
+        if (!p.group_loop) {
+            const size_t rows = p.trunked ? Et : E;
+            R(p.part_k, p.hc * rows * 2, "ws dK partials");
+            R(p.part_v, p.hc * rows * 2, "ws dV partials");
+        }
         if (!p.trunked) {
             R(p.k_c, p.kvc * E, "ws K_c");
             R(p.v_c, p.kvc * E, "ws V_c");
@@ -525,8 +558,8 @@ static void add_workspace(char* ws, const hc::Plan& p) {
             }
         }
         for (int s = 0; s < p.carry_slots; ++s) {
-            R(p.carry_k[s], E * 2, "ws dK carry");
-            R(p.carry_v[s], E * 2, "ws dV carry");
+            R(p.carry_k[s], p.group_loop ? E * 4 : E * 2, "ws dK carry");
+            R(p.carry_v[s], p.group_loop ? E * 4 : E * 2, "ws dV carry");
         }
     }
 }
@@ -564,7 +597,7 @@ static void run_case(int64_t S, int Hq, int Hkv, int D, int causal, int hc, int6
     g_allocs.push_back({(uintptr_t)wf, (uintptr_t)wf + nf, false});
     hc::Plan pf, pb;
     char msg[256];
-    hc::make_plan(false, S, Hq, Hkv, D, causal, hc, T, &pf, msg, sizeof msg);
+    hc::make_plan(false, S, Hq, Hkv, D, causal, hc, T, &pf, msg, sizeof msg, g_gl_min_s);
     const size_t keep = g_regions.size();
     add_workspace(wf, pf);
     int rc = attn_fwd(q.p(), k.p(), v.p(), o.p(), (float*)lse.p(), S, Hq, Hkv, D, causal, hc, T,
@@ -585,7 +618,7 @@ static void run_case(int64_t S, int Hq, int Hkv, int D, int causal, int hc, int6
         g_allocs.pop_back();
     }
     g_allocs.push_back({(uintptr_t)wb, (uintptr_t)wb + nb, false});
-    hc::make_plan(true, S, Hq, Hkv, D, causal, hc, T, &pb, msg, sizeof msg);
+    hc::make_plan(true, S, Hq, Hkv, D, causal, hc, T, &pb, msg, sizeof msg, g_gl_min_s);
     add_workspace(wb, pb);
     rc = attn_bwd(q.p(), k.p(), v.p(), o.p(), dout.p(), (const float*)lse.p(), dq.p(), dk.p(),
                   dv.p(), S, Hq, Hkv, D, causal, hc, T, wb, nb, nullptr);
@@ -633,7 +666,7 @@ static void run_layer_case(int64_t S, int dm, int Hq, int Hkv, int D, int causal
     char msg[256];
     for (int bwd = 0; bwd < 2; ++bwd) {
         hc::Plan p;
-        hc::make_plan(bwd, S, Hq, Hkv, D, causal, hc, 0, &p, msg, sizeof msg);
+        hc::make_plan(bwd, S, Hq, Hkv, D, causal, hc, 0, &p, msg, sizeof msg, g_gl_min_s);
         char* ws = bwd ? wb : wf;
         add_workspace(ws, p);
         size_t off = p.total;
@@ -679,6 +712,10 @@ int main(int argc, char** argv) {
     struct Heads { int Hq, Hkv; };
     const Heads hs[] = {{1, 1}, {2, 1}, {4, 2}, {8, 2}, {8, 1}, {4, 4}, {6, 2}};
     long cases = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+    // pass 1: the group-loop dK/dV schedule at every length
+    g_gl_min_s = pass == 0 ? hc::kGroupLoopMinS : 1;
+    attn_set_group_loop_min_s(g_gl_min_s);
     unsigned rng = 12345u;
     auto pick = [&](int n) { rng = rng * 1103515245u + 12345u; return (int)((rng >> 16) % (unsigned)n); };
     for (int64_t S : Ss)
@@ -712,6 +749,7 @@ int main(int argc, char** argv) {
         }
     run_layer_case(200, 192, 4, 1, 128, 0, 2); ++cases;
     run_layer_case(777, 256, 4, 2, 128, 1, 4); ++cases;
+    }
     printf("cases: %ld  accesses checked: %ld  failures: %ld\n", cases, g_checks, g_fails);
     return g_fails == 0 ? 0 : 1;
 }

@@ -64,8 +64,14 @@ static void check_plan(const hc::Plan& p) {
     } else {
         const size_t rows_b = p.trunked ? Et : E;
         r = {{p.q_c, p.hc * E}, {p.do_c, p.hc * E}, {p.delta_c, (size_t)p.hc * p.S * 4},
-             {p.lse2_c, (size_t)p.hc * p.S * 4}, {p.part_k, p.hc * rows_b * 2},
-             {p.part_v, p.hc * rows_b * 2}};
+             {p.lse2_c, (size_t)p.hc * p.S * 4}};
+        // per-head fp32 partials only in the per-head dK/dV schedule (S below
+        // the group-loop threshold)
+        CHECK(p.group_loop == (p.S >= hc::kGroupLoopMinS), "group loop at S=%lld", (long long)p.S);
+        if (!p.group_loop) {
+            r.push_back({p.part_k, p.hc * rows_b * 2});
+            r.push_back({p.part_v, p.hc * rows_b * 2});
+        }
         if (!p.trunked) {
             r.push_back({p.k_c, p.kvc * E});
             r.push_back({p.v_c, p.kvc * E});
@@ -78,9 +84,10 @@ static void check_plan(const hc::Plan& p) {
                 r.push_back({p.stage_v[s], p.kvc * Et});
             }
         }
+        // carries: fp32 [S][D], or [2][S][D] (both row halves) in the group loop
         for (int s = 0; s < p.carry_slots; ++s) {
-            r.push_back({p.carry_k[s], E * 2});
-            r.push_back({p.carry_v[s], E * 2});
+            r.push_back({p.carry_k[s], p.group_loop ? E * 4 : E * 2});
+            r.push_back({p.carry_v[s], p.group_loop ? E * 4 : E * 2});
         }
     }
     std::sort(r.begin(), r.end(), [](const Region& a, const Region& b) { return a.off < b.off; });
@@ -95,8 +102,8 @@ static void check_plan(const hc::Plan& p) {
 }
 
 int main() {
-    const int64_t Ss[] = {1, 2, 63, 64, 255, 256, 257, 1000, 32768, 262144, 524288, 5242880,
-                          (int64_t)1 << 30};
+    const int64_t Ss[] = {1, 2, 63, 64, 255, 256, 257, 1000, 32768, 65535, 65536, 262144,
+                          524288, 5242880, (int64_t)1 << 30};
     const int HqHkv[][2] = {{1, 1}, {2, 1}, {4, 2}, {8, 2}, {8, 1}, {32, 8}, {40, 8}, {4, 1}, {6, 3}};
     const int64_t Ts[] = {0, 256, 512, 65536, 262144};
     char err[256];

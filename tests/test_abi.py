@@ -70,6 +70,36 @@ def test_backward_workspace_formula_aligned_chunks():
         assert hc.bwd_workspace_bytes(S, Hq, Hkv, D, True, hc_, 0) == want
 
 
+def test_backward_workspace_formula_group_loop():
+    # S >= 65536: the group-loop dK/dV schedule keeps no per-head fp32
+    # partials; a group spanning chunks carries both row halves' fp32 sums
+    S, Hq, Hkv, D = 262144, 32, 8, 128
+    for hc_ in (4, 8, 32):
+        kvc = hc_ // 4
+        want = 2 * A(hc_ * E(S, D)) + 2 * A(hc_ * S * 4) + 2 * A(kvc * E(S, D))
+        assert hc.bwd_workspace_bytes(S, Hq, Hkv, D, True, hc_, 0) == want
+    # hc = 1 and 2 (g = 4): one carry slot of [2][S][D] fp32 for dK and for dV
+    for hc_ in (1, 2):
+        want = 2 * A(hc_ * E(S, D)) + 2 * A(hc_ * S * 4) + 2 * A(E(S, D)) + 2 * A(4 * E(S, D))
+        assert hc.bwd_workspace_bytes(S, Hq, Hkv, D, True, hc_, 0) == want
+
+
+def test_group_loop_threshold_switch():
+    L = lib()
+    L.attn_set_group_loop_min_s.argtypes = [ctypes.c_int64]
+    L.attn_set_group_loop_min_s.restype = ctypes.c_int64
+    S, Hq, Hkv, D = 4096, 8, 2, 128
+    per_head = hc.bwd_workspace_bytes(S, Hq, Hkv, D, True, 4, 0)
+    prev = L.attn_set_group_loop_min_s(1)
+    try:
+        assert prev == 65536
+        looped = hc.bwd_workspace_bytes(S, Hq, Hkv, D, True, 4, 0)
+    finally:
+        assert L.attn_set_group_loop_min_s(prev) == 1
+    assert per_head - looped == 2 * A(4 * E(S, D) * 2)  # the per-head partials
+    assert hc.bwd_workspace_bytes(S, Hq, Hkv, D, True, 4, 0) == per_head
+
+
 def test_trunked_workspace_scales_with_trunk_not_sequence():
     a = hc.fwd_workspace_bytes(524288, 40, 8, 128, True, 5, 65536)
     b = hc.fwd_workspace_bytes(1048576, 40, 8, 128, True, 5, 65536)
