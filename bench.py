@@ -51,6 +51,9 @@ def parse():
                     help="skip the pinned-host-trunk line (workload 4)")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the attention-layer line (projections around attention)")
+    ap.add_argument("--group-loop-min-s", type=int, default=0,
+                    help="sequence length from which dK/dV takes the group-loop schedule "
+                         "(0 = the library default, 65536)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=12288,
                     help="tokens of the CPU-oracle sample (one GQA group)")
@@ -151,6 +154,13 @@ def cpu_oracle_baseline(D: int, g: int, tokens: int) -> dict:
             "sample": f"fp64 oracle forward+backward of one GQA group ({g} query heads, 1 kv "
                       f"head, D={D}) over the first {tokens} tokens; {dt:.1f} s wall, counted "
                       f"FLOPs 7*S^2*D*heads"}
+
+
+def group_loop_min_s(hcm) -> int:
+    """The library's current group-loop threshold (read without changing it)."""
+    prev = hcm.set_group_loop_min_s(0)
+    hcm.set_group_loop_min_s(prev)
+    return prev
 
 
 def run_workload(hcm, torch, w, hc, T, dev, steps, warmup, timing, kv_on_host, trunk_merge=False,
@@ -304,6 +314,8 @@ def main():
         T = int(args.kv_trunk)
     causal = True
 
+    if args.group_loop_min_s > 0:
+        hcm.set_group_loop_min_s(args.group_loop_min_s)
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         a = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -355,6 +367,7 @@ def main():
                                        else "given" if int(args.kv_trunk) >= 0 else "workload"),
                    "causal": causal, "batch": 1},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "dkdv_schedule": "group loop" if S >= group_loop_min_s(hcm) else "per head",
         "fwd_tflops": round(2.0 * S * S * D * Hq / (r["fwd_ms"] / 1e3) / 1e12, 2),
         "bwd_tflops": round(5.0 * S * S * D * Hq / (r["bwd_ms"] / 1e3) / 1e12, 2),
         "workspace_bytes": {str(hc): {"fwd": r["ws_fwd"], "bwd": r["ws_bwd"],
