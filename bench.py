@@ -271,20 +271,32 @@ def run_layer(hcm, torch, w, hc, dev, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    hcm.timing_reset()
+    hcm.timing_enable(True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
         step()
     e1.record()
     torch.cuda.synchronize()
+    hcm.timing_enable(False)
+    kern = hcm.timing_read()
+    hcm.timing_reset()
     ms = e0.elapsed_time(e1) / steps
     peak = torch.cuda.max_memory_allocated(dev) - base
     print(f"layer {w.name}: head_chunk={hc}: {ms:.1f} ms per step", file=sys.stderr, flush=True)
     # counted work: attention 7*S^2*D*Hq, projections 2*S*dm*D*(2 Hq + 2 Hkv) forward and
     # twice that backward (the backward's recomputation is not counted)
-    flops = 7.0 * S * S * D * Hq + 3 * 2.0 * S * dm * D * (2 * Hq + 2 * Hkv)
+    proj = 2.0 * S * dm * D * (2 * Hq + 2 * Hkv)
+    flops = 7.0 * S * S * D * Hq + 3 * proj
+    # products executed per step: forward projections + output projection,
+    # backward recomputed projections, dO, dWo, dx and the weight gradients
+    gemm_flops = 4 * proj - 2.0 * S * dm * D * Hq
+    gemm_ms = kern["gemm"][1] / steps
     return {"head_chunk": hc, "ms_per_step": round(ms, 1),
             "tflops": round(flops / (ms / 1e3) / 1e12, 2),
+            "kernel_ms_per_step": {f: round(kern[f][1] / steps, 2) for f in kern if kern[f][0]},
+            "gemm_tflops": round(gemm_flops / (gemm_ms / 1e3) / 1e12, 1) if gemm_ms > 0 else None,
             "workspace_bytes": {"fwd": fb, "bwd": bb}, "peak_intermediate": peak}
 
 

@@ -14,10 +14,10 @@
 // and the same for B with n in place of m.  Segments are multiples of 8.
 //
 // Workgroup = 4 waves on a 128 x 128 tile of C, 2 x 2 waves of 64 x 64; K in
-// steps of 32 staged through LDS (registers -> LDS, double-buffered, one
-// barrier per step).  A k-contiguous operand tile is [128][32] with rows
-// padded to 80 bytes (conflict-free 8-byte reads); an m- or n-contiguous one
-// is [32][128] with the XOR-swizzled rows of the attention kernels, read
+// steps of 64 staged through LDS (registers -> LDS, double-buffered, one
+// barrier per step).  A k-contiguous operand tile is [128][64] with rows
+// padded by 16 bytes (conflict-free 8-byte reads); an m- or n-contiguous one
+// is [64][128] with the XOR-swizzled rows of the attention kernels, read
 // transposed by ds_read_b64_tr_b16.  Both reads deliver the 16 reduction
 // indices of an MFMA step in the same order (k0 + 4c + 0..3, k0 + 8 + 4c +
 // 0..3 for lane half c), so any pair of layouts multiplies consistently.
@@ -29,7 +29,8 @@
 // fp32 accumulated into C: the accumulators then start from C's values, so a
 // reduction split over several launches (one head chunk each) adds its terms
 // in the same order as a single launch, bit for bit.
-// Split-K: blockIdx.z takes k in [z * k_split, (z + 1) * k_split) and writes
+// Split-K: blockIdx.z takes k in [z * k_split, (z + 1) * k_split) (k_split a
+// multiple of 64) and writes
 // fp32 partials at c + z * c_zs; gemm_reduce adds the slices in ascending z.
 #include "device_common.h"
 #include "kernels.h"
@@ -38,8 +39,8 @@ namespace hc {
 
 namespace {
 
-constexpr int GBM = 128, GBN = 128, GBK = 32;
-constexpr int KC_PITCH = 40;  // bf16 per padded row of a k-contiguous tile
+constexpr int GBM = 128, GBN = 128, GBK = 64;
+constexpr int KC_PITCH = GBK + 8;  // bf16 per padded row of a k-contiguous tile (16 B pad)
 
 // 16 reduction indices of one MFMA step from a k-contiguous [rows][KC_PITCH]
 // tile, row `row`, in the transposed-read order
@@ -52,20 +53,22 @@ __device__ __forceinline__ bf16x8 kc_frag(const char* tile, int row, int k0, int
 
 template <bool KC>
 struct OperandTile {
-    // 512 16-byte chunks per 128 x 32 tile, two per thread
-    uint4 r[2];
+    // 1024 16-byte chunks per 128 x 64 tile, four per thread
+    static constexpr int NCH = GBM * GBK / 8 / 256;
+    static constexpr int KCH = GBK / 8;  // chunks per k-contiguous row
+    uint4 r[NCH];
 
     // rows (m or n) r0.., reduction indices k0..; zero outside [0, R) x [0, K)
     __device__ __forceinline__ void load(const uint16_t* base, int64_t rs, int64_t seg,
                                          int64_t segs, int64_t r0, int64_t R, int64_t k0,
                                          int64_t K, int tid) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NCH; ++i) {
             const int idx = tid + i * 256;
             int64_t row, k;
             if constexpr (KC) {
-                row = r0 + idx / 4;
-                k = k0 + (idx % 4) * 8;
+                row = r0 + idx / KCH;
+                k = k0 + (idx % KCH) * 8;
             } else {
                 k = k0 + idx / 16;
                 row = r0 + (idx % 16) * 8;
@@ -81,10 +84,10 @@ struct OperandTile {
     }
     __device__ __forceinline__ void store(char* lds, int tid) const {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NCH; ++i) {
             const int idx = tid + i * 256;
             int off;
-            if constexpr (KC) off = (idx / 4) * (KC_PITCH * 2) + (idx % 4) * 16;
+            if constexpr (KC) off = (idx / KCH) * (KC_PITCH * 2) + (idx % KCH) * 16;
             else off = lds_off<128>(idx / 16, (idx % 16) * 8);
             *reinterpret_cast<uint4*>(lds + off) = r[i];
         }

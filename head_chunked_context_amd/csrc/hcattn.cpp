@@ -681,7 +681,7 @@ int layer_plan(bool bwd, int64_t S, int dm, int Hq, int Hkv, int D, int causal, 
         L->dv_c = take(p.kvc * E);
         // split-K of the weight gradients: a function of S only, so that every
         // weight row sums its terms the same way whatever the chunking
-        L->k_split = (S + 32 * kWgradSplits - 1) / (32 * kWgradSplits) * 32;
+        L->k_split = (S + 64 * kWgradSplits - 1) / (64 * kWgradSplits) * 64;
         L->splits = (int)((S + L->k_split - 1) / L->k_split);
         L->wpart = take((size_t)L->splits * p.hc * D * dm * 4);
     }

@@ -174,7 +174,7 @@ struct GemmParams {
     int64_t M, N, K;
     void* c;           int64_t c_rs, c_seg, c_segs;
     int out_mode;
-    int64_t k_split;   // reduction indices per split (multiple of 32); 0 = no split
+    int64_t k_split;   // reduction indices per split (multiple of 64); 0 = no split
     int64_t c_zs;      // elements between the splits' fp32 partial outputs
 };
 // out[m][n] (+ out[m][n] if add) = sum over z ascending of part[z * part_zs + m * N + n]

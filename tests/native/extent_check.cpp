@@ -446,11 +446,12 @@ hipError_t launch_dq(const DqParams& p, int HD, hipStream_t) {
 // gemm_kernel<A_KC, B_KC> as launched by launch_gemm: every 16-byte operand
 // chunk a 128 x 32 tile load reads, and every C row segment the epilogue (and
 // the accumulating prologue) touches
+static const int kGemmBK = 64;  // reduction indices per operand tile load
 static void gemm_operand(const uint16_t* base, int64_t rs, int64_t seg, int64_t segs, bool kc,
                          int64_t r0, int64_t R, int64_t k0, int64_t K, const char* what) {
-    for (int idx = 0; idx < 512; ++idx) {
+    for (int idx = 0; idx < 128 * kGemmBK / 8; ++idx) {
         int64_t row, k;
-        if (kc) { row = r0 + idx / 4; k = k0 + (idx % 4) * 8; }
+        if (kc) { row = r0 + idx / (kGemmBK / 8); k = k0 + (idx % (kGemmBK / 8)) * 8; }
         else { k = k0 + idx / 16; row = r0 + (idx % 16) * 8; }
         if (row >= R || k >= K) continue;
         const int64_t off = kc ? (k / seg) * segs + row * rs + k % seg
@@ -464,7 +465,7 @@ hipError_t launch_gemm(const GemmParams& p, bool a_kc, bool b_kc, int splits, hi
     if ((a_kc || b_kc) && p.K % 8 != 0) return hipErrorInvalidValue;
     if (!a_kc && p.M % 8 != 0) return hipErrorInvalidValue;
     if (p.N % 8 != 0 || p.a_seg % 8 != 0 || p.b_seg % 8 != 0 || p.c_seg % 4 != 0 ||
-        (p.k_split > 0 && p.k_split % 32 != 0) || splits < 1 || splits > 65535)
+        (p.k_split > 0 && p.k_split % kGemmBK != 0) || splits < 1 || splits > 65535)
         return hipErrorInvalidValue;
     const int64_t gx = (p.M + 127) / 128, gy = (p.N + 127) / 128;
     for (int z = 0; z < splits; ++z)
@@ -474,7 +475,7 @@ hipError_t launch_gemm(const GemmParams& p, bool a_kc, bool b_kc, int splits, hi
                 const int64_t kb = p.k_split > 0 ? (int64_t)z * p.k_split : 0;
                 int64_t ke = p.k_split > 0 ? kb + p.k_split : p.K;
                 ke = ke < p.K ? ke : p.K;
-                for (int64_t k0 = kb; k0 < ke; k0 += 32) {
+                for (int64_t k0 = kb; k0 < ke; k0 += kGemmBK) {
                     gemm_operand(p.a, p.a_rs, p.a_seg, p.a_segs, a_kc, m0, p.M, k0, ke, "gemm A");
                     gemm_operand(p.b, p.b_rs, p.b_seg, p.b_segs, b_kc, n0, p.N, k0, ke, "gemm B");
                 }
@@ -680,7 +681,7 @@ static void run_layer_case(int64_t S, int dm, int Hq, int Hkv, int D, int causal
             R(p.hc * E, "ws dQ_c");
             R(p.kvc * E, "ws dK_c");
             R(p.kvc * E, "ws dV_c");
-            const int64_t ks = (S + 32 * 8 - 1) / (32 * 8) * 32;
+            const int64_t ks = (S + 64 * 8 - 1) / (64 * 8) * 64;
             const int64_t splits = (S + ks - 1) / ks;
             R((size_t)splits * p.hc * D * dm * 4, "ws weight-gradient partials");
         }
