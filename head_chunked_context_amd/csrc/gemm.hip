@@ -11,7 +11,8 @@
 // chunk buffers ([h][S][D], whose columns h * D + d jump by S * D at every D):
 //   A_KC (k contiguous):  A(m, k) = a[(k / a_seg) a_segs + m a_rs + k % a_seg]
 //   else (m contiguous):  A(m, k) = a[(m / a_seg) a_segs + k a_rs + m % a_seg]
-// and the same for B with n in place of m.  Segments are multiples of 8.
+// and the same for B with n in place of m.  Segments are multiples of 8, and
+// of 64 for a k-contiguous operand.
 //
 // Workgroup = 4 waves on a 128 x 128 tile of C, 2 x 2 waves of 64 x 64; K in
 // steps of 64 staged through LDS (registers -> LDS, double-buffered, one
@@ -57,39 +58,70 @@ struct OperandTile {
     static constexpr int NCH = GBM * GBK / 8 / 256;
     static constexpr int KCH = GBK / 8;  // chunks per k-contiguous row
     uint4 r[NCH];
+    int64_t off[NCH];  // element offset of the thread's chunk i at the tile's first k
+    int kk[NCH];       // its reduction index relative to the tile's first k
+    bool row_ok[NCH];
 
-    // rows (m or n) r0.., reduction indices k0..; zero outside [0, R) x [0, K)
-    __device__ __forceinline__ void load(const uint16_t* base, int64_t rs, int64_t seg,
-                                         int64_t segs, int64_t r0, int64_t R, int64_t k0,
-                                         int64_t K, int tid) {
+    // The per-thread part of every address is worked out once: a thread's
+    // chunks keep their rows, and a 64-wide k step never leaves a segment
+    // (k-contiguous segments are multiples of 64), so a step only moves the
+    // offsets by a wave-uniform amount.
+    __device__ __forceinline__ void init(int64_t rs, int64_t seg, int64_t segs, int64_t r0,
+                                         int64_t R, int tid) {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int idx = tid + i * 256;
-            int64_t row, k;
             if constexpr (KC) {
-                row = r0 + idx / KCH;
-                k = k0 + (idx % KCH) * 8;
+                const int64_t row = r0 + idx / KCH;
+                kk[i] = (idx % KCH) * 8;
+                row_ok[i] = row < R;
+                off[i] = row * rs + kk[i];
             } else {
-                k = k0 + idx / 16;
-                row = r0 + (idx % 16) * 8;
+                const int64_t row = r0 + (idx % 16) * 8;
+                kk[i] = idx / 16;
+                row_ok[i] = row < R;
+                off[i] = (row / seg) * segs + row % seg + kk[i] * rs;
             }
-            if (row < R && k < K) {
-                const int64_t off = KC ? (k / seg) * segs + row * rs + k % seg
-                                       : (row / seg) * segs + k * rs + row % seg;
-                r[i] = *reinterpret_cast<const uint4*>(base + off);
-            } else {
-                r[i] = make_uint4(0, 0, 0, 0);
+        }
+    }
+    // wave-uniform offset of the current tile's first k, and (k-contiguous)
+    // that k's position in its segment
+    int64_t k0, cur, kr;
+    __device__ __forceinline__ void begin(int64_t rs, int64_t seg, int64_t segs, int64_t k) {
+        k0 = k;
+        kr = KC ? k % seg : 0;
+        cur = KC ? (k / seg) * segs + kr : k * rs;
+    }
+    __device__ __forceinline__ void advance(int64_t rs, int64_t seg, int64_t segs) {
+        k0 += GBK;
+        if constexpr (KC) {
+            kr += GBK;
+            cur += GBK;
+            if (kr == seg) {  // into the next segment
+                kr = 0;
+                cur += segs - seg;
             }
+        } else {
+            cur += GBK * rs;
+        }
+    }
+    // the current tile; zero outside [0, R) x [k0, K)
+    __device__ __forceinline__ void load(const uint16_t* base, int64_t K) {
+        const uint16_t* b = base + cur;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            if (row_ok[i] && k0 + kk[i] < K) r[i] = *reinterpret_cast<const uint4*>(b + off[i]);
+            else r[i] = make_uint4(0, 0, 0, 0);
         }
     }
     __device__ __forceinline__ void store(char* lds, int tid) const {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int idx = tid + i * 256;
-            int off;
-            if constexpr (KC) off = (idx / KCH) * (KC_PITCH * 2) + (idx % KCH) * 16;
-            else off = lds_off<128>(idx / 16, (idx % 16) * 8);
-            *reinterpret_cast<uint4*>(lds + off) = r[i];
+            int o;
+            if constexpr (KC) o = (idx / KCH) * (KC_PITCH * 2) + (idx % KCH) * 16;
+            else o = lds_off<128>(idx / 16, (idx % 16) * 8);
+            *reinterpret_cast<uint4*>(lds + o) = r[i];
         }
     }
 };
@@ -152,9 +184,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
         }
 
     const OperandOffsets<128> off(lane);
+    ta.init(p.a_rs, p.a_seg, p.a_segs, m0, p.M, tid);
+    tb.init(p.b_rs, p.b_seg, p.b_segs, n0, p.N, tid);
+    ta.begin(p.a_rs, p.a_seg, p.a_segs, kb);
+    tb.begin(p.b_rs, p.b_seg, p.b_segs, kb);
     if (nkt > 0) {
-        ta.load(p.a, p.a_rs, p.a_seg, p.a_segs, m0, p.M, kb, ke, tid);
-        tb.load(p.b, p.b_rs, p.b_seg, p.b_segs, n0, p.N, kb, ke, tid);
+        ta.load(p.a, ke);
+        tb.load(p.b, ke);
         ta.store(sa[0], tid);
         tb.store(sb[0], tid);
     }
@@ -162,9 +198,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     for (int kt = 0; kt < nkt; ++kt) {
         const int buf = kt & 1;
         if (kt + 1 < nkt) {
-            const int64_t k1 = kb + (int64_t)(kt + 1) * GBK;
-            ta.load(p.a, p.a_rs, p.a_seg, p.a_segs, m0, p.M, k1, ke, tid);
-            tb.load(p.b, p.b_rs, p.b_seg, p.b_segs, n0, p.N, k1, ke, tid);
+            ta.advance(p.a_rs, p.a_seg, p.a_segs);
+            tb.advance(p.b_rs, p.b_seg, p.b_segs);
+            ta.load(p.a, ke);
+            tb.load(p.b, ke);
         }
 #pragma unroll
         for (int ks = 0; ks < GBK / 16; ++ks) {
@@ -235,6 +272,8 @@ hipError_t launch_gemm(const GemmParams& p, bool a_kc, bool b_kc, int splits, hi
     // 16-byte operand chunks never straddle a segment, the end of a k-contiguous
     // row or the end of an r-contiguous one
     if ((a_kc || b_kc) && p.K % 8 != 0) return hipErrorInvalidValue;
+    // a 64-wide k step of a k-contiguous operand stays inside one segment
+    if ((a_kc && p.a_seg % GBK != 0) || (b_kc && p.b_seg % GBK != 0)) return hipErrorInvalidValue;
     if (!a_kc && p.M % 8 != 0) return hipErrorInvalidValue;
     if (p.N % 8 != 0 || p.a_seg % 8 != 0 || p.b_seg % 8 != 0 || p.c_seg % 4 != 0 ||
         (p.k_split > 0 && p.k_split % GBK != 0) || splits < 1 || splits > 65535)
