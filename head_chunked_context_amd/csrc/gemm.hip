@@ -15,9 +15,10 @@
 // of 64 for a k-contiguous operand.
 //
 // Workgroup = 4 waves on a 128 x 128 tile of C, 2 x 2 waves of 64 x 64; K in
-// steps of 64 staged through LDS (registers -> LDS, double-buffered, one
-// barrier per step).  A k-contiguous operand tile is [128][64] with rows
-// padded by 16 bytes (conflict-free 8-byte reads); an m- or n-contiguous one
+// steps of 64 staged through LDS (global -> registers two steps ahead, two
+// register sets; registers -> LDS double-buffered, one barrier per step).  A
+// k-contiguous operand tile is [128][64] with rows padded by 16 bytes
+// (conflict-free 8-byte reads); an m- or n-contiguous one
 // is [64][128] with the XOR-swizzled rows of the attention kernels, read
 // transposed by ds_read_b64_tr_b16.  Both reads deliver the 16 reduction
 // indices of an MFMA step in the same order (k0 + 4c + 0..3, k0 + 8 + 4c +
@@ -33,6 +34,8 @@
 // Split-K: blockIdx.z takes k in [z * k_split, (z + 1) * k_split) (k_split a
 // multiple of 64) and writes
 // fp32 partials at c + z * c_zs; gemm_reduce adds the slices in ascending z.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -57,7 +60,7 @@ struct OperandTile {
     // 1024 16-byte chunks per 128 x 64 tile, four per thread
     static constexpr int NCH = GBM * GBK / 8 / 256;
     static constexpr int KCH = GBK / 8;  // chunks per k-contiguous row
-    uint4 r[NCH];
+    uint4 r[2][NCH];   // two register sets: a tile lands in one while the other is stored
     int64_t off[NCH];  // element offset of the thread's chunk i at the tile's first k
     int kk[NCH];       // its reduction index relative to the tile's first k
     bool row_ok[NCH];
@@ -84,16 +87,32 @@ struct OperandTile {
             }
         }
     }
-    // wave-uniform offset of the current tile's first k, and (k-contiguous)
-    // that k's position in its segment
-    int64_t k0, cur, kr;
-    __device__ __forceinline__ void begin(int64_t rs, int64_t seg, int64_t segs, int64_t k) {
+    // wave-uniform state: the current part's operand and where that part
+    // ends, the offset of the current tile's first k in it, and
+    // (k-contiguous) that k's position in its segment
+    const uint16_t* base;
+    int64_t k0, cur, kr, kend;
+    int part;
+    __device__ __forceinline__ void begin(const uint16_t* x, int64_t rs, int64_t seg, int64_t segs,
+                                          int64_t k, int64_t part_end) {
+        base = x;
+        part = 0;
+        kend = part_end;
         k0 = k;
         kr = KC ? k % seg : 0;
         cur = KC ? (k / seg) * segs + kr : k * rs;
     }
-    __device__ __forceinline__ void advance(int64_t rs, int64_t seg, int64_t segs) {
+    __device__ __forceinline__ void advance(const GemmParams& p, bool is_a, int64_t rs,
+                                            int64_t seg, int64_t segs) {
         k0 += GBK;
+        if (k0 == kend && part + 1 < p.k_parts) {  // into the next part
+            ++part;
+            base = is_a ? p.a_at[part] : p.b_at[part];
+            kend = p.k_at[part + 1];
+            kr = 0;
+            cur = 0;
+            return;
+        }
         if constexpr (KC) {
             kr += GBK;
             cur += GBK;
@@ -105,15 +124,17 @@ struct OperandTile {
             cur += GBK * rs;
         }
     }
-    // the current tile; zero outside [0, R) x [k0, K)
-    __device__ __forceinline__ void load(const uint16_t* base, int64_t K) {
+    // the current tile into register set SET; zero outside [0, R) x [k0, K)
+    template <int SET>
+    __device__ __forceinline__ void load(int64_t K) {
         const uint16_t* b = base + cur;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-            if (row_ok[i] && k0 + kk[i] < K) r[i] = *reinterpret_cast<const uint4*>(b + off[i]);
-            else r[i] = make_uint4(0, 0, 0, 0);
+            if (row_ok[i] && k0 + kk[i] < K) r[SET][i] = *reinterpret_cast<const uint4*>(b + off[i]);
+            else r[SET][i] = make_uint4(0, 0, 0, 0);
         }
     }
+    template <int SET>
     __device__ __forceinline__ void store(char* lds, int tid) const {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
@@ -121,7 +142,7 @@ struct OperandTile {
             int o;
             if constexpr (KC) o = (idx / KCH) * (KC_PITCH * 2) + (idx % KCH) * 16;
             else o = lds_off<128>(idx / 16, (idx % 16) * 8);
-            *reinterpret_cast<uint4*>(lds + o) = r[i];
+            *reinterpret_cast<uint4*>(lds + o) = r[SET][i];
         }
     }
 };
@@ -145,7 +166,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1, hi = lane >> 5;
-    const int64_t m0 = (int64_t)blockIdx.x * GBM, n0 = (int64_t)blockIdx.y * GBN;
+    // tile order: the workgroups of a row of C tiles (one m tile, every n
+    // tile) are consecutive and, with workgroup b running on die b % 8, on one
+    // die, so they share that die's L2 copy of their A tile
+    const int64_t gy = (p.N + GBN - 1) / GBN, ntiles = (int64_t)gridDim.x;
+    int64_t t = blockIdx.x;
+    if (t < ntiles / 8 * 8) t = (t % 8) * (ntiles / 8) + t / 8;
+    const int64_t m0 = (t / gy) * GBM, n0 = (t % gy) * GBN;
     const int64_t kb = p.k_split > 0 ? (int64_t)blockIdx.z * p.k_split : 0;
     int64_t ke = p.k_split > 0 ? kb + p.k_split : p.K;
     ke = ke < p.K ? ke : p.K;
@@ -186,23 +213,27 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     const OperandOffsets<128> off(lane);
     ta.init(p.a_rs, p.a_seg, p.a_segs, m0, p.M, tid);
     tb.init(p.b_rs, p.b_seg, p.b_segs, n0, p.N, tid);
-    ta.begin(p.a_rs, p.a_seg, p.a_segs, kb);
-    tb.begin(p.b_rs, p.b_seg, p.b_segs, kb);
-    if (nkt > 0) {
-        ta.load(p.a, ke);
-        tb.load(p.b, ke);
-        ta.store(sa[0], tid);
-        tb.store(sb[0], tid);
+    if (p.k_parts > 1) {  // (no split: kb = 0)
+        ta.begin(p.a_at[0], p.a_rs, p.a_seg, p.a_segs, 0, p.k_at[1]);
+        tb.begin(p.b_at[0], p.b_rs, p.b_seg, p.b_segs, 0, p.k_at[1]);
+    } else {
+        ta.begin(p.a, p.a_rs, p.a_seg, p.a_segs, kb, ke);
+        tb.begin(p.b, p.b_rs, p.b_seg, p.b_segs, kb, ke);
     }
-    __syncthreads();
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nkt) {
-            ta.advance(p.a_rs, p.a_seg, p.a_segs);
-            tb.advance(p.b_rs, p.b_seg, p.b_segs);
-            ta.load(p.a, ke);
-            tb.load(p.b, ke);
-        }
+    // k tiles: tile j is multiplied from LDS buffer j % 2; its operands were
+    // loaded into register set j % 2 two tiles earlier and stored to LDS at
+    // the end of tile j - 1, so every load has two tiles' time to land
+    auto fetch = [&](auto set) {
+        ta.advance(p, true, p.a_rs, p.a_seg, p.a_segs);
+        tb.advance(p, false, p.b_rs, p.b_seg, p.b_segs);
+        ta.template load<decltype(set)::value>(ke);
+        tb.template load<decltype(set)::value>(ke);
+    };
+    auto put = [&](auto set) {
+        ta.template store<decltype(set)::value>(sa[decltype(set)::value], tid);
+        tb.template store<decltype(set)::value>(sb[decltype(set)::value], tid);
+    };
+    auto multiply = [&](int buf) {
 #pragma unroll
         for (int ks = 0; ks < GBK / 16; ++ks) {
             bf16x8 bf[2], af[2];
@@ -215,11 +246,27 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma32(bf[nb], af[mb], acc[nb][mb]);
         }
-        if (kt + 1 < nkt) {
-            ta.store(sa[buf ^ 1], tid);
-            tb.store(sb[buf ^ 1], tid);
-        }
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    if (nkt > 0) {
+        ta.template load<0>(ke);
+        tb.template load<0>(ke);
+    }
+    if (nkt > 1) fetch(S1{});
+    if (nkt > 0) put(S0{});
+    __syncthreads();
+    for (int kt = 0; kt < nkt; kt += 2) {
+        if (kt + 2 < nkt) fetch(S0{});
+        multiply(0);
+        if (kt + 1 < nkt) put(S1{});
         __syncthreads();
+        if (kt + 1 < nkt) {
+            if (kt + 3 < nkt) fetch(S1{});
+            multiply(1);
+            if (kt + 2 < nkt) put(S0{});
+            __syncthreads();
+        }
     }
 
 #pragma unroll
@@ -274,13 +321,22 @@ hipError_t launch_gemm(const GemmParams& p, bool a_kc, bool b_kc, int splits, hi
     if ((a_kc || b_kc) && p.K % 8 != 0) return hipErrorInvalidValue;
     // a 64-wide k step of a k-contiguous operand stays inside one segment
     if ((a_kc && p.a_seg % GBK != 0) || (b_kc && p.b_seg % GBK != 0)) return hipErrorInvalidValue;
+    // reduction parts: ascending multiples of 64 from 0 to K, no split-K
+    if (p.k_parts > 1) {
+        if (p.k_parts > kGemmMaxParts || p.k_split != 0 || splits != 1 || p.k_at[0] != 0 ||
+            p.k_at[p.k_parts] != p.K)
+            return hipErrorInvalidValue;
+        for (int i = 0; i < p.k_parts; ++i)
+            if (p.k_at[i + 1] <= p.k_at[i] || p.k_at[i + 1] % GBK != 0 || !p.a_at[i] || !p.b_at[i])
+                return hipErrorInvalidValue;
+    }
     if (!a_kc && p.M % 8 != 0) return hipErrorInvalidValue;
     if (p.N % 8 != 0 || p.a_seg % 8 != 0 || p.b_seg % 8 != 0 || p.c_seg % 4 != 0 ||
         (p.k_split > 0 && p.k_split % GBK != 0) || splits < 1 || splits > 65535)
         return hipErrorInvalidValue;
     const int64_t gx = (p.M + GBM - 1) / GBM, gy = (p.N + GBN - 1) / GBN;
-    if (gx > 0x7fffffffLL || gy > 65535) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)splits), block(256);
+    if (gx * gy > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)(gx * gy), 1, (unsigned)splits), block(256);
     if (a_kc && b_kc) hipLaunchKernelGGL((gemm_kernel<true, true>), grid, block, 0, st, p);
     else if (a_kc) hipLaunchKernelGGL((gemm_kernel<true, false>), grid, block, 0, st, p);
     else if (b_kc) hipLaunchKernelGGL((gemm_kernel<false, true>), grid, block, 0, st, p);

@@ -785,13 +785,23 @@ int layer_bwd_run(Common& c, const LayerPlan& L, const uint16_t* x, const uint16
     uint16_t* dVc = reinterpret_cast<uint16_t*>(c.ws + L.dv_c);
     float* lse_c = reinterpret_cast<float*>(c.ws + L.lse_c);
     bool dx_started = false;
-    // dx += A(m = s, k) B(n, k) over k < K: A head-major [K / D][S][D] (k
-    // contiguous), B = rows r0.. of a weight [*][dm] read n-contiguous
-    auto dx_add = [&](const uint16_t* a, const uint16_t* w, int64_t K) -> int {
+    // dx += sum over parts i of A_i(m = s, k) B_i(n, k), k < K_i, in part
+    // order, in one product: A_i head-major [K_i / D][S][D] (k contiguous),
+    // B_i = rows of a weight [*][dm] read n-contiguous
+    auto dx_add = [&](int nparts, const uint16_t* const* a, const uint16_t* const* w,
+                      const int64_t* kk) -> int {
         hc::GemmParams g{};
-        g.a = a; g.a_rs = D; g.a_seg = D; g.a_segs = S * D;
-        g.b = w; g.b_rs = dm; g.b_seg = dm; g.b_segs = 0;
-        g.M = S; g.N = dm; g.K = K;
+        g.a = a[0]; g.a_rs = D; g.a_seg = D; g.a_segs = S * D;
+        g.b = w[0]; g.b_rs = dm; g.b_seg = dm; g.b_segs = 0;
+        g.M = S; g.N = dm; g.K = 0;
+        g.k_parts = nparts;
+        for (int i = 0; i < nparts; ++i) {
+            g.k_at[i] = g.K;
+            g.a_at[i] = a[i];
+            g.b_at[i] = w[i];
+            g.K += kk[i];
+        }
+        g.k_at[nparts] = g.K;
         g.c = dx; g.c_rs = dm; g.c_seg = dm; g.c_segs = 0;
         g.out_mode = dx_started ? hc::kGemmF32Add : hc::kGemmF32;
         dx_started = true;
@@ -841,20 +851,21 @@ int layer_bwd_run(Common& c, const LayerPlan& L, const uint16_t* x, const uint16
         dq.dq = dQc; dq.dq_rs = D; dq.dq_hs = S * D;
         LAUNCH(K_DQ, hc::launch_dq(dq, D, c.st));
         // per GQA group, ascending: dx += dQ_g Wq_g, then dK Wk + dV Wv when the
-        // group's last head is in this chunk; weight-gradient rows
+        // group's last head is in this chunk (one product, parts in that
+        // order); weight-gradient rows
         const int carry_out = p.carry_out_slot(ci) >= 0 ? 1 : 0;
         for (int kl = 0; kl < ch.nkv; ++kl) {
             const int kvg = ch.kv0 + kl;
             int hb = kvg * p.g, he = hb + p.g;
             hb = hb < ch.h0 ? ch.h0 : hb;
             he = he > ch.h0 + ch.nh ? ch.h0 + ch.nh : he;
-            const uint16_t* dq_g = dQc + (size_t)(hb - ch.h0) * S * D;
-            if ((r = dx_add(dq_g, wq + (size_t)hb * D * dm, (int64_t)(he - hb) * D))) return r;
             const bool done = !(carry_out && kl == ch.nkv - 1);
-            if (done) {
-                if ((r = dx_add(dKc + (size_t)kl * S * D, wk + (size_t)kvg * D * dm, D))) return r;
-                if ((r = dx_add(dVc + (size_t)kl * S * D, wv + (size_t)kvg * D * dm, D))) return r;
-            }
+            const uint16_t* a[3] = {dQc + (size_t)(hb - ch.h0) * S * D, dKc + (size_t)kl * S * D,
+                                    dVc + (size_t)kl * S * D};
+            const uint16_t* w[3] = {wq + (size_t)hb * D * dm, wk + (size_t)kvg * D * dm,
+                                    wv + (size_t)kvg * D * dm};
+            const int64_t kk[3] = {(int64_t)(he - hb) * D, D, D};
+            if ((r = dx_add(done ? 3 : 1, a, w, kk))) return r;
         }
         if ((r = w_rows(dQc, (int64_t)ch.nh * D, dwq + (size_t)ch.h0 * D * dm))) return r;
         const int nfin = ch.nkv - carry_out;

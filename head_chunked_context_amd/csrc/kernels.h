@@ -168,6 +168,13 @@ enum GemmOut : int {
     kGemmF32 = 1,     // C = A B in fp32
     kGemmF32Add = 2,  // C = C + A B in fp32 (accumulators start from C)
 };
+// The reduction may also run over up to kGemmMaxParts parts (k_parts > 1,
+// no split-K): part i covers k in [k_at[i], k_at[i + 1]) (boundaries
+// multiples of 64, k_at[0] = 0, k_at[k_parts] = K) and reads A from a_at[i]
+// and B from b_at[i] with the strides above, k counted from k_at[i]; one
+// product then adds several operand pairs in order, as the same products
+// launched one after another into an accumulating C would, bit for bit.
+constexpr int kGemmMaxParts = 3;
 struct GemmParams {
     const uint16_t* a; int64_t a_rs, a_seg, a_segs;
     const uint16_t* b; int64_t b_rs, b_seg, b_segs;
@@ -176,6 +183,10 @@ struct GemmParams {
     int out_mode;
     int64_t k_split;   // reduction indices per split (multiple of 64); 0 = no split
     int64_t c_zs;      // elements between the splits' fp32 partial outputs
+    int k_parts;       // 0 or 1: one part (a, b)
+    int64_t k_at[kGemmMaxParts + 1];
+    const uint16_t* a_at[kGemmMaxParts];
+    const uint16_t* b_at[kGemmMaxParts];
 };
 // out[m][n] (+ out[m][n] if add) = sum over z ascending of part[z * part_zs + m * N + n]
 struct GemmReduceParams {

@@ -443,8 +443,11 @@ hipError_t launch_dq(const DqParams& p, int HD, hipStream_t) {
     return hipSuccess;
 }
 
-// gemm_kernel<A_KC, B_KC> as launched by launch_gemm: every 16-byte operand
-// chunk a 128 x 32 tile load reads, and every C row segment the epilogue (and
+// gemm_kernel<A_KC, B_KC> as launched by launch_gemm (every tile of C once,
+// whatever the dispatch order): every 16-byte operand
+// chunk a 128 x 64 tile load reads (the kernel's per-thread offset plus its
+// per-step segment offset, which equals this formula while a k-contiguous
+// segment is a multiple of 64), and every C row segment the epilogue (and
 // the accumulating prologue) touches
 static const int kGemmBK = 64;  // reduction indices per operand tile load
 static void gemm_operand(const uint16_t* base, int64_t rs, int64_t seg, int64_t segs, bool kc,
@@ -463,11 +466,21 @@ static void gemm_operand(const uint16_t* base, int64_t rs, int64_t seg, int64_t 
 hipError_t launch_gemm(const GemmParams& p, bool a_kc, bool b_kc, int splits, hipStream_t) {
     if (p.M <= 0 || p.N <= 0) return hipSuccess;
     if ((a_kc || b_kc) && p.K % 8 != 0) return hipErrorInvalidValue;
+    if ((a_kc && p.a_seg % kGemmBK != 0) || (b_kc && p.b_seg % kGemmBK != 0)) return hipErrorInvalidValue;
+    if (p.k_parts > 1) {
+        if (p.k_parts > kGemmMaxParts || p.k_split != 0 || splits != 1 || p.k_at[0] != 0 ||
+            p.k_at[p.k_parts] != p.K)
+            return hipErrorInvalidValue;
+        for (int i = 0; i < p.k_parts; ++i)
+            if (p.k_at[i + 1] <= p.k_at[i] || p.k_at[i + 1] % kGemmBK != 0 || !p.a_at[i] || !p.b_at[i])
+                return hipErrorInvalidValue;
+    }
     if (!a_kc && p.M % 8 != 0) return hipErrorInvalidValue;
     if (p.N % 8 != 0 || p.a_seg % 8 != 0 || p.b_seg % 8 != 0 || p.c_seg % 4 != 0 ||
         (p.k_split > 0 && p.k_split % kGemmBK != 0) || splits < 1 || splits > 65535)
         return hipErrorInvalidValue;
     const int64_t gx = (p.M + 127) / 128, gy = (p.N + 127) / 128;
+    if (gx * gy > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     for (int z = 0; z < splits; ++z)
         for (int64_t bx = 0; bx < gx; ++bx)
             for (int64_t by = 0; by < gy; ++by) {
@@ -475,9 +488,20 @@ hipError_t launch_gemm(const GemmParams& p, bool a_kc, bool b_kc, int splits, hi
                 const int64_t kb = p.k_split > 0 ? (int64_t)z * p.k_split : 0;
                 int64_t ke = p.k_split > 0 ? kb + p.k_split : p.K;
                 ke = ke < p.K ? ke : p.K;
-                for (int64_t k0 = kb; k0 < ke; k0 += kGemmBK) {
-                    gemm_operand(p.a, p.a_rs, p.a_seg, p.a_segs, a_kc, m0, p.M, k0, ke, "gemm A");
-                    gemm_operand(p.b, p.b_rs, p.b_seg, p.b_segs, b_kc, n0, p.N, k0, ke, "gemm B");
+                if (p.k_parts > 1) {
+                    // part i: its own operands, k counted from the part's start
+                    for (int i = 0; i < p.k_parts; ++i) {
+                        const int64_t kl = p.k_at[i + 1] - p.k_at[i];
+                        for (int64_t k0 = 0; k0 < kl; k0 += kGemmBK) {
+                            gemm_operand(p.a_at[i], p.a_rs, p.a_seg, p.a_segs, a_kc, m0, p.M, k0, kl, "gemm A part");
+                            gemm_operand(p.b_at[i], p.b_rs, p.b_seg, p.b_segs, b_kc, n0, p.N, k0, kl, "gemm B part");
+                        }
+                    }
+                } else {
+                    for (int64_t k0 = kb; k0 < ke; k0 += kGemmBK) {
+                        gemm_operand(p.a, p.a_rs, p.a_seg, p.a_segs, a_kc, m0, p.M, k0, ke, "gemm A");
+                        gemm_operand(p.b, p.b_rs, p.b_seg, p.b_segs, b_kc, n0, p.N, k0, ke, "gemm B");
+                    }
                 }
                 const int esz = p.out_mode == kGemmBf16 ? 2 : 4;
                 const char* cz = (const char*)p.c + (int64_t)z * p.c_zs * esz;
