@@ -566,13 +566,23 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 f32x16 s[1], dp[1];
+                // MFMA j: S^T (even j) or dP^T (odd j) over d 16 (j / 2) ..;
+                // its A operand (K or V rows) is read DIST MFMAs ahead
+                constexpr int NJ = 2 * NS, DIST = 2;
+                auto read_a = [&](int j) {
+                    return lds_read_b128((j & 1) ? Vs : Ks, off.row[j >> 1] + b * 32 * HD * 2);
+                };
+                bf16x8 ring[DIST];
 #pragma unroll
-                for (int st = 0; st < NS; ++st) {
-                    const int o = off.row[st] + b * 32 * HD * 2;
-                    const bf16x8 ak = lds_read_b128(Ks, o);
-                    const bf16x8 av = lds_read_b128(Vs, o);
-                    s[0] = mfma32(ak, qf[st], st == 0 ? f32x16{} : s[0]);
-                    dp[0] = mfma32(av, df[st], st == 0 ? ndsplat : dp[0]);
+                for (int j = 0; j < DIST; ++j) ring[j] = read_a(j);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const bf16x8 a = ring[j % DIST];
+                    if (j + DIST < NJ) ring[j % DIST] = read_a(j + DIST);
+                    const int st = j >> 1;
+                    if (j & 1) dp[0] = mfma32(a, df[st], st == 0 ? ndsplat : dp[0]);
+                    else s[0] = mfma32(a, qf[st], st == 0 ? f32x16{} : s[0]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 bf16x8 dsb[1][2];
                 if (need_mask) {
