@@ -243,11 +243,13 @@ def run_workload(hcm, torch, w, hc, T, dev, steps, warmup, timing, kv_on_host, t
             "ws_fwd": fb, "ws_bwd": bb, "peak_intermediate": peak}
 
 
-def run_layer(hcm, torch, w, hc, dev, steps, warmup):
+def run_layer(hcm, torch, w, hc, dev, steps, warmup, keep_o=False):
     """The attention layer around the attention at workload w's shape with
     d_model = Hq * D: forward + backward, head chunk by head chunk.  Returns
     timings, workspace bytes and the peak intermediate device memory (torch's
-    peak-allocation delta over inputs, weights and outputs)."""
+    peak-allocation delta over inputs, weights and outputs).  keep_o: the
+    forward keeps the attention output and LSE for the backward, which then
+    skips recomputing them (kept_bytes: that activation)."""
     from head_chunked_context_amd.inputs import layer_inputs
     S, Hq, Hkv, D = w.S, w.Hq, w.Hkv, w.D
     dm = Hq * D
@@ -262,11 +264,21 @@ def run_layer(hcm, torch, w, hc, dev, steps, warmup):
     base = torch.cuda.memory_allocated(dev)
     ws = torch.empty(max(fb, bb), dtype=torch.uint8, device=dev)
     a = (inp["x"], inp["wq"], inp["wk"], inp["wv"], inp["wo"])
+    kept = None
+    if keep_o:
+        kept = (torch.empty((Hq, S, D), dtype=torch.bfloat16, device=dev),
+                torch.empty((Hq, S), dtype=torch.float32, device=dev))
 
     def step():
-        hcm.attn_layer_fwd(*a, Hq=Hq, Hkv=Hkv, D=D, head_chunk=hc, out=y, workspace=ws)
-        hcm.attn_layer_bwd(*a, inp["dy"], Hq=Hq, Hkv=Hkv, D=D, head_chunk=hc, grads=grads,
-                           workspace=ws)
+        if keep_o:
+            hcm.attn_layer_fwd(*a, Hq=Hq, Hkv=Hkv, D=D, head_chunk=hc, out=y, keep_o=True,
+                               o_keep=kept[0], lse=kept[1], workspace=ws)
+            hcm.attn_layer_bwd(*a, inp["dy"], Hq=Hq, Hkv=Hkv, D=D, head_chunk=hc, o_kept=kept[0],
+                               lse_kept=kept[1], grads=grads, workspace=ws)
+        else:
+            hcm.attn_layer_fwd(*a, Hq=Hq, Hkv=Hkv, D=D, head_chunk=hc, out=y, workspace=ws)
+            hcm.attn_layer_bwd(*a, inp["dy"], Hq=Hq, Hkv=Hkv, D=D, head_chunk=hc, grads=grads,
+                               workspace=ws)
 
     for _ in range(warmup):
         step()
@@ -284,7 +296,8 @@ def run_layer(hcm, torch, w, hc, dev, steps, warmup):
     hcm.timing_reset()
     ms = e0.elapsed_time(e1) / steps
     peak = torch.cuda.max_memory_allocated(dev) - base
-    print(f"layer {w.name}: head_chunk={hc}: {ms:.1f} ms per step", file=sys.stderr, flush=True)
+    print(f"layer {w.name}: head_chunk={hc}{', kept O' if keep_o else ''}: {ms:.1f} ms per step",
+          file=sys.stderr, flush=True)
     # counted work: attention 7*S^2*D*Hq, projections 2*S*dm*D*(2 Hq + 2 Hkv) forward and
     # twice that backward (the backward's recomputation is not counted)
     proj = 2.0 * S * dm * D * (2 * Hq + 2 * Hkv)
@@ -293,7 +306,8 @@ def run_layer(hcm, torch, w, hc, dev, steps, warmup):
     # backward recomputed projections, dO, dWo, dx and the weight gradients
     gemm_flops = 4 * proj - 2.0 * S * dm * D * Hq
     gemm_ms = kern["gemm"][1] / steps
-    return {"head_chunk": hc, "ms_per_step": round(ms, 1),
+    extra = {"keep_o": True, "kept_bytes": Hq * S * D * 2 + Hq * S * 4} if keep_o else {}
+    return {"head_chunk": hc, **extra, "ms_per_step": round(ms, 1),
             "tflops": round(flops / (ms / 1e3) / 1e12, 2),
             "kernel_ms_per_step": {f: round(kern[f][1] / steps, 2) for f in kern if kern[f][0]},
             "gemm_tflops": round(gemm_flops / (gemm_ms / 1e3) / 1e12, 1) if gemm_ms > 0 else None,
@@ -436,6 +450,7 @@ def main():
     if not args.no_layer and args.workload in (2, 3):
         torch.cuda.empty_cache()
         rows = [run_layer(hcm, torch, w, h, dev, 1, 1) for h in (hc, Hq)]
+        rows.append(run_layer(hcm, torch, w, hc, dev, 1, 1, keep_o=True))
         line["layer"] = {"d_model": Hq * D, "settings": rows,
                          "workspace_ratio": round(max(rows[0]["workspace_bytes"].values()) /
                                                   max(rows[1]["workspace_bytes"].values()), 4)}

@@ -705,23 +705,24 @@ hc::GemmParams proj_params(const uint16_t* x, const uint16_t* w, int rows, int64
 #define LAUNCH_GEMM(prm, akc, bkc, splits) \
     KCHK(timed(K_GEMM, c.st, 0.0, [&]() { return hc::launch_gemm((prm), (akc), (bkc), (splits), c.st); }))
 
-// the chunk's projections and attention output into the chunk buffers
+// the chunk's projections into the chunk buffers and, if Oc is given, its
+// attention output into Oc (head-major [nh][S][D]) with the LSE
 int layer_chunk_forward(Common& c, const LayerPlan& L, const hc::Chunk& ch, const uint16_t* x,
-                        const uint16_t* wq, const uint16_t* wk, const uint16_t* wv, float* lse,
-                        int64_t lse_hs) {
+                        const uint16_t* wq, const uint16_t* wk, const uint16_t* wv, uint16_t* Oc,
+                        float* lse, int64_t lse_hs) {
     const hc::Plan& p = L.at;
     const int64_t S = p.S;
     const int D = p.D, dm = L.dm;
     uint16_t* Qc = reinterpret_cast<uint16_t*>(c.ws + L.q_c);
     uint16_t* Kc = reinterpret_cast<uint16_t*>(c.ws + L.k_c);
     uint16_t* Vc = reinterpret_cast<uint16_t*>(c.ws + L.v_c);
-    uint16_t* Oc = reinterpret_cast<uint16_t*>(c.ws + L.o_c);
     hc::GemmParams g = proj_params(x, wq + (size_t)ch.h0 * D * dm, ch.nh * D, S, dm, D, Qc);
     LAUNCH_GEMM(g, true, true, 1);
     g = proj_params(x, wk + (size_t)ch.kv0 * D * dm, ch.nkv * D, S, dm, D, Kc);
     LAUNCH_GEMM(g, true, true, 1);
     g = proj_params(x, wv + (size_t)ch.kv0 * D * dm, ch.nkv * D, S, dm, D, Vc);
     LAUNCH_GEMM(g, true, true, 1);
+    if (Oc == nullptr) return ATTN_OK;
     hc::FwdParams f{};
     f.q = Qc; f.q_rs = D; f.q_hs = S * D;
     f.k = Kc; f.k_rs = D; f.k_hs = S * D;
@@ -736,17 +737,22 @@ int layer_chunk_forward(Common& c, const LayerPlan& L, const hc::Chunk& ch, cons
 }
 
 int layer_fwd_run(Common& c, const LayerPlan& L, const uint16_t* x, const uint16_t* wq,
-                  const uint16_t* wk, const uint16_t* wv, const uint16_t* wo, float* y, float* lse) {
+                  const uint16_t* wk, const uint16_t* wv, const uint16_t* wo, float* y, float* lse,
+                  uint16_t* o_keep) {
     const hc::Plan& p = L.at;
     const int64_t S = p.S;
     const int D = p.D, dm = L.dm;
     for (int ci = 0; ci < p.nchunks; ++ci) {
         const hc::Chunk ch = p.chunk(ci);
-        int r = layer_chunk_forward(c, L, ch, x, wq, wk, wv, lse ? lse + (size_t)ch.h0 * S : nullptr, S);
+        // the chunk's attention output: the reused chunk buffer, or its heads
+        // of the caller's kept output
+        uint16_t* Oc = o_keep ? o_keep + (size_t)ch.h0 * S * D : reinterpret_cast<uint16_t*>(c.ws + L.o_c);
+        int r = layer_chunk_forward(c, L, ch, x, wq, wk, wv, Oc,
+                                    lse ? lse + (size_t)ch.h0 * S : nullptr, S);
         if (r) return r;
         // y += O_c wo[:, h0 D .. (h0 + nh) D]^T
         hc::GemmParams g{};
-        g.a = reinterpret_cast<const uint16_t*>(c.ws + L.o_c); g.a_rs = D; g.a_seg = D; g.a_segs = S * D;
+        g.a = Oc; g.a_rs = D; g.a_seg = D; g.a_segs = S * D;
         g.b = wo + (size_t)ch.h0 * D; g.b_rs = (int64_t)p.Hq * D; g.b_seg = (int64_t)p.Hq * D; g.b_segs = 0;
         g.M = S; g.N = dm; g.K = (int64_t)ch.nh * D;
         g.c = y; g.c_rs = dm; g.c_seg = dm; g.c_segs = 0;
@@ -772,7 +778,8 @@ int wgrad(Common& c, const LayerPlan& L, hc::GemmParams g, float* out, int64_t o
 
 int layer_bwd_run(Common& c, const LayerPlan& L, const uint16_t* x, const uint16_t* wq,
                   const uint16_t* wk, const uint16_t* wv, const uint16_t* wo, const uint16_t* dy,
-                  float* dx, float* dwq, float* dwk, float* dwv, float* dwo) {
+                  const uint16_t* o_kept, const float* lse_kept, float* dx, float* dwq, float* dwk,
+                  float* dwv, float* dwo) {
     const hc::Plan& p = L.at;
     const int64_t S = p.S;
     const int D = p.D, dm = L.dm, Hq = p.Hq;
@@ -818,8 +825,12 @@ int layer_bwd_run(Common& c, const LayerPlan& L, const uint16_t* x, const uint16
     };
     for (int ci = 0; ci < p.nchunks; ++ci) {
         const hc::Chunk ch = p.chunk(ci);
-        int r = layer_chunk_forward(c, L, ch, x, wq, wk, wv, lse_c, S);
+        // the chunk's projections, and its attention output and LSE unless the
+        // forward kept them (the same kernels on the same inputs: same bits)
+        int r = layer_chunk_forward(c, L, ch, x, wq, wk, wv, o_kept ? nullptr : Oc, lse_c, S);
         if (r) return r;
+        const uint16_t* Ou = o_kept ? o_kept + (size_t)ch.h0 * S * D : Oc;
+        const float* lse_u = o_kept ? lse_kept + (size_t)ch.h0 * S : lse_c;
         // dO_c = dy wo[:, chunk columns]  (bf16, head-major, where prep reads it)
         hc::GemmParams g{};
         g.a = dy; g.a_rs = dm; g.a_seg = dm; g.a_segs = 0;
@@ -831,14 +842,14 @@ int layer_bwd_run(Common& c, const LayerPlan& L, const uint16_t* x, const uint16
         // dWo[:, chunk columns] = dy^T O_c
         g = hc::GemmParams{};
         g.a = dy; g.a_rs = dm; g.a_seg = dm; g.a_segs = 0;    // A(m, s) = dy[s][m]
-        g.b = Oc; g.b_rs = D; g.b_seg = D; g.b_segs = S * D;  // B(n, s) = O_c[n / D][s][n % D]
+        g.b = Ou; g.b_rs = D; g.b_seg = D; g.b_segs = S * D;  // B(n, s) = O_c[n / D][s][n % D]
         g.M = dm; g.N = (int64_t)ch.nh * D; g.K = S;
         if ((r = wgrad(c, L, g, dwo + (size_t)ch.h0 * D, (int64_t)Hq * D))) return r;
         // attention backward of the chunk (Delta from O_c, dO_c in place)
         hc::PrepParams pr{};
-        pr.o = Oc; pr.o_rs = D; pr.o_hs = S * D;
+        pr.o = Ou; pr.o_rs = D; pr.o_hs = S * D;
         pr.dO = dOc; pr.do_rs = D; pr.do_hs = S * D;
-        pr.lse = lse_c; pr.lse_hs = S;
+        pr.lse = lse_u; pr.lse_hs = S;
         pr.dO_c = dOc; pr.c_rs = D; pr.c_hs = S * D;
         pr.ndelta = reinterpret_cast<float*>(c.ws + p.delta_c); pr.ndelta_hs = S;
         pr.nlse2 = reinterpret_cast<float*>(c.ws + p.lse2_c); pr.nlse2_hs = S;
@@ -1043,8 +1054,8 @@ size_t attn_layer_bwd_workspace_bytes(int64_t S, int32_t d_model, int32_t Hq, in
 }
 
 int attn_layer_fwd(const void* x, const void* wq, const void* wk, const void* wv, const void* wo,
-                   float* y, float* lse, int64_t S, int32_t d_model, int32_t Hq, int32_t Hkv,
-                   int32_t D, int32_t causal, int32_t head_chunk, void* workspace,
+                   float* y, float* lse, void* o_keep, int64_t S, int32_t d_model, int32_t Hq,
+                   int32_t Hkv, int32_t D, int32_t causal, int32_t head_chunk, void* workspace,
                    size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     LayerPlan L;
@@ -1060,6 +1071,7 @@ int attn_layer_fwd(const void* x, const void* wq, const void* wk, const void* wv
     for (int i = 0; i < 7; ++i)
         if ((r = check_ptr(ins[i], names[i], false, nullptr))) return r;
     if (lse != nullptr && (r = check_ptr(lse, "lse", false, nullptr))) return r;
+    if (o_keep != nullptr && (r = check_ptr(o_keep, "o_keep", false, nullptr))) return r;
     Common c;
     init_common(c, L.at, workspace);
     if ((r = device_resources(&c.dev))) return r;
@@ -1067,15 +1079,16 @@ int attn_layer_fwd(const void* x, const void* wq, const void* wk, const void* wv
     if ((r = enter(c, static_cast<hipStream_t>(stream)))) return r;
     r = layer_fwd_run(c, L, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wq),
                       static_cast<const uint16_t*>(wk), static_cast<const uint16_t*>(wv),
-                      static_cast<const uint16_t*>(wo), y, lse);
+                      static_cast<const uint16_t*>(wo), y, lse, static_cast<uint16_t*>(o_keep));
     const int r2 = leave(c);
     return r ? r : r2;
 }
 
 int attn_layer_bwd(const void* x, const void* wq, const void* wk, const void* wv, const void* wo,
-                   const void* dy, float* dx, float* dwq, float* dwk, float* dwv, float* dwo,
-                   int64_t S, int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D, int32_t causal,
-                   int32_t head_chunk, void* workspace, size_t workspace_bytes, void* stream) {
+                   const void* dy, const void* o_kept, const float* lse_kept, float* dx, float* dwq,
+                   float* dwk, float* dwv, float* dwo, int64_t S, int32_t d_model, int32_t Hq,
+                   int32_t Hkv, int32_t D, int32_t causal, int32_t head_chunk, void* workspace,
+                   size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     LayerPlan L;
     int r = layer_plan(true, S, d_model, Hq, Hkv, D, causal, head_chunk, &L);
@@ -1090,6 +1103,12 @@ int attn_layer_bwd(const void* x, const void* wq, const void* wk, const void* wv
                            "workspace"};
     for (int i = 0; i < 12; ++i)
         if ((r = check_ptr(ins[i], names[i], false, nullptr))) return r;
+    if ((o_kept == nullptr) != (lse_kept == nullptr))
+        return fail(ATTN_EINVAL, "o_kept and lse_kept come together (both NULL: recompute)");
+    if (o_kept != nullptr) {
+        if ((r = check_ptr(o_kept, "o_kept", false, nullptr))) return r;
+        if ((r = check_ptr(lse_kept, "lse_kept", false, nullptr))) return r;
+    }
     Common c;
     init_common(c, L.at, workspace);
     if ((r = device_resources(&c.dev))) return r;
@@ -1097,13 +1116,13 @@ int attn_layer_bwd(const void* x, const void* wq, const void* wk, const void* wv
     if ((r = enter(c, static_cast<hipStream_t>(stream)))) return r;
     r = layer_bwd_run(c, L, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wq),
                       static_cast<const uint16_t*>(wk), static_cast<const uint16_t*>(wv),
-                      static_cast<const uint16_t*>(wo), static_cast<const uint16_t*>(dy), dx, dwq,
-                      dwk, dwv, dwo);
+                      static_cast<const uint16_t*>(wo), static_cast<const uint16_t*>(dy),
+                      static_cast<const uint16_t*>(o_kept), lse_kept, dx, dwq, dwk, dwv, dwo);
     const int r2 = leave(c);
     return r ? r : r2;
 }
 
-const char* attn_version(void) { return "0.2.0"; }
+const char* attn_version(void) { return "0.3.0"; }
 
 int attn_timing_enable(int on) { return g_timing.exchange(on ? 1 : 0); }
 

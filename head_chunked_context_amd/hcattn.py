@@ -58,9 +58,9 @@ def lib():
     L.attn_layer_fwd_workspace_bytes.restype = sz
     L.attn_layer_bwd_workspace_bytes.argtypes = lshape
     L.attn_layer_bwd_workspace_bytes.restype = sz
-    L.attn_layer_fwd.argtypes = [vp] * 7 + lshape + [vp, sz, vp]
+    L.attn_layer_fwd.argtypes = [vp] * 8 + lshape + [vp, sz, vp]
     L.attn_layer_fwd.restype = ctypes.c_int
-    L.attn_layer_bwd.argtypes = [vp] * 11 + lshape + [vp, sz, vp]
+    L.attn_layer_bwd.argtypes = [vp] * 13 + lshape + [vp, sz, vp]
     L.attn_layer_bwd.restype = ctypes.c_int
     L.attn_last_error.argtypes = []
     L.attn_last_error.restype = ctypes.c_char_p
@@ -294,37 +294,52 @@ def layer_bwd_workspace_bytes(S, d_model, Hq, Hkv, D, causal=True, head_chunk=0)
 
 def attn_layer_fwd(x, wq, wk, wv, wo, *, Hq: int, Hkv: int, D: int, head_chunk: int = 0,
                    causal: bool = True, out=None, lse=None, with_lse: bool = False,
-                   workspace=None):
+                   keep_o: bool = False, o_keep=None, workspace=None):
     """y = attention(x wq^T, x wk^T, x wv^T) wo^T walked head chunk by head chunk
     (attn_layer_fwd).  x [S, d_model] bf16; weights [out, in] bf16.  Returns
-    (y [S, d_model] fp32, lse [Hq, S] fp32 or None)."""
+    (y [S, d_model] fp32, lse [Hq, S] fp32 or None), plus the attention output
+    o [Hq, S, D] bf16 as a third element when keep_o (it implies with_lse):
+    attn_layer_bwd(..., o_kept=o, lse_kept=lse) then skips recomputing it."""
     S, dm, specs = _layer_specs(x, wq, wk, wv, wo, Hq, Hkv, D)
+    with_lse = with_lse or keep_o
     specs += [("out", out, (S, dm), torch.float32),
-              ("lse", lse if with_lse else None, (Hq, S), torch.float32)]
+              ("lse", lse if with_lse else None, (Hq, S), torch.float32),
+              ("o_keep", o_keep if keep_o else None, (Hq, S, D), torch.bfloat16)]
     dev, _ = _validate(specs, ())
     y = torch.empty((S, dm), dtype=torch.float32, device=dev) if out is None else out
     l = None
     if with_lse:
         l = torch.empty((Hq, S), dtype=torch.float32, device=dev) if lse is None else lse
+    ok = None
+    if keep_o:
+        ok = torch.empty((Hq, S, D), dtype=torch.bfloat16, device=dev) if o_keep is None else o_keep
     nb = layer_fwd_workspace_bytes(S, dm, Hq, Hkv, D, causal, head_chunk)
     ws = _workspace(nb, dev, workspace)
     _check(lib().attn_layer_fwd(x.data_ptr(), wq.data_ptr(), wk.data_ptr(), wv.data_ptr(),
                                 wo.data_ptr(), y.data_ptr(), l.data_ptr() if l is not None else None,
+                                ok.data_ptr() if ok is not None else None,
                                 S, dm, Hq, Hkv, D, int(causal), head_chunk, ws.data_ptr(), nb,
                                 _stream(dev)))
-    return y, l
+    return (y, l, ok) if keep_o else (y, l)
 
 
 def attn_layer_bwd(x, wq, wk, wv, wo, dy, *, Hq: int, Hkv: int, D: int, head_chunk: int = 0,
-                   causal: bool = True, grads=None, workspace=None):
+                   causal: bool = True, o_kept=None, lse_kept=None, grads=None, workspace=None):
     """Gradients of sum(y * dy) through attn_layer_fwd (attn_layer_bwd): returns
-    fp32 (dx, dwq, dwk, dwv, dwo).  dy [S, d_model] bf16."""
+    fp32 (dx, dwq, dwk, dwv, dwo).  dy [S, d_model] bf16.  o_kept / lse_kept: the
+    attention output and LSE a forward kept (keep_o=True), or both None to
+    recompute them; the results are bitwise the same."""
     S, dm, specs = _layer_specs(x, wq, wk, wv, wo, Hq, Hkv, D)
+    if (o_kept is None) != (lse_kept is None):
+        raise ValueError("o_kept and lse_kept come together (both None: recompute)")
     f32 = torch.float32
     shapes = [(S, dm), (Hq * D, dm), (Hkv * D, dm), (Hkv * D, dm), (dm, Hq * D)]
     names = ("dx", "dwq", "dwk", "dwv", "dwo")
     grads = list(grads) if grads is not None else [None] * 5
     specs += [("dy", dy, (S, dm), torch.bfloat16)]
+    if o_kept is not None:
+        specs += [("o_kept", o_kept, (Hq, S, D), torch.bfloat16),
+                  ("lse_kept", lse_kept, (Hq, S), f32)]
     specs += [(n, g, sh, f32) for n, g, sh in zip(names, grads, shapes)]
     dev, _ = _validate(specs, ())
     grads = [torch.empty(sh, dtype=f32, device=dev) if g is None else g
@@ -332,7 +347,10 @@ def attn_layer_bwd(x, wq, wk, wv, wo, dy, *, Hq: int, Hkv: int, D: int, head_chu
     nb = layer_bwd_workspace_bytes(S, dm, Hq, Hkv, D, causal, head_chunk)
     ws = _workspace(nb, dev, workspace)
     _check(lib().attn_layer_bwd(x.data_ptr(), wq.data_ptr(), wk.data_ptr(), wv.data_ptr(),
-                                wo.data_ptr(), dy.data_ptr(), *[g.data_ptr() for g in grads],
+                                wo.data_ptr(), dy.data_ptr(),
+                                o_kept.data_ptr() if o_kept is not None else None,
+                                lse_kept.data_ptr() if lse_kept is not None else None,
+                                *[g.data_ptr() for g in grads],
                                 S, dm, Hq, Hkv, D, int(causal), head_chunk, ws.data_ptr(), nb,
                                 _stream(dev)))
     return tuple(grads)

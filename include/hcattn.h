@@ -197,6 +197,11 @@ int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float
  *   y        : fp32 [S][d_model] = attention(x wq^T, x wk^T, x wv^T) wo^T,
  *              accumulated over chunks in fp32 (written, not added to).
  *   lse      : fp32 [Hq][S] or NULL, as attn_fwd.
+ *   o_keep   : bf16 [Hq][S][D] (head-major) or NULL.  When given, receives
+ *              the attention output before the output projection, for an
+ *              attn_layer_bwd that then skips recomputing it (pass lse too).
+ *              The caller owns it; it is an activation kept from forward to
+ *              backward, outside the workspace.
  *   d_model a positive multiple of 64; other shape rules as attn_fwd; no
  *   key/value trunks; no bias or rotary embedding.
  * The chunk's projections are written head-major by the library's matrix
@@ -207,8 +212,8 @@ int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float
 size_t attn_layer_fwd_workspace_bytes(int64_t S, int32_t d_model, int32_t Hq, int32_t Hkv,
                                       int32_t D, int32_t causal, int32_t head_chunk);
 int attn_layer_fwd(const void* x, const void* wq, const void* wk, const void* wv, const void* wo,
-                   float* y, float* lse, int64_t S, int32_t d_model, int32_t Hq, int32_t Hkv,
-                   int32_t D, int32_t causal, int32_t head_chunk, void* workspace,
+                   float* y, float* lse, void* o_keep, int64_t S, int32_t d_model, int32_t Hq,
+                   int32_t Hkv, int32_t D, int32_t causal, int32_t head_chunk, void* workspace,
                    size_t workspace_bytes, void* stream);
 
 /*
@@ -221,13 +226,20 @@ int attn_layer_fwd(const void* x, const void* wq, const void* wk, const void* wv
  * dx += dQ_g wq_g (+ dK wk + dV wv once the group's last head is done),
  * dwq = dQ^T x, dwk = dK^T x, dwv = dV^T x.  Bitwise identical for every
  * head_chunk.
+ *   o_kept, lse_kept : both NULL (recompute), or the o_keep and lse a forward
+ *              on the same x and weights (any head_chunk) wrote: the chunk's
+ *              attention output is then read from them instead of being
+ *              recomputed (the projections still are).  Results are bitwise
+ *              identical either way.  One given without the other is
+ *              ATTN_EINVAL.  The workspace is the same in both modes.
  */
 size_t attn_layer_bwd_workspace_bytes(int64_t S, int32_t d_model, int32_t Hq, int32_t Hkv,
                                       int32_t D, int32_t causal, int32_t head_chunk);
 int attn_layer_bwd(const void* x, const void* wq, const void* wk, const void* wv, const void* wo,
-                   const void* dy, float* dx, float* dwq, float* dwk, float* dwv, float* dwo,
-                   int64_t S, int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D, int32_t causal,
-                   int32_t head_chunk, void* workspace, size_t workspace_bytes, void* stream);
+                   const void* dy, const void* o_kept, const float* lse_kept, float* dx, float* dwq,
+                   float* dwk, float* dwv, float* dwo, int64_t S, int32_t d_model, int32_t Hq,
+                   int32_t Hkv, int32_t D, int32_t causal, int32_t head_chunk, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /* This thread's message for the last non-zero status ("" if none). */
 const char* attn_last_error(void);

@@ -650,7 +650,8 @@ static void run_case(int64_t S, int Hq, int Hkv, int D, int causal, int hc, int6
     if (rc != ATTN_OK) fail_msg("attn_bwd returned %llu (%llu)", attn_last_error(), (size_t)rc, 0);
 }
 
-// one attn_layer_fwd + attn_layer_bwd pair on exactly sized buffers; the
+// attn_layer_fwd and attn_layer_bwd, each without and with the kept
+// attention output, on exactly sized buffers; the
 // workspace regions restate the layer's carve: the attention plan's regions,
 // then O_c (and for the backward LSE_c, dQ_c, dK_c, dV_c and the split-K
 // partials of the weight gradients)
@@ -659,8 +660,9 @@ static void run_layer_case(int64_t S, int dm, int Hq, int Hkv, int D, int causal
     snprintf(name, sizeof name, "layer S=%lld dm=%d Hq=%d Hkv=%d D=%d causal=%d hc=%d",
              (long long)S, dm, Hq, Hkv, D, causal, hc);
     g_case = name;
-    Buffer x, wq, wk, wv, wo, y, lse, dy, dx, dwq, dwk, dwv, dwo;
+    Buffer x, wq, wk, wv, wo, y, lse, dy, dx, dwq, dwk, dwv, dwo, o;
     x.mem.resize((size_t)S * dm * 2); dy.mem.resize((size_t)S * dm * 2);
+    o.mem.resize((size_t)Hq * S * D * 2);
     wq.mem.resize((size_t)Hq * D * dm * 2); wo.mem.resize((size_t)Hq * D * dm * 2);
     wk.mem.resize((size_t)Hkv * D * dm * 2); wv.mem.resize((size_t)Hkv * D * dm * 2);
     y.mem.resize((size_t)S * dm * 4); dx.mem.resize((size_t)S * dm * 4);
@@ -678,10 +680,10 @@ static void run_layer_case(int64_t S, int dm, int Hq, int Hkv, int D, int causal
     char* wb = bbuf.data() + (256 - (uintptr_t)bbuf.data() % 256) % 256;
     g_regions.clear();
     g_allocs.clear();
-    Buffer* bufs[] = {&x, &wq, &wk, &wv, &wo, &y, &lse, &dy, &dx, &dwq, &dwk, &dwv, &dwo};
+    Buffer* bufs[] = {&x, &wq, &wk, &wv, &wo, &y, &lse, &dy, &dx, &dwq, &dwk, &dwv, &dwo, &o};
     const char* names[] = {"x", "wq", "wk", "wv", "wo", "y", "lse", "dy", "dx", "dwq", "dwk",
-                           "dwv", "dwo"};
-    for (int i = 0; i < 13; ++i) {
+                           "dwv", "dwo", "o_keep"};
+    for (int i = 0; i < 14; ++i) {
         add_region(bufs[i]->p(), bufs[i]->mem.size(), names[i]);
         g_allocs.push_back({(uintptr_t)bufs[i]->p(), (uintptr_t)bufs[i]->p() + bufs[i]->mem.size(),
                             false});
@@ -689,7 +691,10 @@ static void run_layer_case(int64_t S, int dm, int Hq, int Hkv, int D, int causal
     const size_t keep = g_regions.size();
     const size_t E = (size_t)S * D * 2;
     char msg[256];
-    for (int bwd = 0; bwd < 2; ++bwd) {
+    // forward, forward keeping O, backward recomputing O, backward reading it
+    for (int it = 0; it < 4; ++it) {
+        const int bwd = it >= 2;
+        const bool kept = it & 1;
         hc::Plan p;
         hc::make_plan(bwd, S, Hq, Hkv, D, causal, hc, 0, &p, msg, sizeof msg, g_gl_min_s);
         char* ws = bwd ? wb : wf;
@@ -715,9 +720,10 @@ static void run_layer_case(int64_t S, int dm, int Hq, int Hkv, int D, int causal
         int rc;
         if (!bwd)
             rc = attn_layer_fwd(x.p(), wq.p(), wk.p(), wv.p(), wo.p(), (float*)y.p(), (float*)lse.p(),
-                                S, dm, Hq, Hkv, D, causal, hc, wf, nf, nullptr);
+                                kept ? o.p() : nullptr, S, dm, Hq, Hkv, D, causal, hc, wf, nf, nullptr);
         else
-            rc = attn_layer_bwd(x.p(), wq.p(), wk.p(), wv.p(), wo.p(), dy.p(), (float*)dx.p(),
+            rc = attn_layer_bwd(x.p(), wq.p(), wk.p(), wv.p(), wo.p(), dy.p(), kept ? o.p() : nullptr,
+                                kept ? (const float*)lse.p() : nullptr, (float*)dx.p(),
                                 (float*)dwq.p(), (float*)dwk.p(), (float*)dwv.p(), (float*)dwo.p(),
                                 S, dm, Hq, Hkv, D, causal, hc, wb, nb, nullptr);
         if (rc != ATTN_OK)

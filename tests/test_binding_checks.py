@@ -79,3 +79,33 @@ def test_tensors_off_the_gpu_are_rejected_before_the_library():
         hc.attn_fwd(**fwd_args())
     with pytest.raises(ValueError, match="q must be on a GPU"):
         hc.attn_bwd(**bwd_args())
+
+
+DM = HQ * D
+
+
+def layer_args():
+    return dict(x=t(S, DM), wq=t(HQ * D, DM), wk=t(HKV * D, DM), wv=t(HKV * D, DM),
+                wo=t(DM, HQ * D))
+
+
+def test_layer_forward_checks_the_kept_output():
+    a = layer_args()
+    with pytest.raises(ValueError, match="o_keep has shape"):
+        hc.attn_layer_fwd(*a.values(), Hq=HQ, Hkv=HKV, D=D, keep_o=True, o_keep=t(S, HQ, D))
+    with pytest.raises(ValueError, match="o_keep has dtype"):
+        hc.attn_layer_fwd(*a.values(), Hq=HQ, Hkv=HKV, D=D, keep_o=True,
+                          o_keep=t(HQ, S, D, dtype=torch.float32))
+
+
+def test_layer_backward_checks_the_kept_output_and_lse():
+    a = list(layer_args().values()) + [t(S, DM)]
+    with pytest.raises(ValueError, match="come together"):
+        hc.attn_layer_bwd(*a, Hq=HQ, Hkv=HKV, D=D, o_kept=t(HQ, S, D))
+    with pytest.raises(ValueError, match="come together"):
+        hc.attn_layer_bwd(*a, Hq=HQ, Hkv=HKV, D=D, lse_kept=t(HQ, S, dtype=torch.float32))
+    with pytest.raises(ValueError, match="o_kept has shape"):
+        hc.attn_layer_bwd(*a, Hq=HQ, Hkv=HKV, D=D, o_kept=t(S, HQ, D),
+                          lse_kept=t(HQ, S, dtype=torch.float32))
+    with pytest.raises(ValueError, match="lse_kept has dtype"):
+        hc.attn_layer_bwd(*a, Hq=HQ, Hkv=HKV, D=D, o_kept=t(HQ, S, D), lse_kept=t(HQ, S))

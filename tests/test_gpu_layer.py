@@ -121,3 +121,47 @@ def test_llama3_8b_layer_full_size_sampled_rows_and_head_chunks():
     lerr = float(np.max(np.abs(f64(lse[:, rows]) - rl)))
     print(f"  lse rows: max-abs {lerr:.3e}", flush=True)
     assert lerr <= 1e-2
+
+
+@pytest.mark.parametrize("S,dm,Hq,Hkv,D,causal,hc_f,hc_b", [
+    (300, 128, 8, 2, 64, True, 8, 3),      # groups split across chunks, ragged S
+    (1000, 256, 4, 2, 128, True, 4, 1),
+    (513, 192, 4, 1, 128, False, 3, 4),    # non-causal, ragged chunk
+])
+def test_layer_backward_from_kept_output_is_bitwise_the_recomputing_one(S, dm, Hq, Hkv, D, causal,
+                                                                        hc_f, hc_b):
+    # the forward keeps the attention output and LSE (keep_o); a backward that
+    # reads them instead of recomputing gives the same bits, whatever the two
+    # calls' head_chunk, and the forward's y is unchanged by keeping
+    inp = layer_inputs(S, dm, Hq, Hkv, D, 90 + S % 13)
+    d = {n: t.to(DEV) for n, t in inp.items()}
+    w = (d["x"], d["wq"], d["wk"], d["wv"], d["wo"])
+    print(f"layer keep-O S={S} dm={dm} Hq={Hq} Hkv={Hkv} D={D} causal={causal} "
+          f"hc {hc_f} / {hc_b}", flush=True)
+    y0, l0 = attn_layer_fwd(*w, Hq=Hq, Hkv=Hkv, D=D, head_chunk=hc_f, causal=causal, with_lse=True)
+    y1, l1, o1 = attn_layer_fwd(*w, Hq=Hq, Hkv=Hkv, D=D, head_chunk=hc_f, causal=causal,
+                                keep_o=True)
+    g0 = attn_layer_bwd(*w, d["dy"], Hq=Hq, Hkv=Hkv, D=D, head_chunk=hc_b, causal=causal)
+    g1 = attn_layer_bwd(*w, d["dy"], Hq=Hq, Hkv=Hkv, D=D, head_chunk=hc_b, causal=causal,
+                        o_kept=o1, lse_kept=l1)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(l0, l1)
+    for a, b, n in zip(g0, g1, ("dx", "dwq", "dwk", "dwv", "dwo")):
+        assert torch.equal(a, b), f"{n} differs between kept and recomputed attention output"
+
+
+def test_kept_output_is_the_attention_output_head_major():
+    # identity projections: the kept output is attn_fwd's output, head-major
+    from head_chunked_context_amd import attn_fwd
+    S, Hq, D = 640, 2, 128
+    dm = Hq * D
+    g = torch.Generator(device="cpu").manual_seed(6)
+    x = torch.randn((S, dm), generator=g).to(torch.bfloat16).to(DEV)
+    eye = torch.eye(dm, dtype=torch.bfloat16, device=DEV)
+    y, lse, o = attn_layer_fwd(x, eye, eye, eye, eye, Hq=Hq, Hkv=Hq, D=D, head_chunk=1,
+                               keep_o=True)
+    xs = x.view(S, Hq, D).contiguous()
+    ref, l = attn_fwd(xs, xs, xs, head_chunk=2)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref.permute(1, 0, 2).contiguous())
+    assert torch.equal(lse, l)
