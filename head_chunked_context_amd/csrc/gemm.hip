@@ -17,7 +17,7 @@
 // Workgroup = 4 waves on a 128 x 128 tile of C, 2 x 2 waves of 64 x 64; K in
 // steps of 64 staged through LDS (global -> registers two steps ahead, two
 // register sets; registers -> LDS double-buffered, one barrier per step).  A
-// k-contiguous operand tile is [128][64] with rows padded by 16 bytes
+// k-contiguous operand tile is [128][64] with rows padded by 8 bytes
 // (conflict-free 8-byte reads); an m- or n-contiguous one
 // is [64][128] with the XOR-swizzled rows of the attention kernels, read
 // transposed by ds_read_b64_tr_b16.  Both reads deliver the 16 reduction
@@ -44,7 +44,10 @@ namespace hc {
 namespace {
 
 constexpr int GBM = 128, GBN = 128, GBK = 64;
-constexpr int KC_PITCH = GBK + 8;  // bf16 per padded row of a k-contiguous tile (16 B pad)
+// bf16 per padded row of a k-contiguous tile: 136 bytes, so that the 32 rows
+// one 8-byte read pass touches start 34 words apart, on 32 distinct even banks
+// of the 64 (a 16-byte pad repeats the banks every 16 rows: 2-way conflicts)
+constexpr int KC_PITCH = GBK + 4;
 
 // 16 reduction indices of one MFMA step from a k-contiguous [rows][KC_PITCH]
 // tile, row `row`, in the transposed-read order
@@ -139,10 +142,15 @@ struct OperandTile {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int idx = tid + i * 256;
-            int o;
-            if constexpr (KC) o = (idx / KCH) * (KC_PITCH * 2) + (idx % KCH) * 16;
-            else o = lds_off<128>(idx / 16, (idx % 16) * 8);
-            *reinterpret_cast<uint4*>(lds + o) = r[SET][i];
+            if constexpr (KC) {
+                // 8-byte aligned rows: the chunk goes in two 8-byte halves
+                const int o = (idx / KCH) * (KC_PITCH * 2) + (idx % KCH) * 16;
+                const uint4 v = r[SET][i];
+                *reinterpret_cast<uint2*>(lds + o) = make_uint2(v.x, v.y);
+                *reinterpret_cast<uint2*>(lds + o + 8) = make_uint2(v.z, v.w);
+            } else {
+                *reinterpret_cast<uint4*>(lds + lds_off<128>(idx / 16, (idx % 16) * 8)) = r[SET][i];
+            }
         }
     }
 };
