@@ -35,6 +35,10 @@
 static bool g_plant = false;
 static int64_t g_gl_min_s = hc::kGroupLoopMinS;  // the library's group-loop threshold
 static long g_fails = 0, g_checks = 0;
+// failure injection: the copy / kernel launch with this index (counted from
+// when it is armed) fails; -1 = none
+static long g_copy_fail_at = -1, g_copy_calls = 0, g_launch_fail_at = -1, g_launch_calls = 0;
+static bool inject_launch() { return g_launch_fail_at >= 0 && g_launch_calls++ == g_launch_fail_at; }
 static std::string g_case;
 
 // ------------------------------------------------------------ buffer model
@@ -117,6 +121,7 @@ hipError_t hipPointerGetAttributes(hipPointerAttribute_t* a, const void* p) {
 }
 hipError_t hipMemcpy2DAsync(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width,
                             size_t height, hipMemcpyKind, hipStream_t) {
+    if (g_copy_fail_at >= 0 && g_copy_calls++ == g_copy_fail_at) return hipErrorInvalidValue;
     for (size_t r = 0; r < height; ++r) {
         touch((const void*)((uintptr_t)src + r * spitch), (int64_t)width, "copy source row");
         touch((const void*)((uintptr_t)dst + r * dpitch), (int64_t)width, "copy destination row");
@@ -162,6 +167,7 @@ static void vec64(const float* src, int64_t nvalid, const char* what) {
 }
 
 hipError_t launch_pack(const PackParams& p, hipStream_t) {
+    if (inject_launch()) return hipErrorLaunchFailure;
     if (p.nh <= 0 || p.rows <= 0) return hipSuccess;
     for (int64_t h = 0; h < p.nh; ++h)
         for (int64_t row = 0; row < p.rows; ++row) {
@@ -172,6 +178,7 @@ hipError_t launch_pack(const PackParams& p, hipStream_t) {
 }
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t) {
+    if (inject_launch()) return hipErrorLaunchFailure;
     if (p.nh <= 0 || p.rows <= 0) return hipSuccess;
     for (int64_t h = 0; h < p.nh; ++h)
         for (int64_t row = 0; row < p.rows; ++row) {
@@ -189,6 +196,7 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t) {
 }
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t) {
+    if (inject_launch()) return hipErrorLaunchFailure;
     if (p.nh <= 0 || p.rows <= 0) return hipSuccess;
     for (int64_t h = 0; h < p.nh; ++h)
         for (int64_t row = 0; row < p.rows; ++row) {
@@ -204,6 +212,7 @@ hipError_t launch_prep(const PrepParams& p, hipStream_t) {
 
 // fwd_kernel<HD, NW> as launched by launch_fwd
 hipError_t launch_fwd(const FwdParams& p, int HD, hipStream_t) {
+    if (inject_launch()) return hipErrorLaunchFailure;
     if (p.nq <= 0 || p.nh <= 0) return hipSuccess;
     const bool wide = (p.nq + 255) / 256 * p.nh >= kWideMinBlocks;
     const int NW = wide ? 8 : 4, WQ = 32, BM = NW * WQ, BN = 64;
@@ -260,6 +269,7 @@ hipError_t launch_fwd(const FwdParams& p, int HD, hipStream_t) {
 
 // dkdv_kernel<HD, RUNS, GLOOP> as launched by launch_dkdv
 hipError_t launch_dkdv(const DkdvParams& p, int HD, hipStream_t) {
+    if (inject_launch()) return hipErrorLaunchFailure;
     const int units = p.group_loop ? p.nkv : p.nh;
     if (p.nk <= 0 || units <= 0) return hipSuccess;
     const int BQ = 64, BNK = 128;
@@ -366,6 +376,7 @@ hipError_t launch_dkdv(const DkdvParams& p, int HD, hipStream_t) {
 }
 
 hipError_t launch_dkdv_reduce(const DkdvReduceParams& p, hipStream_t) {
+    if (inject_launch()) return hipErrorLaunchFailure;
     if (p.nk <= 0 || p.nkv <= 0) return hipSuccess;
     for (int kvl = 0; kvl < p.nkv; ++kvl) {
         const int kvg = p.kv_base + kvl;
@@ -395,6 +406,7 @@ hipError_t launch_dkdv_reduce(const DkdvReduceParams& p, hipStream_t) {
 
 // dq_kernel<HD, NW> as launched by launch_dq
 hipError_t launch_dq(const DqParams& p, int HD, hipStream_t) {
+    if (inject_launch()) return hipErrorLaunchFailure;
     if (p.nq <= p.q_begin || p.nh <= 0) return hipSuccess;
     const bool wide = ((p.nq + 255) / 256 - p.q_begin / 256) * p.nh >= kWideMinBlocks;
     const int bm = wide ? 256 : 128;
@@ -464,6 +476,7 @@ static void gemm_operand(const uint16_t* base, int64_t rs, int64_t seg, int64_t 
 }
 
 hipError_t launch_gemm(const GemmParams& p, bool a_kc, bool b_kc, int splits, hipStream_t) {
+    if (inject_launch()) return hipErrorLaunchFailure;
     if (p.M <= 0 || p.N <= 0) return hipSuccess;
     if ((a_kc || b_kc) && p.K % 8 != 0) return hipErrorInvalidValue;
     if ((a_kc && p.a_seg % kGemmBK != 0) || (b_kc && p.b_seg % kGemmBK != 0)) return hipErrorInvalidValue;
@@ -515,6 +528,7 @@ hipError_t launch_gemm(const GemmParams& p, bool a_kc, bool b_kc, int splits, hi
 }
 
 hipError_t launch_gemm_reduce(const GemmReduceParams& p, hipStream_t) {
+    if (inject_launch()) return hipErrorLaunchFailure;
     if (p.M <= 0 || p.N <= 0) return hipSuccess;
     if (p.N % 4 != 0 || p.splits < 1) return hipErrorInvalidValue;
     for (int64_t m = 0; m < p.M; ++m) {
@@ -590,6 +604,45 @@ static void add_workspace(char* ws, const hc::Plan& p) {
 }
 
 // one attn_fwd + attn_bwd call pair on exactly sized buffers
+// one armed failure: ABI call `call` (0 forward, 1 backward) sees the copy
+// (copy) or kernel launch with index `at` of that call fail
+struct Inject {
+    int call = -1;
+    bool copy = false;
+    long at = 0;
+};
+static Inject g_inj;
+static long g_inject_hits = 0;
+
+// one ABI call.  With the failure armed for it, the call must return
+// ATTN_EHIP naming the failing HIP call, and the same call unarmed must then
+// succeed: an error leaves nothing half-done that breaks the next call.
+template <class F>
+static void checked_call(int which, const char* what, F&& f) {
+    const bool armed = g_inj.call == which;
+    if (armed) {
+        g_copy_calls = g_launch_calls = 0;
+        (g_inj.copy ? g_copy_fail_at : g_launch_fail_at) = g_inj.at;
+    }
+    int rc = f();
+    const bool hit = armed && (g_inj.copy ? g_copy_calls : g_launch_calls) > g_inj.at;
+    g_copy_fail_at = g_launch_fail_at = -1;
+    if (!hit) {
+        if (rc != ATTN_OK) fail_msg("call returned %llu (%llu)", what, (size_t)rc, 0);
+        return;
+    }
+    const char* want = g_inj.copy ? "hipMemcpy2DAsync" : "launch_";
+    if (rc != ATTN_EHIP || strstr(attn_last_error(), want) == nullptr) {
+        fprintf(stderr, "  injected failure, message: %s\n", attn_last_error());
+        fail_msg("an injected failure returned %llu (%llu), not ATTN_EHIP naming the call", what,
+                 (size_t)rc, 0);
+        return;
+    }
+    ++g_inject_hits;
+    rc = f();
+    if (rc != ATTN_OK) fail_msg("the call after an injected failure returned %llu (%llu)", what, (size_t)rc, 0);
+}
+
 static void run_case(int64_t S, int Hq, int Hkv, int D, int causal, int hc, int64_t T, bool host) {
     char name[160];
     snprintf(name, sizeof name, "S=%lld Hq=%d Hkv=%d D=%d causal=%d hc=%d T=%lld host=%d",
@@ -625,12 +678,14 @@ static void run_case(int64_t S, int Hq, int Hkv, int D, int causal, int hc, int6
     hc::make_plan(false, S, Hq, Hkv, D, causal, hc, T, &pf, msg, sizeof msg, g_gl_min_s);
     const size_t keep = g_regions.size();
     add_workspace(wf, pf);
-    int rc = attn_fwd(q.p(), k.p(), v.p(), o.p(), (float*)lse.p(), S, Hq, Hkv, D, causal, hc, T,
-                      wf, nf, nullptr);
-    if (rc != ATTN_OK) fail_msg("attn_fwd returned %llu (%llu)", attn_last_error(), (size_t)rc, 0);
+    checked_call(0, "attn_fwd", [&]() {
+        return attn_fwd(q.p(), k.p(), v.p(), o.p(), (float*)lse.p(), S, Hq, Hkv, D, causal, hc, T, wf,
+                        nf, nullptr);
+    });
     g_regions.resize(keep);
     g_allocs.pop_back();
-    if (nf <= ATTN_NOALLOC_WORKSPACE_BYTES) {
+    int rc;
+    if (nf <= ATTN_NOALLOC_WORKSPACE_BYTES && g_inj.call < 0) {
         // the same forward on the built-in workspace
         char* sb = scratch_base();
         g_allocs.push_back({(uintptr_t)sb, (uintptr_t)sb + hc::kScratchBytes, false});
@@ -645,9 +700,10 @@ static void run_case(int64_t S, int Hq, int Hkv, int D, int causal, int hc, int6
     g_allocs.push_back({(uintptr_t)wb, (uintptr_t)wb + nb, false});
     hc::make_plan(true, S, Hq, Hkv, D, causal, hc, T, &pb, msg, sizeof msg, g_gl_min_s);
     add_workspace(wb, pb);
-    rc = attn_bwd(q.p(), k.p(), v.p(), o.p(), dout.p(), (const float*)lse.p(), dq.p(), dk.p(),
-                  dv.p(), S, Hq, Hkv, D, causal, hc, T, wb, nb, nullptr);
-    if (rc != ATTN_OK) fail_msg("attn_bwd returned %llu (%llu)", attn_last_error(), (size_t)rc, 0);
+    checked_call(1, "attn_bwd", [&]() {
+        return attn_bwd(q.p(), k.p(), v.p(), o.p(), dout.p(), (const float*)lse.p(), dq.p(), dk.p(),
+                        dv.p(), S, Hq, Hkv, D, causal, hc, T, wb, nb, nullptr);
+    });
 }
 
 // attn_layer_fwd and attn_layer_bwd, each without and with the kept
@@ -734,8 +790,30 @@ static void run_layer_case(int64_t S, int dm, int Hq, int Hkv, int D, int causal
 }
 
 int main(int argc, char** argv) {
-    for (int i = 1; i < argc; ++i)
+    bool inject = false;
+    for (int i = 1; i < argc; ++i) {
         if (strcmp(argv[i], "--plant-dkdv-overread") == 0) g_plant = true;
+        if (strcmp(argv[i], "--inject") == 0) inject = true;
+    }
+    if (inject) {
+        // a failing trunk copy (pinned host K/V: forward and backward) or
+        // kernel launch, early, in the middle and late in each call
+        long cases = 0;
+        for (int call = 0; call < 2; ++call)
+            for (int copy = 0; copy < 2; ++copy)
+                for (long at : {0L, 1L, 5L, 17L}) {
+                    g_inj.call = call;
+                    g_inj.copy = copy != 0;
+                    g_inj.at = at;
+                    run_case(1100, 8, 2, 128, 1, 4, 256, true);
+                    run_case(700, 4, 2, 64, 1, 2, 0, false);
+                    cases += 2;
+                }
+        g_inj = Inject{};
+        printf("injection cases: %ld  failures injected: %ld  failures: %ld\n", cases, g_inject_hits,
+               g_fails);
+        return g_fails == 0 && g_inject_hits > 0 ? 0 : 1;
+    }
     // sequence lengths at and around tile edges (64-row tiles, 128-key dK/dV
     // tiles, 128/256-row forward and dQ workgroups, 256-token trunks)
     const int64_t Ss[] = {1, 2, 33, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257,

@@ -4,7 +4,9 @@ against a fake HIP runtime that replays each kernel's index arithmetic on the
 host (tests/native/extent_check.cpp), built with the address and
 undefined-behaviour sanitizers, over ~1400 shapes around tile, workgroup and
 trunk edges with exactly sized user tensors and workspace regions.  A planted
-copy of a load that once read past the last key must be reported."""
+copy of a load that once read past the last key must be reported, and HIP
+failures injected into copies and kernel launches must come back as
+ATTN_EHIP without breaking the next call."""
 import os
 import shutil
 import subprocess
@@ -48,3 +50,12 @@ def test_planted_over_read_is_reported(extent_exe):
     r = _run(extent_exe, "--plant-dkdv-overread")
     assert r.returncode == 1
     assert "dkdv V tile" in r.stderr and "failures: 0" not in r.stdout
+
+
+def test_injected_copy_and_launch_failures_surface_and_leave_no_state(extent_exe):
+    # a trunk copy or kernel launch that fails makes the call return
+    # ATTN_EHIP naming it, and the same call right after succeeds
+    r = _run(extent_exe, "--inject")
+    print(r.stdout, r.stderr[-2000:])
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "failures: 0" in r.stdout
