@@ -14,9 +14,10 @@
 // and the same for B with n in place of m.  Segments are multiples of 8, and
 // of 64 for a k-contiguous operand.
 //
-// Workgroup = 4 waves on a 128 x 128 tile of C, 2 x 2 waves of 64 x 64; K in
-// steps of 64 staged through LDS (global -> registers two steps ahead, two
-// register sets; registers -> LDS double-buffered, one barrier per step).  A
+// Workgroup = 4 waves on a 128 x 128 tile of C (2 x 2 waves of 64 x 64) or 8
+// waves on a 256 x 256 one (2 x 4 waves of 128 x 64); K in steps of 64 staged
+// through LDS (global -> registers -> LDS, double-buffered, one barrier per
+// step).  A
 // k-contiguous operand tile is [128][64] with rows padded by 8 bytes
 // (conflict-free 8-byte reads); an m- or n-contiguous one
 // is [64][128] with the XOR-swizzled rows of the attention kernels, read
@@ -34,8 +35,6 @@
 // Split-K: blockIdx.z takes k in [z * k_split, (z + 1) * k_split) (k_split a
 // multiple of 64) and writes
 // fp32 partials at c + z * c_zs; gemm_reduce adds the slices in ascending z.
-#include <type_traits>
-
 #include "device_common.h"
 #include "kernels.h"
 
@@ -43,7 +42,20 @@ namespace hc {
 
 namespace {
 
-constexpr int GBM = 128, GBN = 128, GBK = 64;
+constexpr int GBK = 64;
+
+// Tile configurations: a BM x BN tile of C per workgroup of WM x WN waves,
+// each wave 32 MB x 32 NB.  The small one (4 waves, 64 x 64 per wave) serves
+// narrow products; the large one (8 waves, 128 x 64 per wave) halves the
+// operand traffic per product term where both dimensions allow it.
+template <int BM_, int BN_, int WM_, int WN_>
+struct GemmCfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int THREADS = WM * WN * 64;
+    static constexpr int MB = BM / WM / 32, NB = BN / WN / 32;
+};
+using GemmSmall = GemmCfg<128, 128, 2, 2>;
+using GemmLarge = GemmCfg<256, 256, 2, 4>;
 // bf16 per padded row of a k-contiguous tile: 136 bytes, so that the 32 rows
 // one 8-byte read pass touches start 34 words apart, on 32 distinct even banks
 // of the 64 (a 16-byte pad repeats the banks every 16 rows: 2-way conflicts)
@@ -58,12 +70,14 @@ __device__ __forceinline__ bf16x8 kc_frag(const char* tile, int row, int k0, int
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <bool KC>
+// ROWS x 64 operand tile (ROWS a multiple of 128) loaded by THREADS threads;
+// an r-contiguous one sits in LDS as ROWS / 128 sub-tiles [64][128]
+template <bool KC, int ROWS, int THREADS>
 struct OperandTile {
-    // 1024 16-byte chunks per 128 x 64 tile, four per thread
-    static constexpr int NCH = GBM * GBK / 8 / 256;
+    static constexpr int NCH = ROWS * GBK / 8 / THREADS;  // 16-byte chunks per thread
     static constexpr int KCH = GBK / 8;  // chunks per k-contiguous row
-    uint4 r[2][NCH];   // two register sets: a tile lands in one while the other is stored
+    static constexpr int RCH = ROWS / 8;  // chunks per r-contiguous row
+    uint4 r[NCH];
     int64_t off[NCH];  // element offset of the thread's chunk i at the tile's first k
     int kk[NCH];       // its reduction index relative to the tile's first k
     bool row_ok[NCH];
@@ -76,15 +90,15 @@ struct OperandTile {
                                          int64_t R, int tid) {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-            const int idx = tid + i * 256;
+            const int idx = tid + i * THREADS;
             if constexpr (KC) {
                 const int64_t row = r0 + idx / KCH;
                 kk[i] = (idx % KCH) * 8;
                 row_ok[i] = row < R;
                 off[i] = row * rs + kk[i];
             } else {
-                const int64_t row = r0 + (idx % 16) * 8;
-                kk[i] = idx / 16;
+                const int64_t row = r0 + (idx % RCH) * 8;
+                kk[i] = idx / RCH;
                 row_ok[i] = row < R;
                 off[i] = (row / seg) * segs + row % seg + kk[i] * rs;
             }
@@ -127,29 +141,29 @@ struct OperandTile {
             cur += GBK * rs;
         }
     }
-    // the current tile into register set SET; zero outside [0, R) x [k0, K)
-    template <int SET>
+    // the current tile into registers; zero outside [0, R) x [k0, K)
     __device__ __forceinline__ void load(int64_t K) {
         const uint16_t* b = base + cur;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-            if (row_ok[i] && k0 + kk[i] < K) r[SET][i] = *reinterpret_cast<const uint4*>(b + off[i]);
-            else r[SET][i] = make_uint4(0, 0, 0, 0);
+            if (row_ok[i] && k0 + kk[i] < K) r[i] = *reinterpret_cast<const uint4*>(b + off[i]);
+            else r[i] = make_uint4(0, 0, 0, 0);
         }
     }
-    template <int SET>
     __device__ __forceinline__ void store(char* lds, int tid) const {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-            const int idx = tid + i * 256;
+            const int idx = tid + i * THREADS;
             if constexpr (KC) {
                 // 8-byte aligned rows: the chunk goes in two 8-byte halves
                 const int o = (idx / KCH) * (KC_PITCH * 2) + (idx % KCH) * 16;
-                const uint4 v = r[SET][i];
+                const uint4 v = r[i];
                 *reinterpret_cast<uint2*>(lds + o) = make_uint2(v.x, v.y);
                 *reinterpret_cast<uint2*>(lds + o + 8) = make_uint2(v.z, v.w);
             } else {
-                *reinterpret_cast<uint4*>(lds + lds_off<128>(idx / 16, (idx % 16) * 8)) = r[SET][i];
+                const int k = idx / RCH, row = (idx % RCH) * 8;
+                *reinterpret_cast<uint4*>(lds + (row / 128) * (GBK * 128 * 2) + lds_off<128>(k, row % 128)) =
+                    r[i];
             }
         }
     }
@@ -159,21 +173,22 @@ template <bool KC>
 __device__ __forceinline__ bf16x8 frag(const char* tile, const OperandOffsets<128>& off,
                                        int blk32, int k0, int lane) {
     if constexpr (KC) return kc_frag(tile, blk32 * 32 + (lane & 31), k0, lane >> 5);
-    else return lds_read_tr_at<128>(tile, off, k0, blk32);
+    else return lds_read_tr_at<128>(tile + (blk32 / 4) * (GBK * 128 * 2), off, k0, blk32 % 4);
 }
 
 }  // namespace
 
-template <bool A_KC, bool B_KC>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
-    constexpr int TA = A_KC ? GBM * KC_PITCH * 2 : GBK * 128 * 2;
-    constexpr int TB = B_KC ? GBN * KC_PITCH * 2 : GBK * 128 * 2;
+template <bool A_KC, bool B_KC, class CFG>
+__global__ __launch_bounds__(CFG::THREADS) void gemm_kernel(GemmParams p) {
+    constexpr int GBM = CFG::BM, GBN = CFG::BN, MB = CFG::MB, NB = CFG::NB, NT = CFG::THREADS;
+    constexpr int TA = A_KC ? GBM * KC_PITCH * 2 : GBK * GBM * 2;
+    constexpr int TB = B_KC ? GBN * KC_PITCH * 2 : GBK * GBN * 2;
     __shared__ __attribute__((aligned(1024))) char sa[2][TA];
     __shared__ __attribute__((aligned(1024))) char sb[2][TB];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1, hi = lane >> 5;
+    const int wm = wave / CFG::WN, wn = wave % CFG::WN, hi = lane >> 5;
     // tile order: the workgroups of a row of C tiles (one m tile, every n
     // tile) are consecutive and, with workgroup b running on die b % 8, on one
     // die, so they share that die's L2 copy of their A tile
@@ -186,23 +201,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     ke = ke < p.K ? ke : p.K;
     const int nkt = ke > kb ? (int)((ke - kb + GBK - 1) / GBK) : 0;
 
-    OperandTile<A_KC> ta;
-    OperandTile<B_KC> tb;
+    OperandTile<A_KC, GBM, NT> ta;
+    OperandTile<B_KC, GBN, NT> tb;
     // lane: row m of C; register group g4 of block nb: columns n .. n + 3
     char* cz = static_cast<char*>(p.c) +
                (int64_t)blockIdx.z * p.c_zs * (p.out_mode == kGemmBf16 ? 2 : 4);
     auto c_off = [&](int mb, int nb, int g4, int64_t* m, int64_t* n) {
-        *m = m0 + wm * 64 + mb * 32 + (lane & 31);
-        *n = n0 + wn * 64 + nb * 32 + g4 * 8 + hi * 4;
+        *m = m0 + wm * (32 * MB) + mb * 32 + (lane & 31);
+        *n = n0 + wn * (32 * NB) + nb * 32 + g4 * 8 + hi * 4;
         return (*n / p.c_seg) * p.c_segs + *m * p.c_rs + *n % p.c_seg;
     };
     // accumulating products start from C itself, so a product whose reduction
     // is split over several launches adds in the same order as one launch
-    f32x16 acc[2][2];
+    f32x16 acc[NB][MB];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
             acc[nb][mb] = f32x16{};
             if (p.out_mode == kGemmF32Add) {
 #pragma unroll
@@ -228,59 +243,49 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
         ta.begin(p.a, p.a_rs, p.a_seg, p.a_segs, kb, ke);
         tb.begin(p.b, p.b_rs, p.b_seg, p.b_segs, kb, ke);
     }
-    // k tiles: tile j is multiplied from LDS buffer j % 2; its operands were
-    // loaded into register set j % 2 two tiles earlier and stored to LDS at
-    // the end of tile j - 1, so every load has two tiles' time to land
-    auto fetch = [&](auto set) {
-        ta.advance(p, true, p.a_rs, p.a_seg, p.a_segs);
-        tb.advance(p, false, p.b_rs, p.b_seg, p.b_segs);
-        ta.template load<decltype(set)::value>(ke);
-        tb.template load<decltype(set)::value>(ke);
-    };
-    auto put = [&](auto set) {
-        ta.template store<decltype(set)::value>(sa[decltype(set)::value], tid);
-        tb.template store<decltype(set)::value>(sb[decltype(set)::value], tid);
-    };
+    // k tiles: tile j is multiplied from LDS buffer j % 2 while tile j + 1
+    // loads into registers, which go to the other buffer at the end of the step
     auto multiply = [&](int buf) {
 #pragma unroll
         for (int ks = 0; ks < GBK / 16; ++ks) {
-            bf16x8 bf[2], af[2];
+            bf16x8 bf[NB], af[MB];
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) bf[nb] = frag<B_KC>(sb[buf], off, wn * 2 + nb, ks * 16, lane);
+            for (int nb = 0; nb < NB; ++nb) bf[nb] = frag<B_KC>(sb[buf], off, wn * NB + nb, ks * 16, lane);
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) af[mb] = frag<A_KC>(sa[buf], off, wm * 2 + mb, ks * 16, lane);
+            for (int mb = 0; mb < MB; ++mb) af[mb] = frag<A_KC>(sa[buf], off, wm * MB + mb, ks * 16, lane);
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma32(bf[nb], af[mb], acc[nb][mb]);
+                for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma32(bf[nb], af[mb], acc[nb][mb]);
         }
     };
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
     if (nkt > 0) {
-        ta.template load<0>(ke);
-        tb.template load<0>(ke);
+        ta.load(ke);
+        tb.load(ke);
+        ta.store(sa[0], tid);
+        tb.store(sb[0], tid);
     }
-    if (nkt > 1) fetch(S1{});
-    if (nkt > 0) put(S0{});
     __syncthreads();
-    for (int kt = 0; kt < nkt; kt += 2) {
-        if (kt + 2 < nkt) fetch(S0{});
-        multiply(0);
-        if (kt + 1 < nkt) put(S1{});
-        __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int buf = kt & 1;
         if (kt + 1 < nkt) {
-            if (kt + 3 < nkt) fetch(S1{});
-            multiply(1);
-            if (kt + 2 < nkt) put(S0{});
-            __syncthreads();
+            ta.advance(p, true, p.a_rs, p.a_seg, p.a_segs);
+            tb.advance(p, false, p.b_rs, p.b_seg, p.b_segs);
+            ta.load(ke);
+            tb.load(ke);
         }
+        multiply(buf);
+        if (kt + 1 < nkt) {
+            ta.store(sa[buf ^ 1], tid);
+            tb.store(sb[buf ^ 1], tid);
+        }
+        __syncthreads();
     }
 
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 int64_t m, n;
@@ -342,13 +347,26 @@ hipError_t launch_gemm(const GemmParams& p, bool a_kc, bool b_kc, int splits, hi
     if (p.N % 8 != 0 || p.a_seg % 8 != 0 || p.b_seg % 8 != 0 || p.c_seg % 4 != 0 ||
         (p.k_split > 0 && p.k_split % GBK != 0) || splits < 1 || splits > 65535)
         return hipErrorInvalidValue;
-    const int64_t gx = (p.M + GBM - 1) / GBM, gy = (p.N + GBN - 1) / GBN;
+    // the large tiles where both dimensions fill them
+    const bool large = p.M >= GemmLarge::BM && p.N >= GemmLarge::BN;
+    const int64_t bm = large ? GemmLarge::BM : GemmSmall::BM, bn = large ? GemmLarge::BN : GemmSmall::BN;
+    const int64_t gx = (p.M + bm - 1) / bm, gy = (p.N + bn - 1) / bn;
     if (gx * gy > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)(gx * gy), 1, (unsigned)splits), block(256);
-    if (a_kc && b_kc) hipLaunchKernelGGL((gemm_kernel<true, true>), grid, block, 0, st, p);
-    else if (a_kc) hipLaunchKernelGGL((gemm_kernel<true, false>), grid, block, 0, st, p);
-    else if (b_kc) hipLaunchKernelGGL((gemm_kernel<false, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((gemm_kernel<false, false>), grid, block, 0, st, p);
+    const dim3 grid((unsigned)(gx * gy), 1, (unsigned)splits);
+#define HC_GEMM(AK, BK, CFG) \
+    hipLaunchKernelGGL((gemm_kernel<AK, BK, CFG>), grid, dim3(CFG::THREADS), 0, st, p)
+    if (large) {
+        if (a_kc && b_kc) HC_GEMM(true, true, GemmLarge);
+        else if (a_kc) HC_GEMM(true, false, GemmLarge);
+        else if (b_kc) HC_GEMM(false, true, GemmLarge);
+        else HC_GEMM(false, false, GemmLarge);
+    } else {
+        if (a_kc && b_kc) HC_GEMM(true, true, GemmSmall);
+        else if (a_kc) HC_GEMM(true, false, GemmSmall);
+        else if (b_kc) HC_GEMM(false, true, GemmSmall);
+        else HC_GEMM(false, false, GemmSmall);
+    }
+#undef HC_GEMM
     return hipGetLastError();
 }
 
