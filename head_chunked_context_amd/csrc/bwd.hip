@@ -247,16 +247,29 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) dpacc[0][g4 * 4 + e] = nd[e];
             }
+            // MFMA j: S (even j) or dP (odd j) over d 16 (j / 2) ..; both of
+            // its operands are read DIST MFMAs ahead
+            {
+                constexpr int NJ = 2 * NS, DIST = 2;
+                auto rd = [&](int j, bf16x8& x, bf16x8& y) {
+                    const int st = j >> 1;
+                    const int ko = off.row[st] + kw * 32 * HD * 2;
+                    const int qo = off.row[st] + rh * 32 * HD * 2;
+                    x = lds_read_b128((j & 1) ? Os : Qs, qo);
+                    y = lds_read_b128(skv[j & 1], ko);
+                };
+                bf16x8 ra[DIST], rb[DIST];
 #pragma unroll
-            for (int st = 0; st < NS; ++st) {
-                const int ko = off.row[st] + kw * 32 * HD * 2;
-                const int qo = off.row[st] + rh * 32 * HD * 2;
-                const bf16x8 kf = lds_read_b128(skv[0], ko);
-                const bf16x8 vf = lds_read_b128(skv[1], ko);
-                const bf16x8 aq = lds_read_b128(Qs, qo);
-                const bf16x8 ao = lds_read_b128(Os, qo);
-                sacc[0] = mfma32(aq, kf, st == 0 ? f32x16{} : sacc[0]);
-                dpacc[0] = mfma32(ao, vf, dpacc[0]);
+                for (int j = 0; j < DIST; ++j) rd(j, ra[j], rb[j]);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const bf16x8 a = ra[j % DIST], b = rb[j % DIST];
+                    if (j + DIST < NJ) rd(j + DIST, ra[j % DIST], rb[j % DIST]);
+                    const int st = j >> 1;
+                    if (j & 1) dpacc[0] = mfma32(a, b, dpacc[0]);
+                    else sacc[0] = mfma32(a, b, st == 0 ? f32x16{} : sacc[0]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
             bf16x8 pb[1][2], dsb[1][2];
             const bool edge_k = wj0 + WK > p.nk;
@@ -273,14 +286,24 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
                 dkdv_p_ds<1, false>(sacc, dpacc, sl, hi, p.scale_log2, 0, 0, 0, pb, dsb);
             }
             // dV^T += dO^T P and dK^T += Q^T dS, reduction over the wave's 32 rows
+            {
+                // MFMA j: dV (even j) or dK (odd j) of d block j / 4, rows
+                // 16 ((j / 2) % 2) ..; its A operand is read 2 MFMAs ahead
+                constexpr int NJ = 4 * NDB, DIST = 3;
+                auto rd = [&](int j) {
+                    return lds_read_tr_at<HD>((j & 1) ? Qs : Os, off, rh * 32 + ((j >> 1) & 1) * 16, j >> 2);
+                };
+                bf16x8 ring[DIST];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
+                for (int j = 0; j < DIST; ++j) ring[j] = rd(j);
 #pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    bf16x8 ao = lds_read_tr_at<HD>(Os, off, rh * 32 + h2 * 16, db);
-                    dv[db] = mfma32(ao, pb[0][h2], dv[db]);
-                    bf16x8 aq = lds_read_tr_at<HD>(Qs, off, rh * 32 + h2 * 16, db);
-                    dk[db] = mfma32(aq, dsb[0][h2], dk[db]);
+                for (int j = 0; j < NJ; ++j) {
+                    const bf16x8 a = ring[j % DIST];
+                    if (j + DIST < NJ) ring[j % DIST] = rd(j + DIST);
+                    const int db = j >> 2, h2 = (j >> 1) & 1;
+                    if (j & 1) dk[db] = mfma32(a, dsb[0][h2], dk[db]);
+                    else dv[db] = mfma32(a, pb[0][h2], dv[db]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
