@@ -615,13 +615,20 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
                 } else {
                     dq_ds<1, false>(s, dp, p.scale_log2, nlse2, hi, 0, 0, dsb);
                 }
-                // dQ^T += K^T dS^T over the half's 32 keys
+                // dQ^T += K^T dS^T over the half's 32 keys; MFMA j (d block
+                // j / 2, keys 16 (j % 2) ..) has its K^T operand read DIST ahead
+                {
+                    constexpr int NJ = 2 * NDB, DIST = 3;
+                    auto rdt = [&](int j) { return lds_read_tr_at<HD>(Ks, off, b * 32 + (j & 1) * 16, j >> 1); };
+                    bf16x8 ring[DIST];
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
+                    for (int j = 0; j < DIST; ++j) ring[j] = rdt(j);
 #pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        bf16x8 ak = lds_read_tr_at<HD>(Ks, off, b * 32 + h2 * 16, db);
-                        acc[db] = mfma32(ak, dsb[0][h2], acc[db]);
+                    for (int j = 0; j < NJ; ++j) {
+                        const bf16x8 ak = ring[j % DIST];
+                        if (j + DIST < NJ) ring[j % DIST] = rdt(j + DIST);
+                        acc[j >> 1] = mfma32(ak, dsb[0][j & 1], acc[j >> 1]);
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
             }
