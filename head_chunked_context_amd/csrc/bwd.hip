@@ -15,19 +15,24 @@
 // accumulator (the MFMAs then yield dP - Delta), and -LSE * log2(e), the
 // addend of the exponent's fused multiply-add.
 //
-// dkdv_kernel: workgroup = 8 waves on 128 keys of one query head's kv head;
-// K and V of the 128 keys sit in LDS for the whole kernel.  Each step loads a
-// 64-row query tile of Q and dO (plus the rows' statistics) straight into LDS,
-// double-buffered.  Waves w and w + 4 share keys 32 (w % 4) .. +31 and take
-// the lower / upper 32 rows of every tile:
-//   S[q][key]   = Q K^T        A = Q rows (LDS),   B = K (LDS)
-//   dP[q][key]  = dO V^T       A = dO rows (LDS),  B = V (LDS)
-//   dV^T[d][key] += dO^T P     A = dO rows, transposed LDS reads
-//   dK^T[d][key] += Q^T dS     A = Q rows, transposed LDS reads
-// so each lane owns one key (lanes l and l^32 split the wave's rows).  Two
-// waves per SIMD let one wave's softmax-side VALU work run under the other's
-// MFMAs.  At the end the upper-half wave hands its dK/dV partial to its
-// partner through LDS, which adds it after its own (fixed order).
+// dkdv_kernel: workgroup = 4 waves (one per SIMD) on 128 keys of one kv head;
+// wave w owns keys 32 w .. 32 w + 31 for the whole kernel, with their K and V
+// rows as MFMA operands in registers and their fp32 dK/dV sums in the
+// accumulation registers.  Each step covers a 64-row query tile (two 32-row
+// blocks b), whose Q and dO rows (plus the rows' statistics) are loaded
+// straight into a 4-slot LDS ring three steps ahead:
+//   S_b[q][key]   = Q_b K^T       A = Q rows (LDS),   B = K (registers)
+//   dP_b[q][key]  = dO_b V^T      A = dO rows (LDS),  B = V (registers)
+//   dV^T[d][key] += dO_b^T P_b    A = dO rows, transposed LDS reads
+//   dK^T[d][key] += Q_b^T dS_b    A = Q rows, transposed LDS reads
+// so each lane owns one key (lanes l and l^32 split the rows).  With one wave
+// per SIMD nothing hides one wave's vector work under another's MFMAs, so
+// each step is a fixed sequence of 64 MFMA groups (S/dP of block 0, S/dP of
+// block 1, dV/dK of block 0, dV/dK of block 1) with the exponentials and
+// products of one block spread over the MFMAs of the next phase, every
+// operand read four MFMAs ahead, and the next step's loads and first operand
+// reads in the last phase.  Per MFMA this reads 1 KB from LDS (2 KB for the
+// S/dP MFMAs of the two-waves-per-SIMD layout with K/V in LDS).
 //
 // dq_kernel: workgroup = NW waves x 32 query rows of one head (NW = 8 with a
 // 4-slot K/V ring and two tiles per barrier for large launches, NW = 4
@@ -40,77 +45,51 @@
 namespace hc {
 
 
-// P and dS of one 64-row query tile against this lane's key, as bf16 MFMA
-// operands.  MASK adds the causal / ragged-edge test; the common interior
-// tiles skip it entirely.
-template <int NQB, bool MASK>
-__device__ __forceinline__ void dkdv_p_ds(const f32x16 (&sacc)[NQB], const f32x16 (&dpacc)[NQB],
-                                          const float* s_nlse2, int hi, float scale_log2,
-                                          int qrel0, int krel, int qlim, bf16x8 (&pb)[NQB][2],
-                                          bf16x8 (&dsb)[NQB][2]) {
+// dK / dV accumulation with the accumulator held in the accumulation
+// registers (AGPRs) for the whole kernel, while the score MFMAs keep theirs in
+// ordinary VGPRs (the compiler, left to itself, shuttles the dK / dV sums
+// between the two files around every MFMA).  The compiler does not know this
+// instruction is an MFMA, so it supplies no wait states around it: the step
+// loop that uses it has no other access to the accumulators, and
+// agpr_settle() waits before anything after that loop reads or moves them.
+__device__ __forceinline__ void mfma32_agpr(f32x16& c, bf16x8 a, bf16x8 b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// the same with its own wait states: two before it (for a vector write of an
+// operand just before) and sixteen after it (for a read of the result, or a
+// write of the accumulator, just after); for code in which the compiler may
+// move the accumulators between registers around it
+__device__ __forceinline__ void mfma32_agpr_padded(f32x16& c, bf16x8 a, bf16x8 b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(c) : "v"(a), "v"(b));
+}
+// 24 wait states after the last mfma32_agpr, ordered before any later use of
+// the accumulators (each passes through an asm statement here)
+template <int N>
+__device__ __forceinline__ void agpr_settle(f32x16 (&x)[N], f32x16 (&y)[N]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(x[0]), "+a"(y[0]));
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const int qr = qb * 32 + g4 * 8 + hi * 4;  // tile rows qr..qr+3
-            const f32x4 L = *reinterpret_cast<const f32x4*>(s_nlse2 + qr);
-#pragma unroll
-            for (int e = 0; e < 4; e += 2) {
-                const int r = g4 * 4 + e;
-                float pv[2], dsv[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    float x = fast_exp2(__builtin_fmaf(sacc[qb][r + u], scale_log2, L[e + u]));
-                    if constexpr (MASK) {
-                        // qrel/krel: row and key relative to the key tile start;
-                        // visible iff key <= row (causal) and row < qlim
-                        const int qrel = qrel0 + qr + e + u;
-                        x = (krel <= qrel && qrel < qlim) ? x : 0.f;
-                    }
-                    pv[u] = x;
-                    dsv[u] = x * dpacc[qb][r + u];
-                }
-                const bf16x2 pk = to_bf16x2(pv[0], pv[1]);
-                const bf16x2 dk2 = to_bf16x2(dsv[0], dsv[1]);
-                pb[qb][r >> 3][r & 7] = pk[0];
-                pb[qb][r >> 3][(r & 7) + 1] = pk[1];
-                dsb[qb][r >> 3][r & 7] = dk2[0];
-                dsb[qb][r >> 3][(r & 7) + 1] = dk2[1];
-            }
-        }
-    }
+    for (int i = 1; i < N; ++i) asm volatile("" : "+a"(x[i]), "+a"(y[i]));
 }
 
 template <int HD, bool RUNS, bool GLOOP>
-__global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
-    constexpr int BQ = 64, WQ = 32, WK = 32, BNK = 128;
+__global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
+    constexpr int BQ = 64, WK = 32, BNK = 128, NBUF = 4;
     constexpr int NS = HD / 16, NDB = HD / 32;
     constexpr int TILE = BQ * HD * 2;
-    __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [buf][Q / dO]
-    __shared__ __attribute__((aligned(1024))) char skv[2][2 * TILE];  // this tile's K, V
-    __shared__ __attribute__((aligned(16))) float s_nlse2[2][BQ];   // -LSE * log2(e)
-    __shared__ __attribute__((aligned(16))) float s_ndelta[2][BQ];  // -Delta
+    constexpr int NI = TileDma64<HD, false>::NI;  // tile loads per wave
+    constexpr int PH = 2 * NS;        // MFMAs per phase
+    constexpr int GPP = PH / 8;       // groups per pair of score elements
+    constexpr int NG = 4 * PH;        // MFMA groups per step
+    constexpr int DIST = 4;           // operand reads ahead (divides NG)
+    __shared__ __attribute__((aligned(1024))) char smem[NBUF][2][TILE];  // [slot][Q / dO]
+    __shared__ __attribute__((aligned(16))) float s_nlse2[NBUF][BQ];
+    __shared__ __attribute__((aligned(16))) float s_ndelta[NBUF][BQ];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5, l32 = lane & 31;
-    const int kw = wave & 3;   // key block of the wave (32 keys)
-    const int rh = wave >> 2;  // half of every 64-row query tile the wave takes
 
-    // work item = key tile * units + unit, key tiles ascending: heaviest
-    // first (key tile 0 sees every query tile when causal).  A unit is a
-    // query head of the chunk (per-head schedule) or a kv head of the chunk
-    // (group loop).
-    // Workgroup b runs on die b % 8, and each die's L2 serves its resident
-    // workgroups' Q/dO rows.  When the unit count is a multiple of 4, plain
-    // order already gives each die one or two units at key tiles 2 or 1
-    // apart; otherwise (1, 2, 5 ... units: RUNS) each die takes runs of 32
-    // consecutive items per window of 8 x 32, in a snake order across
-    // windows (a last partial window keeps plain order), so that a die's
-    // workgroups stream neighbouring key tiles of few heads.  Measured at
-    // S = 262144 (per-head schedule): dK/dV 5% faster with 1 head, 3.6% with
-    // 2, 4% with 5 (of 40 / 8 kv heads); 4 and 8 heads are 4% faster in
-    // plain order.
     const int units = GLOOP ? p.nkv : p.nh;
     int unit;
     int64_t kt;
@@ -128,7 +107,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
         unit = blockIdx.x % units;
         kt = (int64_t)(blockIdx.x / units);
     }
-    // the unit's kv head (local) and its query heads [hb, he) (local to the chunk)
     int kvl, hb, he;
     if constexpr (GLOOP) {
         kvl = unit;
@@ -140,24 +118,21 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
         he = unit + 1;
         kvl = (p.h0 + unit) / p.group - p.kv_base;
     }
-    const int64_t j0 = kt * BNK;                  // first key of the workgroup
-    const int64_t wj0 = j0 + kw * WK;             // first key of this wave
-    const int64_t myk = wj0 + l32;                // this lane's key
+    const int64_t j0 = kt * BNK;
+    const int64_t wj0 = j0 + wave * WK;
+    const int64_t myk = wj0 + l32;
 
-    // the workgroup's 128 keys of K (waves 0-3) and V (waves 4-7) go to LDS
-    // (rows past nk repeat the last key; their P is masked to zero).  When
-    // the tile holds 64 keys or fewer, every row of the second half repeats
-    // key nk - 1, so no lane reads past the last key.
-    if (j0 < p.nk) {
-        const int64_t nv = p.nk - j0;
-        const int64_t rs = rh == 0 ? p.k_rs : p.v_rs;
-        const uint16_t* src = rh == 0 ? p.k + (int64_t)kvl * p.k_hs + j0 * p.k_rs
-                                      : p.v + (int64_t)kvl * p.v_hs + j0 * p.v_rs;
-        direct_tile64<HD>(skv[rh], src, rs, nv, kw, lane);
-        if (nv > 64)
-            direct_tile64<HD>(skv[rh] + TILE, src + 64 * rs, rs, nv - 64, kw, lane);
-        else
-            direct_tile64<HD>(skv[rh] + TILE, src + (nv - 1) * rs, rs, 1, kw, lane);
+    // K and V of this lane's key (the last key for lanes past it) as B operands
+    bf16x8 kf[NS], vf[NS];
+    {
+        const int64_t kk = myk < p.nk ? myk : p.nk - 1;
+        const uint16_t* kr = p.k + (int64_t)kvl * p.k_hs + kk * p.k_rs + hi * 8;
+        const uint16_t* vr = p.v + (int64_t)kvl * p.v_hs + kk * p.v_rs + hi * 8;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            kf[st] = *reinterpret_cast<const bf16x8*>(kr + st * 16);
+            vf[st] = *reinterpret_cast<const bf16x8*>(vr + st * 16);
+        }
     }
     f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -165,10 +140,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
         dk[db] = f32x16{};
         dv[db] = f32x16{};
     }
-    // a group continued from the previous chunk resumes from its row half's sums
     if (GLOOP && kvl == p.carry_kv_in && myk < p.nk) {
-        const float* ck = p.carry_in_k + rh * p.carry_hs + myk * HD;
-        const float* cv = p.carry_in_v + rh * p.carry_hs + myk * HD;
+        const float* ck = p.carry_in_k + myk * HD;
+        const float* cv = p.carry_in_v + myk * HD;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -183,141 +157,290 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
             }
         }
     }
+    wait_vm_loads();
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        settle(kf[st]);
+        settle(vf[st]);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        settle(dk[db]);
+        settle(dv[db]);
+    }
 
-    // query tiles: causal rows start at the workgroup's first key position
     const int64_t nqt = (p.nq + BQ - 1) / BQ;
     int64_t qt0 = 0;
     if (p.causal) {
         const int64_t first = p.k_pos0 + j0;
         qt0 = first >= p.nq ? nqt : first / BQ;
     }
-    // steps: heads hb..he-1 ascending, each over query tiles qt0..nqt-1 ascending
-    const int64_t nsteps = j0 < p.nk ? nqt - qt0 : 0;
-    const int64_t total = nsteps * (he - hb);
+    const int nsteps = j0 < p.nk ? (int)(nqt - qt0) : 0;
+    const int total = nsteps * (he - hb);
 
-    // one step = Q (waves 0-3) and dO (waves 4-7) rows [i0, i0 + 64) of head
-    // h plus their LSE (wave 0) and Delta (wave 4), straight into LDS buffer b
-    // each wave loads one contiguous run of the tile's rows: with the
-    // interleaved order this kernel ran 7-12% slower at S = 262144 with 32
-    // heads per launch (the forward and dQ kernels showed no difference)
-    const TileDma64<HD, false> dqo(rh == 0 ? p.q_rs : p.do_rs, kw, lane);
-    auto issue_step = [&](int h, int64_t s, int b) {
-        const int64_t i0 = (qt0 + s) * BQ;
-        if (rh == 0)
-            dqo.load(smem[b][0], p.q + (int64_t)h * p.q_hs + i0 * p.q_rs, p.q_rs, p.nq - i0, kw, lane);
-        else
-            dqo.load(smem[b][1], p.dO + (int64_t)h * p.do_hs + i0 * p.do_rs, p.do_rs, p.nq - i0, kw,
-                     lane);
-        if (wave == 0) direct_vec64(s_nlse2[b], p.nlse2 + (int64_t)h * p.nlse2_hs + i0, p.nq - i0, lane);
-        if (wave == 4) direct_vec64(s_ndelta[b], p.ndelta + (int64_t)h * p.ndelta_hs + i0, p.nq - i0, lane);
+    // Loads run three steps ahead into a 4-slot ring.  The issue cursor
+    // (head ih, step is) keeps scalar pointers to the rows it loads next.
+    const TileDma64<HD, false> dmq(p.q_rs, wave, lane), dmo(p.do_rs, wave, lane);
+    int ih = hb;
+    int is = 0;
+    const uint16_t* iq = nullptr;
+    const uint16_t* io = nullptr;
+    const float* il = nullptr;
+    const float* idl = nullptr;
+    int64_t irem = 0;
+    auto cursor_set = [&]() {
+        const int64_t i0 = qt0 * BQ;
+        iq = p.q + (int64_t)ih * p.q_hs + i0 * p.q_rs;
+        io = p.dO + (int64_t)ih * p.do_hs + i0 * p.do_rs;
+        il = p.nlse2 + (int64_t)ih * p.nlse2_hs + i0;
+        idl = p.ndelta + (int64_t)ih * p.ndelta_hs + i0;
+        irem = p.nq - i0;
     };
-    if (total > 0) issue_step(hb, 0, 0);
-    wait_vm_loads();
-    __syncthreads();
+    auto cursor_next = [&]() {
+        if (++is == nsteps) {
+            is = 0;
+            ++ih;
+            cursor_set();
+        } else {
+            iq += BQ * p.q_rs;
+            io += BQ * p.do_rs;
+            il += BQ;
+            idl += BQ;
+            irem -= BQ;
+        }
+    };
+    // LDS byte addresses of ring slot 0's tiles and statistics (wave-uniform)
+    const uint32_t lds_t0 = __builtin_amdgcn_readfirstlane(lds_addr(&smem[0][0][0]));
+    const uint32_t lds_l0 = __builtin_amdgcn_readfirstlane(lds_addr(wave == 0 ? &s_nlse2[0][0] : &s_ndelta[0][0]));
+    const bool fast_rs = p.q_rs < TileDma64<HD, false>::kMaxRs && p.do_rs < TileDma64<HD, false>::kMaxRs;
+    // load k of the cursor's step into ring slot b: k < NI: block k of the
+    // wave's quarter of the Q tile; k < 2 NI: the same of the dO tile;
+    // k = 2 NI: -LSE log2(e) (wave 0) or -Delta (wave 1).  A tile with fewer
+    // than 64 valid rows goes by direct_tile64 (the same number of loads).
+    auto issue_one = [&](auto kc, int b) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (k < 2 * NI) {
+            constexpr int t = k / NI, i = k % NI;
+            const uint16_t* src = t == 0 ? iq : io;
+            if (irem >= BQ && fast_rs) {
+                const uint32_t lds = lds_t0 + (uint32_t)b * (2 * TILE) + t * TILE + wave * (NI * 1024) + i * 1024;
+                dma16(src, (t == 0 ? dmq : dmo).voff[i], lds);
+            } else if constexpr (i == 0) {
+                direct_tile64<HD>(smem[b][t], src, t == 0 ? p.q_rs : p.do_rs, irem, wave, lane);
+            }
+        } else {
+            if (wave < 2) {
+                const float* src = wave == 0 ? il : idl;
+                if (irem >= BQ) dma4(src, (uint32_t)lane * 4u, lds_l0 + (uint32_t)b * (BQ * 4));
+                else direct_vec64(wave == 0 ? s_nlse2[b] : s_ndelta[b], src, irem, lane);
+            }
+        }
+    };
+    // until the loads of one step have landed, with those of the step after
+    // it (LPS loads per wave) still in flight when `more`
+    constexpr int LT = 2 * TileDma64<HD, false>::NI;
+    auto wait_step = [&](bool more) {
+        if (!more) wait_vm_le<0>();
+        else if (wave < 2) wait_vm_le<LT + 1>();
+        else wait_vm_le<LT>();
+    };
+    auto barrier = [&]() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
 
-    const OperandOffsets<HD> off(lane);  // K / V / Q / dO operand reads
-    // positions relative to this wave's first key, in 32-bit
+    cursor_set();
+    for (int i = 0; i < 3; ++i) {
+        if (i < total) {
+            static_for<2 * NI + 1>([&](auto kc) __attribute__((always_inline)) { issue_one(kc, i); });
+            cursor_next();
+        }
+    }
+    if (total > 2) {
+        if (wave < 2) wait_vm_le<2 * (LT + 1)>();
+        else wait_vm_le<2 * LT>();
+    } else {
+        wait_step(total > 1);
+    }
+    barrier();
+
+    const OperandOffsets<HD> off(lane);
     const int64_t wkpos = p.k_pos0 + wj0;
     const int krel = l32;
-    // cursor (head, query step) of step n, and of step n + 1
-    int h_cur = hb;
-    int64_t s_cur = 0;
-    for (int64_t n = 0; n < total; ++n) {
-        const int buf = (int)(n & 1);
-        int h_nxt = h_cur;
-        int64_t s_nxt = s_cur + 1;
-        if (s_nxt == nsteps) {
-            s_nxt = 0;
-            ++h_nxt;
-        }
-        if (n + 1 < total) issue_step(h_nxt, s_nxt, buf ^ 1);
-        const int64_t r0 = (qt0 + s_cur) * BQ + rh * WQ;  // first row of this wave
-        // a wave works on the tile only if some of its rows sees one of its keys
-        const bool live = wj0 < p.nk && r0 < p.nq && (!p.causal || r0 + WQ - 1 >= wkpos);
-        if (live) {
-            const char* Qs = smem[buf][0];
-            const char* Os = smem[buf][1];
-            const float* sl = s_nlse2[buf] + rh * WQ;
-            // dP accumulates onto -Delta of each register's row, so it comes out
-            // as dP - Delta (register r holds row (r / 4) * 8 + hi * 4 + r % 4)
-            f32x16 sacc[1], dpacc[1];
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4 nd = *reinterpret_cast<const f32x4*>(s_ndelta[buf] + rh * WQ + g4 * 8 + hi * 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dpacc[0][g4 * 4 + e] = nd[e];
+    const bool edge_k = wj0 + WK > p.nk;
+    // query steps of each head that need the causal / ragged mask for this
+    // wave: the first d_end (tiles starting before the wave's last key) and
+    // the last one when its tile runs past nq; a wave with keys past nk masks
+    // every step.  The steps in between see all of the wave's keys in all rows.
+    int d_end = 0;
+    if (p.causal) {
+        const int64_t t = (wkpos + WK - 2 + BQ) / BQ - qt0;
+        d_end = t < 0 ? 0 : (t > nsteps ? nsteps : (int)t);
+    }
+    const int u_end = nsteps - (((qt0 + nsteps) * BQ > p.nq) ? 1 : 0);
+
+    // operand A of MFMA g of a step in ring slot `slot`: Q / dO rows of block
+    // g / PH (S, dP phases) or their transposed 16-row slices (dV, dK phases)
+    auto rd = [&](auto gc, int slot) __attribute__((always_inline)) -> bf16x8 {
+        constexpr int g = decltype(gc)::value, ph = g / PH, idx = g % PH;
+        const char* Qs = smem[slot][0];
+        const char* Os = smem[slot][1];
+        if constexpr (ph < 2)
+            return lds_read_b128(idx < NS ? Qs : Os, off.row[idx % NS] + ph * 32 * HD * 2);
+        else
+            return lds_read_tr_at<HD>((idx & 1) ? Qs : Os, off, (ph - 2) * 32 + ((idx >> 1) & 1) * 16, idx >> 2);
+    };
+    bf16x8 ring[DIST];
+    static_for<DIST>([&](auto gc) __attribute__((always_inline)) { ring[decltype(gc)::value] = rd(gc, 0); });
+
+    // one step (ring slot n % 4): the MFMAs of the S and dP phases and of the
+    // first dV / dK block with the vector work interleaved; then a barrier
+    // (after waiting for the next step's loads), the second dV / dK block with
+    // the loads of step n + 3 and the first operand reads of step n + 1
+    auto step = [&](auto mask_tag, int n, int s) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const int slot = (int)(n & (NBUF - 1));
+        const int nslot = (slot + 1) & (NBUF - 1);
+        const int lslot = (slot + 3) & (NBUF - 1);
+        const bool load = n + 3 < total;
+        const int64_t i0 = (qt0 + s) * BQ;
+        bool live = true;
+        if constexpr (MASK) live = wj0 < p.nk && i0 < p.nq && (!p.causal || i0 + BQ - 1 >= wkpos);
+        const float* sl = s_nlse2[slot];
+        const float* sd = s_ndelta[slot];
+        // rows relative to the wave's first key; keys past nk and rows past
+        // nq are invisible; non-causal sees every row
+        const int qrel0 = (int)(p.causal ? i0 - wkpos : WK + i0);
+        const int qlim = (int)(p.causal ? p.nq - wkpos : WK + p.nq);
+        const int kr = (myk < p.nk) ? krel : (1 << 30);
+        f32x16 sacc[2], dpacc[2];
+        bf16x8 pb[2][2], dsb[2][2];
+        f32x4 L[2][4];
+        float px[2][2];
+        auto group = [&](auto gc) __attribute__((always_inline)) {
+            constexpr int g = decltype(gc)::value, ph = g / PH, idx = g % PH;
+            if constexpr (g == 3 * PH) {
+                wait_step(n + 2 < total);
+                barrier();
             }
-            // MFMA j: S (even j) or dP (odd j) over d 16 (j / 2) ..; both of
-            // its operands are read DIST MFMAs ahead
             {
-                constexpr int NJ = 2 * NS, DIST = 2;
-                auto rd = [&](int j, bf16x8& x, bf16x8& y) {
-                    const int st = j >> 1;
-                    const int ko = off.row[st] + kw * 32 * HD * 2;
-                    const int qo = off.row[st] + rh * 32 * HD * 2;
-                    x = lds_read_b128((j & 1) ? Os : Qs, qo);
-                    y = lds_read_b128(skv[j & 1], ko);
-                };
-                bf16x8 ra[DIST], rb[DIST];
+                const bf16x8 a = ring[g % DIST];
+                if constexpr (g + DIST < NG) ring[g % DIST] = rd(std::integral_constant<int, g + DIST>{}, slot);
+                // dP accumulators start at -Delta of their rows
+                if constexpr (g < 2) {
 #pragma unroll
-                for (int j = 0; j < DIST; ++j) rd(j, ra[j], rb[j]);
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const f32x4 nd = *reinterpret_cast<const f32x4*>(sd + g * 32 + g4 * 8 + hi * 4);
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    const bf16x8 a = ra[j % DIST], b = rb[j % DIST];
-                    if (j + DIST < NJ) rd(j + DIST, ra[j % DIST], rb[j % DIST]);
-                    const int st = j >> 1;
-                    if (j & 1) dpacc[0] = mfma32(a, b, dpacc[0]);
-                    else sacc[0] = mfma32(a, b, st == 0 ? f32x16{} : sacc[0]);
-                    __builtin_amdgcn_sched_barrier(0);
+                        for (int e = 0; e < 4; ++e) dpacc[g][g4 * 4 + e] = nd[e];
+                    }
                 }
+                // -LSE log2(e) of the rows of element quad g4, two groups
+                // before the first exponential that needs it
+                static_for<2>([&](auto bc) __attribute__((always_inline)) {
+                    constexpr int b = decltype(bc)::value, base = (b + 1) * PH + 1;
+                    static_for<4>([&](auto qc) __attribute__((always_inline)) {
+                        constexpr int g4 = decltype(qc)::value;
+                        if constexpr (g == base + 2 * g4 * GPP - 2)
+                            L[b][g4] = *reinterpret_cast<const f32x4*>(sl + b * 32 + g4 * 8 + hi * 4);
+                    });
+                });
+                if constexpr (ph < 2) {
+                    constexpr int st = idx % NS;
+                    if constexpr (idx < NS) sacc[ph] = mfma32(a, kf[st], st == 0 ? f32x16{} : sacc[ph]);
+                    else dpacc[ph] = mfma32(a, vf[st], dpacc[ph]);
+                } else {
+                    constexpr int qb = ph - 2, db = idx >> 2, h2 = (idx >> 1) & 1;
+                    if constexpr (MASK) {
+                        if constexpr (idx & 1) mfma32_agpr_padded(dk[db], a, dsb[qb][h2]);
+                        else mfma32_agpr_padded(dv[db], a, pb[qb][h2]);
+                    } else {
+                        if constexpr (idx & 1) mfma32_agpr(dk[db], a, dsb[qb][h2]);
+                        else mfma32_agpr(dv[db], a, pb[qb][h2]);
+                    }
+                }
+                // P and dS of score element pairs: pair j of block b takes its
+                // exponentials at group base + j GPP and its products and
+                // bf16 conversions one group later, so that no group waits on
+                // a result of its own vector work
+                static_for<2>([&](auto bc) __attribute__((always_inline)) {
+                    constexpr int b = decltype(bc)::value, base = (b + 1) * PH + 1;
+                    static_for<8>([&](auto jc) __attribute__((always_inline)) {
+                        constexpr int j = decltype(jc)::value, r = 2 * j, g4 = r >> 2, e = r & 3;
+                        if constexpr (g == base + j * GPP) {
+                            float x0 = fast_exp2(__builtin_fmaf(sacc[b][r], p.scale_log2, L[b][g4][e]));
+                            float x1 = fast_exp2(__builtin_fmaf(sacc[b][r + 1], p.scale_log2, L[b][g4][e + 1]));
+                            if constexpr (MASK) {
+                                const int qrel = qrel0 + b * 32 + g4 * 8 + hi * 4 + e;
+                                x0 = (kr <= qrel && qrel < qlim) ? x0 : 0.f;
+                                x1 = (kr <= qrel + 1 && qrel + 1 < qlim) ? x1 : 0.f;
+                            }
+                            px[j & 1][0] = x0;
+                            px[j & 1][1] = x1;
+                        }
+                        if constexpr (g == base + j * GPP + 1) {
+                            const float x0 = px[j & 1][0], x1 = px[j & 1][1];
+                            const bf16x2 pk = to_bf16x2(x0, x1);
+                            const bf16x2 d2 = to_bf16x2(x0 * dpacc[b][r], x1 * dpacc[b][r + 1]);
+                            pb[b][r >> 3][r & 7] = pk[0];
+                            pb[b][r >> 3][(r & 7) + 1] = pk[1];
+                            dsb[b][r >> 3][r & 7] = d2[0];
+                            dsb[b][r >> 3][(r & 7) + 1] = d2[1];
+                        }
+                    });
+                });
             }
-            bf16x8 pb[1][2], dsb[1][2];
-            const bool edge_k = wj0 + WK > p.nk;
-            const bool edge_q = r0 + WQ > p.nq;
-            const bool diag = p.causal && r0 < wkpos + WK - 1;
-            if (edge_k || edge_q || diag) {
-                // rows relative to the wave's first key; keys past nk and rows
-                // past nq are invisible; non-causal sees every row
-                const int qrel0 = (int)(p.causal ? r0 - wkpos : WK + r0);
-                const int qlim = (int)(p.causal ? p.nq - wkpos : WK + p.nq);
-                const int kr = (myk < p.nk) ? krel : (1 << 30);
-                dkdv_p_ds<1, true>(sacc, dpacc, sl, hi, p.scale_log2, qrel0, kr, qlim, pb, dsb);
+            // the loads of step n + 3, spread over the last phase
+            if constexpr (g >= 3 * PH && g <= 3 * PH + 2 * NI) {
+                if (load) issue_one(std::integral_constant<int, g - 3 * PH>{}, lslot);
+            }
+            if constexpr (g == 3 * PH + 2 * NI) {
+                if (load) cursor_next();
+            }
+            // the first operands of step n + 1
+            if constexpr (g + DIST >= NG) ring[g % DIST] = rd(std::integral_constant<int, g + DIST - NG>{}, nslot);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        if constexpr (!MASK) {
+            static_for<NG>(group);
+        } else if (live) {
+            static_for<NG>(group);
+            agpr_settle(dk, dv);
+        } else {
+            // no row of the tile sees the wave's keys: only the barrier, the
+            // loads of step n + 3 and the first operand reads of step n + 1
+            wait_step(n + 2 < total);
+            barrier();
+            if (load) {
+                static_for<2 * NI + 1>([&](auto kc) __attribute__((always_inline)) { issue_one(kc, lslot); });
+                cursor_next();
+            }
+            static_for<DIST>([&](auto gc) __attribute__((always_inline)) {
+                ring[decltype(gc)::value] = rd(gc, nslot);
+            });
+        }
+    };
+
+    int n = 0;
+    for (int h = hb; h < he; ++h) {
+        int s = 0;
+        while (s < nsteps) {
+            if (edge_k || s < d_end || s >= u_end) {
+                step(std::integral_constant<bool, true>{}, n, s);
+                ++s;
+                ++n;
             } else {
-                dkdv_p_ds<1, false>(sacc, dpacc, sl, hi, p.scale_log2, 0, 0, 0, pb, dsb);
-            }
-            // dV^T += dO^T P and dK^T += Q^T dS, reduction over the wave's 32 rows
-            {
-                // MFMA j: dV (even j) or dK (odd j) of d block j / 4, rows
-                // 16 ((j / 2) % 2) ..; its A operand is read 2 MFMAs ahead
-                constexpr int NJ = 4 * NDB, DIST = 3;
-                auto rd = [&](int j) {
-                    return lds_read_tr_at<HD>((j & 1) ? Qs : Os, off, rh * 32 + ((j >> 1) & 1) * 16, j >> 2);
-                };
-                bf16x8 ring[DIST];
-#pragma unroll
-                for (int j = 0; j < DIST; ++j) ring[j] = rd(j);
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    const bf16x8 a = ring[j % DIST];
-                    if (j + DIST < NJ) ring[j % DIST] = rd(j + DIST);
-                    const int db = j >> 2, h2 = (j >> 1) & 1;
-                    if (j & 1) dk[db] = mfma32(a, dsb[0][h2], dk[db]);
-                    else dv[db] = mfma32(a, pb[0][h2], dv[db]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                for (; s < u_end; ++s, ++n) step(std::integral_constant<bool, false>{}, n, s);
+                agpr_settle(dk, dv);
             }
         }
-        h_cur = h_nxt;
-        s_cur = s_nxt;
-        wait_vm_loads();
-        __syncthreads();
     }
 
-    // group continuing in the next chunk: each row half leaves its own sums
+    if (myk >= p.nk) return;
     if (GLOOP && kvl == p.carry_kv_out) {
-        if (myk >= p.nk) return;
-        float* ck = p.carry_out_k + rh * p.carry_hs + myk * HD;
-        float* cv = p.carry_out_v + rh * p.carry_hs + myk * HD;
+        float* ck = p.carry_out_k + myk * HD;
+        float* cv = p.carry_out_v + myk * HD;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -334,46 +457,15 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
         }
         return;
     }
-
-    // the two waves of a key block hold partial sums over the two row halves:
-    // waves 4-7 hand theirs over through LDS (free after the last barrier) and
-    // waves 0-3 add them, lower half first
-    f32x4* xk = reinterpret_cast<f32x4*>(&smem[0][0][0]) + kw * (NDB * 4 * 64);
-    f32x4* xv = reinterpret_cast<f32x4*>(&skv[0][0]) + kw * (NDB * 4 * 64);
-    if (rh == 1) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                f32x4 x, y;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[e] = dk[db][g4 * 4 + e];
-                    y[e] = dv[db][g4 * 4 + e];
-                }
-                xk[(db * 4 + g4) * 64 + lane] = x;
-                xv[(db * 4 + g4) * 64 + lane] = y;
-            }
-        }
-    }
-    __syncthreads();
-    if (rh == 1 || myk >= p.nk) return;
     if constexpr (GLOOP) {
-        // the group is complete: bf16(scale * dK), bf16(dV)
         uint16_t* ok = p.dk + (int64_t)kvl * p.dk_hs + myk * p.dk_rs;
         uint16_t* ov = p.dv + (int64_t)kvl * p.dk_hs + myk * p.dk_rs;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4 uk = xk[(db * 4 + g4) * 64 + lane];
-                const f32x4 uv = xv[(db * 4 + g4) * 64 + lane];
-                f32x4 x, y;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[e] = dk[db][g4 * 4 + e] + uk[e];
-                    y[e] = dv[db][g4 * 4 + e] + uv[e];
-                }
+                const f32x4 x = {dk[db][g4 * 4], dk[db][g4 * 4 + 1], dk[db][g4 * 4 + 2], dk[db][g4 * 4 + 3]};
+                const f32x4 y = {dv[db][g4 * 4], dv[db][g4 * 4 + 1], dv[db][g4 * 4 + 2], dv[db][g4 * 4 + 3]};
                 const bf16x2 k0 = to_bf16x2(x[0] * p.scale, x[1] * p.scale);
                 const bf16x2 k1 = to_bf16x2(x[2] * p.scale, x[3] * p.scale);
                 const bf16x2 v0 = to_bf16x2(y[0], y[1]), v1 = to_bf16x2(y[2], y[3]);
@@ -388,13 +480,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(DkdvParams p) {
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4 ok = xk[(db * 4 + g4) * 64 + lane];
-                const f32x4 ov = xv[(db * 4 + g4) * 64 + lane];
                 f32x4 x, y;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    x[e] = dk[db][g4 * 4 + e] + ok[e];
-                    y[e] = dv[db][g4 * 4 + e] + ov[e];
+                    x[e] = dk[db][g4 * 4 + e];
+                    y[e] = dv[db][g4 * 4 + e];
                 }
                 *reinterpret_cast<f32x4*>(ak + db * 32 + g4 * 8 + hi * 4) = x;
                 *reinterpret_cast<f32x4*>(av + db * 32 + g4 * 8 + hi * 4) = y;
@@ -687,7 +777,7 @@ hipError_t launch_dkdv(const DkdvParams& p, int D, hipStream_t st) {
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     // die-aware runs of work items unless the unit count is a multiple of 4
     const bool runs = units % 4 != 0;
-    const dim3 grid((unsigned)blocks), block(512);
+    const dim3 grid((unsigned)blocks), block(256);
 #define HC_DKDV(HD, R, G) hipLaunchKernelGGL((dkdv_kernel<HD, R, G>), grid, block, 0, st, p)
     if (D != 128 && D != 64) return hipErrorInvalidValue;
     if (p.group_loop) {

@@ -24,6 +24,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace hc {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -158,6 +161,35 @@ __device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds_base) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                  :: "v"(src), "s"(m0) : "memory");
+}
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1: fully unrolled, with i a
+// compile-time constant in every call
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Wait until at most N vector-memory loads of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm_le() {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Direct global -> LDS loads with a wave-uniform 64-bit global base, a
+// per-lane byte offset and a wave-uniform LDS byte address: lane l writes its
+// 16 / 4 bytes at lds + 16 l / 4 l.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(gbase), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :: "v"(voff), "s"(gbase), "s"(lds) : "memory");
 }
 
 // 64-row x HD-column bf16 tile loaded straight from global memory into the

@@ -475,10 +475,8 @@ int dkdv_run(Common& c, const hc::Chunk& ch, int ci, const BwdIO& io, const uint
         LAUNCH_PASS(K_REDUCE, rd, hc::launch_dkdv_reduce(rd, c.st));
         return ATTN_OK;
     }
-    // carries: [2][S][D] fp32 per slot (lower, upper row halves), at this
-    // launch's first key
+    // carries: [S][D] fp32 per slot, at this launch's first key
     const int in_s = p.carry_in_slot(ci), out_s = p.carry_out_slot(ci);
-    d.carry_hs = p.S * D;
     if (in_s >= 0) {
         d.carry_in_k = reinterpret_cast<const float*>(c.ws + p.carry_k[in_s]) + (size_t)kr0 * D;
         d.carry_in_v = reinterpret_cast<const float*>(c.ws + p.carry_v[in_s]) + (size_t)kr0 * D;

@@ -91,12 +91,10 @@ struct PrepParams {
 //    order.  Rows of part_* are keys of this launch (0..nk).
 //  * group loop (group_loop = 1): one workgroup per (key tile, kv head of the
 //    chunk) walks the chunk's heads of that group, ascending, each over its
-//    query tiles, ascending, into the same fp32 registers.  The two row
-//    halves of every key block keep separate sums; a group that continues in
-//    the next chunk leaves both in carry_out ([2][..][D]: lower half, then
-//    upper half carry_hs elements further) and resumes from carry_in; a
-//    finished group writes bf16(scale * (lower + upper)) to dk and
-//    bf16(lower + upper) to dv (strides dk_rs, dk_hs), with no reduce pass.
+//    query tiles, ascending, into the same fp32 registers.  A group that
+//    continues in the next chunk leaves its fp32 sums in carry_out ([nk][D])
+//    and resumes from carry_in; a finished group writes bf16(scale * dK) to
+//    dk and bf16(dV) to dv (strides dk_rs, dk_hs), with no reduce pass.
 struct DkdvParams {
     const uint16_t* q;  int64_t q_rs, q_hs;    // chunk query heads (local 0..nh)
     const uint16_t* dO; int64_t do_rs, do_hs;
@@ -115,7 +113,6 @@ struct DkdvParams {
     int nkv;                                   // kv heads of the chunk
     const float* carry_in_k; const float* carry_in_v; int carry_kv_in;  // local kv head or -1
     float* carry_out_k; float* carry_out_v; int carry_kv_out;
-    int64_t carry_hs;                          // elements from a carry's lower to upper half
     uint16_t* dk; uint16_t* dv; int64_t dk_rs, dk_hs;
     float scale;
 };
@@ -211,7 +208,7 @@ hipError_t launch_gemm_reduce(const GemmReduceParams& p, hipStream_t st);
 // waves, one per compute unit) once a launch has at least kWideMinBlocks of
 // them, else 128-row workgroups (4 waves, two per compute unit); the rows of
 // each query are computed the same way in both, bit for bit.  dK/dV
-// workgroups take 128 keys.
+// workgroups take 128 keys (4 waves, one per compute unit).
 constexpr int kWideMinBlocks = 256;
 constexpr int kDkdvBlockN = 128;
 

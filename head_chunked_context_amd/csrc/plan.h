@@ -50,7 +50,7 @@ struct Plan {
     size_t ring_k[2] = {0, 0}, ring_v[2] = {0, 0};      // trunk ring slots
     size_t do_c = 0, delta_c = 0, lse2_c = 0, dq_acc = 0; // bwd chunk buffers
     size_t part_k = 0, part_v = 0;                      // bwd per-head fp32 dK/dV (not group_loop)
-    size_t carry_k[2] = {0, 0}, carry_v[2] = {0, 0};    // bwd fp32 carries ([2][S][D] if group_loop)
+    size_t carry_k[2] = {0, 0}, carry_v[2] = {0, 0};    // bwd fp32 carries ([S][D])
     size_t stage_k[2] = {0, 0}, stage_v[2] = {0, 0};    // bwd dK/dV staging
     size_t total = 0;
 
@@ -181,12 +181,9 @@ static inline int make_plan(bool bwd, int64_t S, int Hq, int Hkv, int D, int cau
                 p.stage_v[s] = take(p.kvc * Et);
             }
         }
-        // group loop: the two row halves of every key block keep their own
-        // fp32 sums until the group's last head, so a carry holds both
-        const size_t carry = p.group_loop ? E * 4 : E * 2;
         for (int s = 0; s < p.carry_slots; ++s) {
-            p.carry_k[s] = take(carry);                       // fp32 [S][D] or [2][S][D]
-            p.carry_v[s] = take(carry);
+            p.carry_k[s] = take(E * 2);                       // fp32 [S][D]
+            p.carry_v[s] = take(E * 2);
         }
     }
     p.total = off;

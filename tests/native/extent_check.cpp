@@ -16,9 +16,10 @@
 // size the planner carves (so a read that runs from one region into the next,
 // or past the workspace, is reported even though it stays in mapped memory).
 //
-// With --plant-dkdv-overread the dK/dV key-tile load is replayed as it once
-// was written (the second 64-key half of a short last tile loaded from key
-// j0 + 64), which must be reported: evidence that the check sees reads.
+// With --plant-dkdv-overread the dK/dV kernel's loads of K and V rows into
+// registers are replayed without their clamp (lanes past the last key of a
+// short last tile reading their own key row), which must be reported:
+// evidence that the check sees reads.
 #include <hip/hip_runtime_api.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -315,22 +316,15 @@ hipError_t launch_dkdv(const DkdvParams& p, int HD, hipStream_t) {
         if (kvl < 0 || kvl >= (p.group_loop ? p.nkv : 1 << 30))
             fail_msg("kv head %#llx out of range (%llu)", "dkdv kv head", (uintptr_t)kvl, 0);
         const int64_t j0 = kt * BNK;
-        if (j0 < p.nk) {
-            const int64_t nv = p.nk - j0;
-            for (int rh = 0; rh < 2; ++rh) {
-                const int64_t rs = rh == 0 ? p.k_rs : p.v_rs;
-                const uint16_t* src = rh == 0 ? p.k + (int64_t)kvl * p.k_hs + j0 * p.k_rs
-                                              : p.v + (int64_t)kvl * p.v_hs + j0 * p.v_rs;
-                const char* what = rh == 0 ? "dkdv K tile" : "dkdv V tile";
-                tile64(src, rs, nv, HD, what);
-                if (g_plant)
-                    tile64(src + 64 * rs, rs, nv > 64 ? nv - 64 : 1, HD, what);
-                else if (nv > 64)
-                    tile64(src + 64 * rs, rs, nv - 64, HD, what);
-                else
-                    tile64(src + (nv - 1) * rs, rs, 1, HD, what);
+        // each lane's key row of K and V (16-byte reads of its 8-column
+        // slices), clamped to the last key
+        for (int kw = 0; kw < 4; ++kw)
+            for (int l = 0; l < 32; ++l) {
+                const int64_t myk = j0 + kw * 32 + l;
+                const int64_t kk = g_plant ? myk : (myk < p.nk ? myk : p.nk - 1);
+                touch(p.k + (int64_t)kvl * p.k_hs + kk * p.k_rs, HD * 2, "dkdv K row");
+                touch(p.v + (int64_t)kvl * p.v_hs + kk * p.v_rs, HD * 2, "dkdv V row");
             }
-        }
         const int64_t nqt = (p.nq + BQ - 1) / BQ;
         int64_t qt0 = 0;
         if (p.causal) {
@@ -356,15 +350,13 @@ hipError_t launch_dkdv(const DkdvParams& p, int HD, hipStream_t) {
                     touch(at(p.part_v, ((int64_t)hb * p.nk + myk) * HD), HD * 4, "dkdv dV partial");
                     continue;
                 }
-                for (int rh = 0; rh < 2; ++rh) {
-                    if (kvl == p.carry_kv_in) {
-                        touch(at(p.carry_in_k, rh * p.carry_hs + myk * HD), HD * 4, "dkdv carry in dK");
-                        touch(at(p.carry_in_v, rh * p.carry_hs + myk * HD), HD * 4, "dkdv carry in dV");
-                    }
-                    if (kvl == p.carry_kv_out) {
-                        touch(at(p.carry_out_k, rh * p.carry_hs + myk * HD), HD * 4, "dkdv carry out dK");
-                        touch(at(p.carry_out_v, rh * p.carry_hs + myk * HD), HD * 4, "dkdv carry out dV");
-                    }
+                if (kvl == p.carry_kv_in) {
+                    touch(at(p.carry_in_k, myk * HD), HD * 4, "dkdv carry in dK");
+                    touch(at(p.carry_in_v, myk * HD), HD * 4, "dkdv carry in dV");
+                }
+                if (kvl == p.carry_kv_out) {
+                    touch(at(p.carry_out_k, myk * HD), HD * 4, "dkdv carry out dK");
+                    touch(at(p.carry_out_v, myk * HD), HD * 4, "dkdv carry out dV");
                 }
                 if (kvl != p.carry_kv_out) {
                     touch(at(p.dk, (int64_t)kvl * p.dk_hs + myk * p.dk_rs), HD * 2, "dkdv dK out");
@@ -597,8 +589,8 @@ static void add_workspace(char* ws, const hc::Plan& p) {
             }
         }
         for (int s = 0; s < p.carry_slots; ++s) {
-            R(p.carry_k[s], p.group_loop ? E * 4 : E * 2, "ws dK carry");
-            R(p.carry_v[s], p.group_loop ? E * 4 : E * 2, "ws dV carry");
+            R(p.carry_k[s], E * 2, "ws dK carry");
+            R(p.carry_v[s], E * 2, "ws dV carry");
         }
     }
 }

@@ -84,10 +84,10 @@ static void check_plan(const hc::Plan& p) {
                 r.push_back({p.stage_v[s], p.kvc * Et});
             }
         }
-        // carries: fp32 [S][D], or [2][S][D] (both row halves) in the group loop
+        // carries: fp32 [S][D]
         for (int s = 0; s < p.carry_slots; ++s) {
-            r.push_back({p.carry_k[s], p.group_loop ? E * 4 : E * 2});
-            r.push_back({p.carry_v[s], p.group_loop ? E * 4 : E * 2});
+            r.push_back({p.carry_k[s], E * 2});
+            r.push_back({p.carry_v[s], E * 2});
         }
     }
     std::sort(r.begin(), r.end(), [](const Region& a, const Region& b) { return a.off < b.off; });

@@ -72,15 +72,15 @@ def test_backward_workspace_formula_aligned_chunks():
 
 def test_backward_workspace_formula_group_loop():
     # S >= 65536: the group-loop dK/dV schedule keeps no per-head fp32
-    # partials; a group spanning chunks carries both row halves' fp32 sums
+    # partials; a group spanning chunks carries its fp32 sums
     S, Hq, Hkv, D = 262144, 32, 8, 128
     for hc_ in (4, 8, 32):
         kvc = hc_ // 4
         want = 2 * A(hc_ * E(S, D)) + 2 * A(hc_ * S * 4) + 2 * A(kvc * E(S, D))
         assert hc.bwd_workspace_bytes(S, Hq, Hkv, D, True, hc_, 0) == want
-    # hc = 1 and 2 (g = 4): one carry slot of [2][S][D] fp32 for dK and for dV
+    # hc = 1 and 2 (g = 4): one carry slot of [S][D] fp32 for dK and for dV
     for hc_ in (1, 2):
-        want = 2 * A(hc_ * E(S, D)) + 2 * A(hc_ * S * 4) + 2 * A(E(S, D)) + 2 * A(4 * E(S, D))
+        want = 2 * A(hc_ * E(S, D)) + 2 * A(hc_ * S * 4) + 2 * A(E(S, D)) + 2 * A(2 * E(S, D))
         assert hc.bwd_workspace_bytes(S, Hq, Hkv, D, True, hc_, 0) == want
 
 

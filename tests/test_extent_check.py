@@ -4,7 +4,8 @@ against a fake HIP runtime that replays each kernel's index arithmetic on the
 host (tests/native/extent_check.cpp), built with the address and
 undefined-behaviour sanitizers, over ~1400 shapes around tile, workgroup and
 trunk edges with exactly sized user tensors and workspace regions.  A planted
-copy of a load that once read past the last key must be reported, and HIP
+copy of the dK/dV kernel's K/V row loads without their clamp to the last key
+must be reported, and HIP
 failures injected into copies and kernel launches must come back as
 ATTN_EHIP without breaking the next call."""
 import os
@@ -49,7 +50,7 @@ def test_every_kernel_access_stays_in_its_region(extent_exe):
 def test_planted_over_read_is_reported(extent_exe):
     r = _run(extent_exe, "--plant-dkdv-overread")
     assert r.returncode == 1
-    assert "dkdv V tile" in r.stderr and "failures: 0" not in r.stdout
+    assert "dkdv V row" in r.stderr and "failures: 0" not in r.stdout
 
 
 def test_injected_copy_and_launch_failures_surface_and_leave_no_state(extent_exe):
