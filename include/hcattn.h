@@ -268,7 +268,7 @@ int attn_set_trunk_merge(int on);
  * 65536) take the group-loop schedule: one workgroup per (128-key tile, kv
  * head) walks the chunk's heads of that group and writes bf16 dK/dV itself
  * (no per-head fp32 partials in the workspace, no reduce pass; a group that
- * spans chunks carries fp32 sums of its two row halves).  Shorter sequences
+ * spans chunks carries its fp32 sums).  Shorter sequences
  * keep one workgroup per (key tile, query head) with per-head partials and
  * an ordered reduce, which spreads the causal triangle over more
  * workgroups.  Both are deterministic and bitwise identical across

@@ -1,6 +1,6 @@
 """The group-loop dK/dV schedule (one workgroup per key tile and kv head walks
-the chunk's heads of the group; fp32 carries of both row halves when a group
-spans chunks; bf16 dK/dV written without partials or a reduce pass).  Long
+the chunk's heads of the group; an fp32 carry of its sums when a group spans
+chunks; bf16 dK/dV written without partials or a reduce pass).  Long
 sequences (S >= 65536) take it by default and are checked at full size in
 test_gpu_large.py; here it is forced at small S (attn_set_group_loop_min_s)
 so that every element can be compared with the oracle."""
