@@ -199,8 +199,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
     auto cursor_next = [&]() {
         if (++is == nsteps) {
             is = 0;
-            ++ih;
-            cursor_set();
+            if (++ih < he) cursor_set();
         } else {
             iq += BQ * p.q_rs;
             io += BQ * p.do_rs;
@@ -775,6 +774,8 @@ hipError_t launch_dkdv(const DkdvParams& p, int D, hipStream_t st) {
     if (p.nk <= 0 || units <= 0) return hipSuccess;
     const int64_t blocks = (p.nk + kDkdvBlockN - 1) / kDkdvBlockN * units;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    // a workgroup counts its steps (query tiles x heads of its group) in 32 bits
+    if ((p.nq + 63) / 64 * (p.group_loop ? p.group : 1) > 0x7fffffffLL) return hipErrorInvalidValue;
     // die-aware runs of work items unless the unit count is a multiple of 4
     const bool runs = units % 4 != 0;
     const dim3 grid((unsigned)blocks), block(256);

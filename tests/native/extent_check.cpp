@@ -275,6 +275,7 @@ hipError_t launch_dkdv(const DkdvParams& p, int HD, hipStream_t) {
     if (p.nk <= 0 || units <= 0) return hipSuccess;
     const int BQ = 64, BNK = 128;
     const int64_t blocks = (p.nk + BNK - 1) / BNK * units;
+    if ((p.nq + 63) / 64 * (p.group_loop ? p.group : 1) > 0x7fffffffLL) return hipErrorInvalidValue;
     const bool runs = units % 4 != 0;
     std::vector<char> seen((size_t)blocks, 0);
     for (int64_t b = 0; b < blocks; ++b) {
