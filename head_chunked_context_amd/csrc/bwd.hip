@@ -82,6 +82,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
     constexpr int GPP = PH / 8;       // groups per pair of score elements
     constexpr int NG = 4 * PH;        // MFMA groups per step
     constexpr int DIST = 4;           // operand reads ahead (divides NG)
+    // the step's barrier, and after it the loads of the step three ahead,
+    // sit 3/8 of the way into the last phase (group 54 of 64 at D = 128):
+    // late enough that the slowest wave rarely holds the others there, early
+    // enough for the loads to be issued and the barrier to have published
+    // the next step's tiles before its first operand reads
+    constexpr int BAR_G = 3 * PH + 6 * PH / 16;
+    static_assert(BAR_G + 2 * NI < NG && BAR_G <= NG - DIST, "barrier placement");
     __shared__ __attribute__((aligned(1024))) char smem[NBUF][2][TILE];  // [slot][Q / dO]
     __shared__ __attribute__((aligned(16))) float s_nlse2[NBUF][BQ];
     __shared__ __attribute__((aligned(16))) float s_ndelta[NBUF][BQ];
@@ -319,7 +326,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
         float px[2][2];
         auto group = [&](auto gc) __attribute__((always_inline)) {
             constexpr int g = decltype(gc)::value, ph = g / PH, idx = g % PH;
-            if constexpr (g == 3 * PH) {
+            if constexpr (g == BAR_G) {
                 wait_step(n + 2 < total);
                 barrier();
             }
@@ -338,7 +345,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
                 // -LSE log2(e) of the rows of element quad g4, two groups
                 // before the first exponential that needs it
                 static_for<2>([&](auto bc) __attribute__((always_inline)) {
-                    constexpr int b = decltype(bc)::value, base = (b + 1) * PH + 1;
+                    constexpr int b = decltype(bc)::value, base = (b + 1) * PH;
                     static_for<4>([&](auto qc) __attribute__((always_inline)) {
                         constexpr int g4 = decltype(qc)::value;
                         if constexpr (g == base + 2 * g4 * GPP - 2)
@@ -362,9 +369,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
                 // P and dS of score element pairs: pair j of block b takes its
                 // exponentials at group base + j GPP and its products and
                 // bf16 conversions one group later, so that no group waits on
-                // a result of its own vector work
+                // a result of its own vector work.  Block b starts right after
+                // its last dP MFMA, so its last conversion lands two groups or
+                // more before the dV/dK MFMA that reads it (an inline MFMA
+                // gets no wait states after a vector write of its operand)
                 static_for<2>([&](auto bc) __attribute__((always_inline)) {
-                    constexpr int b = decltype(bc)::value, base = (b + 1) * PH + 1;
+                    constexpr int b = decltype(bc)::value, base = (b + 1) * PH;
                     static_for<8>([&](auto jc) __attribute__((always_inline)) {
                         constexpr int j = decltype(jc)::value, r = 2 * j, g4 = r >> 2, e = r & 3;
                         if constexpr (g == base + j * GPP) {
@@ -390,11 +400,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
                     });
                 });
             }
-            // the loads of step n + 3, spread over the last phase
-            if constexpr (g >= 3 * PH && g <= 3 * PH + 2 * NI) {
-                if (load) issue_one(std::integral_constant<int, g - 3 * PH>{}, lslot);
+            // the loads of step n + 3, one per group from the barrier on
+            if constexpr (g >= BAR_G && g <= BAR_G + 2 * NI) {
+                if (load) issue_one(std::integral_constant<int, g - BAR_G>{}, lslot);
             }
-            if constexpr (g == 3 * PH + 2 * NI) {
+            if constexpr (g == BAR_G + 2 * NI) {
                 if (load) cursor_next();
             }
             // the first operands of step n + 1
