@@ -72,6 +72,42 @@ __device__ __forceinline__ void agpr_settle(f32x16 (&x)[N], f32x16 (&y)[N]) {
     for (int i = 1; i < N; ++i) asm volatile("" : "+a"(x[i]), "+a"(y[i]));
 }
 
+// LDS reads a dK/dV step issues per MFMA group x (PH MFMAs per phase, NG
+// groups, operands read DIST groups ahead, P/dS pairs every GPP groups), in
+// the order the group issues them: the operand of group x + DIST (one 16-byte
+// read in the S / dP phases, two transposed reads in the dV / dK phases), the
+// -Delta starting values (groups 0 and 1), -LSE log2(e) of a row quad, and
+// at the end of the step the first operands of the next one.
+template <int PH, int NG, int DIST, int GPP>
+struct DkdvLdsOps {
+    static constexpr int rd(int x) { return x + DIST < NG ? ((x + DIST) / PH < 2 ? 1 : 2) : 0; }
+    static constexpr int init(int x) { return x < 2 ? 4 : 0; }
+    static constexpr int lrd(int x) {
+        int c = 0;
+        for (int b = 0; b < 2; ++b)
+            for (int g4 = 0; g4 < 4; ++g4) c += x == (b + 1) * PH + 2 * g4 * GPP - 4;
+        return c;
+    }
+    static constexpr int nxt(int x) { return x + DIST >= NG ? 1 : 0; }
+    static constexpr int all(int x) { return rd(x) + init(x) + lrd(x) + nxt(x); }
+    // reads still allowed in flight at the top of group g once the operands
+    // of MFMAs g and g + 1 have arrived: those issued after the operand of
+    // g + 1 (read in group g + 1 - DIST, or last in that group of the step
+    // before)
+    static constexpr int pair_wait(int g) {
+        const int src = g + 1 - DIST;
+        int k = 0;
+        if (src >= 0) {
+            k = init(src) + lrd(src) + nxt(src);
+            for (int x = src + 1; x < g; ++x) k += all(x);
+        } else {
+            for (int x = NG + src + 1; x < NG; ++x) k += all(x);
+            for (int x = 0; x < g; ++x) k += all(x);
+        }
+        return k > 15 ? 15 : k;
+    }
+};
+
 template <int HD, bool RUNS, bool GLOOP>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
     constexpr int BQ = 64, WK = 32, BNK = 128, NBUF = 4;
@@ -192,62 +228,59 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
     int is = 0;
     const uint16_t* iq = nullptr;
     const uint16_t* io = nullptr;
-    const float* il = nullptr;
-    const float* idl = nullptr;
-    int64_t irem = 0;
+    const float* ist = nullptr;
     auto cursor_set = [&]() {
         const int64_t i0 = qt0 * BQ;
         iq = p.q + (int64_t)ih * p.q_hs + i0 * p.q_rs;
         io = p.dO + (int64_t)ih * p.do_hs + i0 * p.do_rs;
-        il = p.nlse2 + (int64_t)ih * p.nlse2_hs + i0;
-        idl = p.ndelta + (int64_t)ih * p.ndelta_hs + i0;
-        irem = p.nq - i0;
+        ist = ((wave & 1) ? p.ndelta + (int64_t)ih * p.ndelta_hs : p.nlse2 + (int64_t)ih * p.nlse2_hs) + i0;
     };
+    const int64_t q_step = BQ * p.q_rs, do_step = BQ * p.do_rs;
     auto cursor_next = [&]() {
+        iq += q_step;
+        io += do_step;
+        ist += BQ;
         if (++is == nsteps) {
             is = 0;
             if (++ih < he) cursor_set();
-        } else {
-            iq += BQ * p.q_rs;
-            io += BQ * p.do_rs;
-            il += BQ;
-            idl += BQ;
-            irem -= BQ;
         }
     };
     // LDS byte addresses of ring slot 0's tiles and statistics (wave-uniform)
     const uint32_t lds_t0 = __builtin_amdgcn_readfirstlane(lds_addr(&smem[0][0][0]));
-    const uint32_t lds_l0 = __builtin_amdgcn_readfirstlane(lds_addr(wave == 0 ? &s_nlse2[0][0] : &s_ndelta[0][0]));
+    const uint32_t lds_l0 = __builtin_amdgcn_readfirstlane(lds_addr((wave & 1) ? &s_ndelta[0][0] : &s_nlse2[0][0]));
     const bool fast_rs = p.q_rs < TileDma64<HD, false>::kMaxRs && p.do_rs < TileDma64<HD, false>::kMaxRs;
+    // query tiles (from qt0) with all 64 rows inside nq: the cursor's tile is
+    // full while is < nfull
+    const int nfull = (int)((p.nq - qt0 * BQ) / BQ);
+    auto cursor_rows = [&]() { return p.nq - (qt0 + is) * BQ; };
     // load k of the cursor's step into ring slot b: k < NI: block k of the
     // wave's quarter of the Q tile; k < 2 NI: the same of the dO tile;
-    // k = 2 NI: -LSE log2(e) (wave 0) or -Delta (wave 1).  A tile with fewer
-    // than 64 valid rows goes by direct_tile64 (the same number of loads).
+    // k = 2 NI: -LSE log2(e) (waves 0, 2) or -Delta (waves 1, 3; each vector
+    // is written twice with the same values, so that every wave issues the
+    // same number of loads).  A tile with fewer than 64 valid rows goes by
+    // direct_tile64 (the same number of loads).
     auto issue_one = [&](auto kc, int b) __attribute__((always_inline)) {
         constexpr int k = decltype(kc)::value;
         if constexpr (k < 2 * NI) {
             constexpr int t = k / NI, i = k % NI;
             const uint16_t* src = t == 0 ? iq : io;
-            if (irem >= BQ && fast_rs) {
+            if (is < nfull && fast_rs) {
                 const uint32_t lds = lds_t0 + (uint32_t)b * (2 * TILE) + t * TILE + wave * (NI * 1024) + i * 1024;
                 dma16(src, (t == 0 ? dmq : dmo).voff[i], lds);
             } else if constexpr (i == 0) {
-                direct_tile64<HD>(smem[b][t], src, t == 0 ? p.q_rs : p.do_rs, irem, wave, lane);
+                direct_tile64<HD>(smem[b][t], src, t == 0 ? p.q_rs : p.do_rs, cursor_rows(), wave, lane);
             }
         } else {
-            if (wave < 2) {
-                const float* src = wave == 0 ? il : idl;
-                if (irem >= BQ) dma4(src, (uint32_t)lane * 4u, lds_l0 + (uint32_t)b * (BQ * 4));
-                else direct_vec64(wave == 0 ? s_nlse2[b] : s_ndelta[b], src, irem, lane);
-            }
+            if (is < nfull) dma4(ist, (uint32_t)lane * 4u, lds_l0 + (uint32_t)b * (BQ * 4));
+            else direct_vec64((wave & 1) ? s_ndelta[b] : s_nlse2[b], ist, cursor_rows(), lane);
         }
     };
+    // loads per wave and step
+    constexpr int LT = 2 * TileDma64<HD, false>::NI + 1;
     // until the loads of one step have landed, with those of the step after
-    // it (LPS loads per wave) still in flight when `more`
-    constexpr int LT = 2 * TileDma64<HD, false>::NI;
+    // it still in flight when `more`
     auto wait_step = [&](bool more) {
         if (!more) wait_vm_le<0>();
-        else if (wave < 2) wait_vm_le<LT + 1>();
         else wait_vm_le<LT>();
     };
     auto barrier = [&]() {
@@ -264,8 +297,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
         }
     }
     if (total > 2) {
-        if (wave < 2) wait_vm_le<2 * (LT + 1)>();
-        else wait_vm_le<2 * LT>();
+        wait_vm_le<2 * LT>();
     } else {
         wait_step(total > 1);
     }
@@ -304,12 +336,19 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
     // first dV / dK block with the vector work interleaved; then a barrier
     // (after waiting for the next step's loads), the second dV / dK block with
     // the loads of step n + 3 and the first operand reads of step n + 1
-    auto step = [&](auto mask_tag, int n, int s) __attribute__((always_inline)) {
+    // FAST: the loads of step n + 3 are due and take the fast form (a full
+    // tile, row strides in range), so the step issues them unconditionally
+    auto step = [&](auto mask_tag, auto fast_tag, int n, int s) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
+        constexpr bool FAST = decltype(fast_tag)::value;
         const int slot = (int)(n & (NBUF - 1));
         const int nslot = (slot + 1) & (NBUF - 1);
         const int lslot = (slot + 3) & (NBUF - 1);
         const bool load = n + 3 < total;
+        // LDS addresses of the wave's part of the load slot's tiles and of
+        // its statistics vector
+        const uint32_t lds_lt = lds_t0 + (uint32_t)lslot * (2 * TILE) + wave * (NI * 1024);
+        const uint32_t lds_ls = lds_l0 + (uint32_t)lslot * (BQ * 4);
         const int64_t i0 = (qt0 + s) * BQ;
         bool live = true;
         if constexpr (MASK) live = wj0 < p.nk && i0 < p.nq && (!p.causal || i0 + BQ - 1 >= wkpos);
@@ -326,8 +365,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
         float px[2][2];
         auto group = [&](auto gc) __attribute__((always_inline)) {
             constexpr int g = decltype(gc)::value, ph = g / PH, idx = g % PH;
+            // one wait for the operands of two MFMAs (the compiler adds none
+            // before the second)
+            if constexpr (FAST && g % 2 == 0) {
+                __builtin_amdgcn_s_waitcnt(0xC07F | (DkdvLdsOps<PH, NG, DIST, GPP>::pair_wait(g) << 8));
+                __builtin_amdgcn_sched_barrier(0);
+            }
             if constexpr (g == BAR_G) {
-                wait_step(n + 2 < total);
+                if constexpr (FAST) wait_vm_le<LT>();
+                else wait_step(n + 2 < total);
                 barrier();
             }
             {
@@ -342,13 +388,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
                         for (int e = 0; e < 4; ++e) dpacc[g][g4 * 4 + e] = nd[e];
                     }
                 }
-                // -LSE log2(e) of the rows of element quad g4, two groups
-                // before the first exponential that needs it
+                // -LSE log2(e) of the rows of element quad g4, four groups
+                // before the first exponential that needs it (so that the
+                // paired operand waits cover it)
                 static_for<2>([&](auto bc) __attribute__((always_inline)) {
                     constexpr int b = decltype(bc)::value, base = (b + 1) * PH;
                     static_for<4>([&](auto qc) __attribute__((always_inline)) {
                         constexpr int g4 = decltype(qc)::value;
-                        if constexpr (g == base + 2 * g4 * GPP - 2)
+                        if constexpr (g == base + 2 * g4 * GPP - 4)
                             L[b][g4] = *reinterpret_cast<const f32x4*>(sl + b * 32 + g4 * 8 + hi * 4);
                     });
                 });
@@ -402,10 +449,20 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
             }
             // the loads of step n + 3, one per group from the barrier on
             if constexpr (g >= BAR_G && g <= BAR_G + 2 * NI) {
-                if (load) issue_one(std::integral_constant<int, g - BAR_G>{}, lslot);
+                constexpr int k = g - BAR_G;
+                if constexpr (FAST) {
+                    if constexpr (k < 2 * NI) {
+                        constexpr int t = k / NI, i = k % NI;
+                        dma16(t == 0 ? iq : io, (t == 0 ? dmq : dmo).voff[i], lds_lt + t * TILE + i * 1024);
+                    } else {
+                        dma4(ist, (uint32_t)lane * 4u, lds_ls);
+                    }
+                } else if (load) {
+                    issue_one(std::integral_constant<int, k>{}, lslot);
+                }
             }
             if constexpr (g == BAR_G + 2 * NI) {
-                if (load) cursor_next();
+                if (FAST || load) cursor_next();
             }
             // the first operands of step n + 1
             if constexpr (g + DIST >= NG) ring[g % DIST] = rd(std::integral_constant<int, g + DIST - NG>{}, nslot);
@@ -435,12 +492,24 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(DkdvParams p) {
     for (int h = hb; h < he; ++h) {
         int s = 0;
         while (s < nsteps) {
-            if (edge_k || s < d_end || s >= u_end) {
-                step(std::integral_constant<bool, true>{}, n, s);
+            // a run of unmasked steps whose loads take the fast form: steps
+            // that need no mask, while step n + 3 exists and the cursor's
+            // tile is full (every tile of a head is when nfull == nsteps);
+            // any other step goes by the masked body, which also handles the
+            // general loads (its mask keeps every element of an unmasked step)
+            int nf = 0;
+            if (!edge_k && s >= d_end && s < u_end && fast_rs && is < nfull) {
+                nf = u_end - s;
+                if (total - 3 - n < nf) nf = total - 3 - n;
+                if (nfull < nsteps && nfull - is < nf) nf = nfull - is;
+            }
+            if (nf <= 0) {
+                step(std::integral_constant<bool, true>{}, std::integral_constant<bool, false>{}, n, s);
                 ++s;
                 ++n;
             } else {
-                for (; s < u_end; ++s, ++n) step(std::integral_constant<bool, false>{}, n, s);
+                for (const int e = s + nf; s < e; ++s, ++n)
+                    step(std::integral_constant<bool, false>{}, std::integral_constant<bool, true>{}, n, s);
                 agpr_settle(dk, dv);
             }
         }
