@@ -764,6 +764,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
                     return lds_read_b128((j & 1) ? Vs : Ks, off.row[j >> 1] + b * 32 * HD * 2);
                 };
                 bf16x8 ring[DIST];
+                // the S / dP products at a raised wave priority: the SIMD's
+                // other wave, on its dS vector work or its dQ products, then
+                // yields the issue slots to them, so the two waves drift apart
+                // in phase instead of reaching their vector work together
+                __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                 for (int j = 0; j < DIST; ++j) ring[j] = read_a(j);
 #pragma unroll
@@ -776,6 +781,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_kernel(DqParams p) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 bf16x8 dsb[1][2];
+                __builtin_amdgcn_s_setprio(0);
                 if (need_mask) {
                     const int64_t qr = p.causal ? qrel_base - kb - b * 32 : (int64_t)BN;
                     const int kl = (int)(p.nk - kb - b * 32);
