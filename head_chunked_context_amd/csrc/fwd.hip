@@ -195,17 +195,29 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(FwdParams p) {
         if (j < ntiles_w) {
             const char* Ks = smem[buf][0];
             const char* Vs = smem[buf][1];
-            // S^T = K Q^T for two 32-key blocks (first step starts from zero)
+            // S^T = K Q^T for two 32-key blocks (first step starts from zero):
+            // MFMA j covers block j % 2 over d 16 (j / 2) .., its K operand
+            // read 3 MFMAs ahead.  Both product phases run at a raised wave
+            // priority: the SIMD's other wave, on its softmax, yields the
+            // issue slots to them, so the two waves drift apart in phase and
+            // one's vector work runs under the other's products.
             f32x16 s[2];
+            __builtin_amdgcn_s_setprio(1);
+            {
+                constexpr int NJ = 2 * NS, DIST = 3;
+                auto rdk = [&](int j) __attribute__((always_inline)) {
+                    return lds_read_b128(Ks, off.row[j >> 1] + (j & 1) * 32 * HD * 2);
+                };
+                bf16x8 ring[DIST];
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-                s[b] = mfma32(lds_read_b128(Ks, off.row[0] + b * 32 * HD * 2), qf[0], f32x16{});
+                for (int j = 0; j < DIST; ++j) ring[j] = rdk(j);
 #pragma unroll
-            for (int st = 1; st < NS; ++st) {
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    bf16x8 a = lds_read_b128(Ks, off.row[st] + b * 32 * HD * 2);
-                    s[b] = mfma32(a, qf[st], s[b]);
+                for (int j = 0; j < NJ; ++j) {
+                    const bf16x8 a = ring[j % DIST];
+                    if (j + DIST < NJ) ring[j % DIST] = rdk(j + DIST);
+                    const int b = j & 1, st = j >> 1;
+                    s[b] = mfma32(a, qf[st], st == 0 ? f32x16{} : s[b]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             const int64_t kb = (int64_t)j * BN;
@@ -213,6 +225,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(FwdParams p) {
                                    (p.causal && p.k_pos0 + kb + BN - 1 > p.q_pos0 + wq0);
             float alpha;
             bf16x8 pb[2][2];
+            __builtin_amdgcn_s_setprio(0);
             if (need_mask) {
                 const int64_t qr = p.causal ? qrel_base - kb : (int64_t)BN;
                 fwd_softmax<true>(s, p.scale_log2, hi, (int)qr, (int)(p.nk - kb), m, lpart,
@@ -226,18 +239,27 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(FwdParams p) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) o[db] *= alpha;
             }
-            // O^T += V^T P^T: reduction over the tile's 64 keys in 4 steps of 16
+            // O^T += V^T P^T: reduction over the tile's 64 keys in 4 steps of 16;
+            // MFMA j covers d block j / 4, keys 16 (j % 4) .., its transposed V
+            // operand read 3 MFMAs ahead
+            __builtin_amdgcn_s_setprio(1);
+            {
+                constexpr int NJ = 4 * NDB, DIST = 3;
+                auto rdv = [&](int j) __attribute__((always_inline)) {
+                    return lds_read_tr_at<HD>(Vs, off, ((j >> 1) & 1) * 32 + (j & 1) * 16, j >> 2);
+                };
+                bf16x8 ring[DIST];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
+                for (int j = 0; j < DIST; ++j) ring[j] = rdv(j);
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        const bf16x8 a = lds_read_tr_at<HD>(Vs, off, b * 32 + h2 * 16, db);
-                        o[db] = mfma32(a, pb[b][h2], o[db]);
-                    }
+                for (int j = 0; j < NJ; ++j) {
+                    const bf16x8 a = ring[j % DIST];
+                    if (j + DIST < NJ) ring[j % DIST] = rdv(j + DIST);
+                    o[j >> 2] = mfma32(a, pb[(j >> 1) & 1][j & 1], o[j >> 2]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
         }
     };
     if constexpr (NW == 8) {
