@@ -10,9 +10,11 @@
 // tiles of K and V loaded straight from global memory into LDS (global_load_
 // lds) through a ring of slots.  Large launches take NW = 8 (256 rows, one
 // workgroup per compute unit, waves 0-3 load K and waves 4-7 load V): each
-// tile then serves twice the rows, and a 4-slot ring lets the workgroup work
-// on two tiles per barrier while the next two load (measured 8% and then
-// another 5% faster than NW = 4 with one barrier per tile, at S = 32768).
+// tile then serves twice the rows, and a 4-slot K ring (5 for V) lets the
+// workgroup work on two tiles per barrier while the next two load (measured
+// 8% and then another 5% faster than NW = 4 with one barrier per tile, at
+// S = 32768).  Wave w + 4 runs one phase behind wave w, which shares its
+// SIMD, so that one's softmax overlaps the other's products.
 // Smaller launches take NW = 4 (128 rows, two workgroups per compute unit,
 // double-buffered, one barrier per tile) so more compute units get work.  Per wave and tile, in the transposed form that keeps one query row
 // per lane pair:
@@ -93,7 +95,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(FwdParams p) {
     // K/V ring slots: 8 waves work on two tiles per barrier while the next
     // two load; 4 waves double-buffer single tiles
     constexpr int NBUF = NW == 8 ? 4 : 2;
-    __shared__ __attribute__((aligned(1024))) char smem[NBUF][2][TILE];
+    // one V slot more with 8 waves, for the deferred P V products below
+    constexpr int NVB = NW == 8 ? NBUF + 1 : NBUF;
+    __shared__ __attribute__((aligned(1024))) char ksm[NBUF][TILE];
+    __shared__ __attribute__((aligned(1024))) char vsm[NVB][TILE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values scalar
@@ -170,10 +175,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(FwdParams p) {
     auto issue = [&](int t) {
         const int64_t nb = (int64_t)t * BN;
         if constexpr (NW == 8) {
-            dkv.load(smem[t % NBUF][kv_sel], kvh + nb * kv_rs, kv_rs, p.nk - nb, wave & 3, lane);
+            dkv.load(kv_sel == 0 ? ksm[t % NBUF] : vsm[t % NVB], kvh + nb * kv_rs, kv_rs, p.nk - nb, wave & 3, lane);
         } else {
-            dkv.load(smem[t % NBUF][0], kh + nb * p.k_rs, p.k_rs, p.nk - nb, wave, lane);
-            dv2.load(smem[t % NBUF][1], vh + nb * p.v_rs, p.v_rs, p.nk - nb, wave, lane);
+            dkv.load(ksm[t % NBUF], kh + nb * p.k_rs, p.k_rs, p.nk - nb, wave, lane);
+            dv2.load(vsm[t % NVB], vh + nb * p.v_rs, p.v_rs, p.nk - nb, wave, lane);
         }
     };
     // registers loaded above settle first; then tiles 0 .. NBUF-2 go in flight
@@ -191,10 +196,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(FwdParams p) {
     const OperandOffsets<HD> off(lane);
     // this lane's query position relative to the key positions of tile 0
     const int64_t qrel_base = p.q_pos0 + myq - p.k_pos0;
-    auto tile = [&](int j, int buf) {
-        if (j < ntiles_w) {
-            const char* Ks = smem[buf][0];
-            const char* Vs = smem[buf][1];
+    // front part of tile j: S^T, the online-softmax update and the O
+    // rescale, leaving the tile's P^T operands in pb; false when the wave
+    // sees no key of the tile
+    auto front = [&](int j, bf16x8 (&pb)[2][2]) __attribute__((always_inline)) -> bool {
+        if (j >= ntiles_w) return false;
+        {
+            const char* Ks = ksm[j % NBUF];
             // S^T = K Q^T for two 32-key blocks (first step starts from zero):
             // MFMA j covers block j % 2 over d 16 (j / 2) .., its K operand
             // read 3 MFMAs ahead.  Both product phases run at a raised wave
@@ -224,7 +232,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(FwdParams p) {
             const bool need_mask = (kb + BN > p.nk) ||
                                    (p.causal && p.k_pos0 + kb + BN - 1 > p.q_pos0 + wq0);
             float alpha;
-            bf16x8 pb[2][2];
             __builtin_amdgcn_s_setprio(0);
             if (need_mask) {
                 const int64_t qr = p.causal ? qrel_base - kb : (int64_t)BN;
@@ -239,6 +246,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(FwdParams p) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) o[db] *= alpha;
             }
+        }
+        return true;
+    };
+    // O^T += V^T P^T for the tile in V slot vs
+    auto pv = [&](int vs, const bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
+        {
+            const char* Vs = vsm[vs];
             // O^T += V^T P^T: reduction over the tile's 64 keys in 4 steps of 16;
             // MFMA j covers d block j / 4, keys 16 (j % 4) .., its transposed V
             // operand read 3 MFMAs ahead
@@ -262,16 +276,41 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(FwdParams p) {
             __builtin_amdgcn_s_setprio(0);
         }
     };
+    auto tile = [&](int j, int vs) __attribute__((always_inline)) {
+        bf16x8 pb[2][2];
+        if (front(j, pb)) pv(vs, pb);
+    };
     if constexpr (NW == 8) {
+        // wave w + 4 shares a SIMD with wave w and runs one phase behind it:
+        // its P V product of each pair's second tile moves past the barrier,
+        // to the start of the next pair, so that while one wave of the SIMD
+        // is on its softmax the other is on its products (4% faster than
+        // the same code without the shift).  Every wave reads all of a V
+        // tile but loads only a quarter of one, so the ring has a fifth V
+        // slot: the tile of a deferred product is not reloaded before every
+        // wave has used it.  Each wave adds into O in the same order as
+        // without the shift.
+        const bool lag = kv_sel != 0;
+        bf16x8 pbd[2][2];
+        int pend = -1;   // tile whose P V product is deferred
+        int vs0 = 0;     // V slot of tile j (j mod NVB)
         for (int j = 0; j < ntiles; j += 2) {
-            // slots of tiles j - 2 and j - 1 were released by the last barrier
+            const int vs1 = vs0 + 1 == NVB ? 0 : vs0 + 1;
+            if (pend >= 0) pv(pend, pbd);
+            pend = -1;
+            // slots of tiles j - 2 and j - 1 (K) and j - 3 and j - 2 (V) are free
             if (j + 2 < ntiles) issue(j + 2);
             if (j + 3 < ntiles) issue(j + 3);
-            tile(j, j % NBUF);
-            if (j + 1 < ntiles) tile(j + 1, (j + 1) % NBUF);
+            tile(j, vs0);
+            if (j + 1 < ntiles && front(j + 1, pbd)) {
+                if (lag) pend = vs1;
+                else pv(vs1, pbd);
+            }
+            vs0 = vs1 + 1 == NVB ? 0 : vs1 + 1;
             wait_vm_loads();  // tiles j + 2 and j + 3
             __syncthreads();
         }
+        if (pend >= 0) pv(pend, pbd);
     } else {
         for (int j = 0; j < ntiles; ++j) {
             if (j + 1 < ntiles) issue(j + 1);
