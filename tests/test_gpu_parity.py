@@ -146,6 +146,25 @@ def test_run_to_run_deterministic():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_wide_launch_run_to_run_deterministic(D):
+    # 64 row tiles x 16 heads = 1024 forward / dQ workgroups: the 8-wave shape,
+    # whose waves 4-7 run a phase behind waves 0-3 through a 5-slot V ring
+    # (a slot reloaded while another wave still reads it shows up as bits
+    # that change from run to run)
+    from head_chunked_context_amd.inputs import attention_inputs
+    S, Hq, Hkv = 16384, 16, 4
+    d = attention_inputs(S, Hq, Hkv, D, 31, device=DEV)
+    runs = []
+    for r in range(3):
+        print(f"wide run-to-run S={S} Hq={Hq} D={D} run {r}", flush=True)
+        o, lse = gpu_fwd(d, Hq)
+        runs.append((o, lse) + tuple(gpu_bwd(d, o, lse, Hq)))
+    for b in runs[1:]:
+        for x, y, n in zip(runs[0], b, ("o", "lse", "dq", "dk", "dv")):
+            assert torch.equal(x, y), f"{n} changes from run to run"
+
+
 def test_q_zero_closed_form():
     # q = 0: P is uniform over the visible keys, LSE_i = ln(i+1), O_i = mean(v_0..v_i)
     S, Hq, Hkv, D = 4096, 2, 1, 128
