@@ -19,7 +19,9 @@
 // With --plant-dkdv-overread the dK/dV kernel's loads of K and V rows into
 // registers are replayed without their clamp (lanes past the last key of a
 // short last tile reading their own key row), which must be reported:
-// evidence that the check sees reads.
+// evidence that the check sees reads.  With --plant-dkdv-fast-run its runs of
+// steps whose Q / dO loads take the unchecked full-tile form lose their
+// limit at the last full tile of a head, which must be reported too.
 #include <hip/hip_runtime_api.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -34,6 +36,7 @@
 #include "plan.h"
 
 static bool g_plant = false;
+static bool g_plant_fast = false;
 static int64_t g_gl_min_s = hc::kGroupLoopMinS;  // the library's group-loop threshold
 static long g_fails = 0, g_checks = 0;
 // failure injection: the copy / kernel launch with this index (counted from
@@ -333,6 +336,61 @@ hipError_t launch_dkdv(const DkdvParams& p, int HD, hipStream_t) {
             qt0 = first >= p.nq ? nqt : first / BQ;
         }
         const int64_t nsteps = j0 < p.nk ? nqt - qt0 : 0;
+        // each wave's step schedule: a run of unmasked steps issues the loads
+        // of step n + 3 in the full-tile form, without a row check, so every
+        // such step needs step n + 3 to exist and the issue cursor's tile
+        // (head ih, step is; three steps ahead) to lie wholly inside nq
+        {
+            const int64_t total = nsteps * (he - hb);
+            const int64_t nfull = (p.nq - qt0 * BQ) / BQ;
+            const bool fast_rs = p.q_rs < ((int64_t)1 << 24) && p.do_rs < ((int64_t)1 << 24);
+            for (int kw = 0; kw < 4; ++kw) {
+                const int64_t wj0 = j0 + kw * 32, wkpos = p.k_pos0 + wj0;
+                const bool edge_k = wj0 + 32 > p.nk;
+                int64_t d_end = 0;
+                if (p.causal) {
+                    const int64_t t = (wkpos + 32 - 2 + BQ) / BQ - qt0;
+                    d_end = t < 0 ? 0 : (t > nsteps ? nsteps : t);
+                }
+                const int64_t u_end = nsteps - (((qt0 + nsteps) * BQ > p.nq) ? 1 : 0);
+                int64_t is = 0, n = 0;
+                int ih = hb;
+                auto cursor_next = [&]() {
+                    if (++is == nsteps) {
+                        is = 0;
+                        ++ih;
+                    }
+                };
+                for (int64_t i = 0; i < 3 && i < total; ++i) cursor_next();
+                for (int h = hb; h < he; ++h) {
+                    int64_t st = 0;
+                    while (st < nsteps) {
+                        int64_t nf = 0;
+                        if (!edge_k && st >= d_end && st < u_end && fast_rs && is < nfull) {
+                            nf = u_end - st;
+                            if (total - 3 - n < nf) nf = total - 3 - n;
+                            if (!g_plant_fast && nfull < nsteps && nfull - is < nf) nf = nfull - is;
+                        }
+                        if (nf <= 0) {
+                            if (n + 3 < total) cursor_next();
+                            ++st;
+                            ++n;
+                            continue;
+                        }
+                        for (const int64_t e = st + nf; st < e; ++st, ++n) {
+                            ++g_checks;
+                            if (n + 3 >= total || ih >= he)
+                                fail_msg("step %#llx issues full-tile loads past the last step (%llu)",
+                                         "dkdv fast run", (uintptr_t)n, (size_t)total);
+                            else if (p.nq - (qt0 + is) * BQ < BQ)
+                                fail_msg("full-tile loads of a partial tile at row %#llx (nq %llu)",
+                                         "dkdv fast run", (uintptr_t)((qt0 + is) * BQ), (size_t)p.nq);
+                            cursor_next();
+                        }
+                    }
+                }
+            }
+        }
         for (int h = hb; h < he; ++h)
             for (int64_t n = 0; n < nsteps; ++n) {
                 const int64_t i0 = (qt0 + n) * BQ;
@@ -786,6 +844,7 @@ int main(int argc, char** argv) {
     bool inject = false;
     for (int i = 1; i < argc; ++i) {
         if (strcmp(argv[i], "--plant-dkdv-overread") == 0) g_plant = true;
+        if (strcmp(argv[i], "--plant-dkdv-fast-run") == 0) g_plant_fast = true;
         if (strcmp(argv[i], "--inject") == 0) inject = true;
     }
     if (inject) {

@@ -5,7 +5,8 @@ host (tests/native/extent_check.cpp), built with the address and
 undefined-behaviour sanitizers, over ~1400 shapes around tile, workgroup and
 trunk edges with exactly sized user tensors and workspace regions.  A planted
 copy of the dK/dV kernel's K/V row loads without their clamp to the last key
-must be reported, and HIP
+must be reported, as must its runs of unchecked full-tile Q / dO loads
+replayed without their limit at a head's last full tile, and HIP
 failures injected into copies and kernel launches must come back as
 ATTN_EHIP without breaking the next call."""
 import os
@@ -51,6 +52,14 @@ def test_planted_over_read_is_reported(extent_exe):
     r = _run(extent_exe, "--plant-dkdv-overread")
     assert r.returncode == 1
     assert "dkdv V row" in r.stderr and "failures: 0" not in r.stdout
+
+
+def test_planted_fast_run_past_the_last_full_tile_is_reported(extent_exe):
+    # the dK/dV kernel's runs of unchecked full-tile loads, replayed without
+    # their limit at a head's last full tile, must show up as partial-tile loads
+    r = _run(extent_exe, "--plant-dkdv-fast-run")
+    assert r.returncode == 1
+    assert "dkdv fast run" in r.stderr and "failures: 0" not in r.stdout
 
 
 def test_injected_copy_and_launch_failures_surface_and_leave_no_state(extent_exe):
