@@ -21,7 +21,9 @@
 // short last tile reading their own key row), which must be reported:
 // evidence that the check sees reads.  With --plant-dkdv-fast-run its runs of
 // steps whose Q / dO loads take the unchecked full-tile form lose their
-// limit at the last full tile of a head, which must be reported too.
+// limit at the last full tile of a head, which must be reported too; with
+// --plant-fwd-v-ring4 the forward's V ring loses its fifth slot, which must be
+// reported as a slot loaded while a wave can still read it.
 #include <hip/hip_runtime_api.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -37,6 +39,7 @@
 
 static bool g_plant = false;
 static bool g_plant_fast = false;
+static bool g_plant_vring = false;
 static int64_t g_gl_min_s = hc::kGroupLoopMinS;  // the library's group-loop threshold
 static long g_fails = 0, g_checks = 0;
 // failure injection: the copy / kernel launch with this index (counted from
@@ -215,6 +218,35 @@ hipError_t launch_prep(const PrepParams& p, hipStream_t) {
 }
 
 // fwd_kernel<HD, NW> as launched by launch_fwd
+// The 8-wave forward's ring schedule over ntiles K / V tiles: between two
+// barriers (tile pair j, j + 1) waves 0-3 read K and V of tiles j and j + 1;
+// waves 4-7 read V of tile j - 1 (their deferred P V product), K of j and
+// j + 1 and V of j; K and V of tiles j + 2 and j + 3 load into their slots
+// meanwhile.  No slot may be loaded while a wave can still read another tile
+// from it.
+static void fwd_ring_check(int ntiles, int nvb) {
+    const int nkb = 4;
+    for (int j = 0; j < ntiles; j += 2) {
+        std::vector<int> rk, rv;
+        for (int t = j; t < j + 2 && t < ntiles; ++t) {
+            rk.push_back(t);
+            rv.push_back(t);
+        }
+        if (j >= 2) rv.push_back(j - 1);
+        for (int t = j + 2; t < j + 4 && t < ntiles; ++t) {
+            ++g_checks;
+            for (int r : rk)
+                if (r % nkb == t % nkb)
+                    fail_msg("K tile %llu loaded into the slot of tile %llu still being read",
+                             "fwd K ring", (uintptr_t)t, (size_t)r);
+            for (int r : rv)
+                if (r % nvb == t % nvb)
+                    fail_msg("V tile %llu loaded into the slot of tile %llu still being read",
+                             "fwd V ring", (uintptr_t)t, (size_t)r);
+        }
+    }
+}
+
 hipError_t launch_fwd(const FwdParams& p, int HD, hipStream_t) {
     if (inject_launch()) return hipErrorLaunchFailure;
     if (p.nq <= 0 || p.nh <= 0) return hipSuccess;
@@ -237,6 +269,15 @@ hipError_t launch_fwd(const FwdParams& p, int HD, hipStream_t) {
             kend = a < kend ? a : kend;
         }
         const int ntiles = kend > 0 ? (int)((kend + BN - 1) / BN) : 0;
+        if (wide) {
+            // the schedule depends on ntiles alone: check each count once
+            static std::vector<char> done;
+            if ((size_t)ntiles >= done.size()) done.resize((size_t)ntiles + 1, 0);
+            if (!done[ntiles]) {
+                done[ntiles] = 1;
+                fwd_ring_check(ntiles, g_plant_vring ? 4 : 5);
+            }
+        }
         for (int t = 0; t < ntiles; ++t) {
             const int64_t nb = (int64_t)t * BN;
             tile64(kh + nb * p.k_rs, p.k_rs, p.nk - nb, HD, "fwd K tile");
@@ -845,6 +886,7 @@ int main(int argc, char** argv) {
     for (int i = 1; i < argc; ++i) {
         if (strcmp(argv[i], "--plant-dkdv-overread") == 0) g_plant = true;
         if (strcmp(argv[i], "--plant-dkdv-fast-run") == 0) g_plant_fast = true;
+        if (strcmp(argv[i], "--plant-fwd-v-ring4") == 0) g_plant_vring = true;
         if (strcmp(argv[i], "--inject") == 0) inject = true;
     }
     if (inject) {
@@ -873,6 +915,9 @@ int main(int argc, char** argv) {
     struct Heads { int Hq, Hkv; };
     const Heads hs[] = {{1, 1}, {2, 1}, {4, 2}, {8, 2}, {8, 1}, {4, 4}, {6, 2}};
     long cases = 0;
+    // the 8-wave forward's ring schedule for every tile count up to 64 (the
+    // launches below are too small to take that shape)
+    for (int nt = 0; nt <= 64; ++nt) hc::fwd_ring_check(nt, g_plant_vring ? 4 : 5);
     for (int pass = 0; pass < 2; ++pass) {
     // pass 1: the group-loop dK/dV schedule at every length
     g_gl_min_s = pass == 0 ? hc::kGroupLoopMinS : 1;

@@ -6,7 +6,8 @@ undefined-behaviour sanitizers, over ~1400 shapes around tile, workgroup and
 trunk edges with exactly sized user tensors and workspace regions.  A planted
 copy of the dK/dV kernel's K/V row loads without their clamp to the last key
 must be reported, as must its runs of unchecked full-tile Q / dO loads
-replayed without their limit at a head's last full tile, and HIP
+replayed without their limit at a head's last full tile, and the forward's
+K / V ring schedule with one V slot too few, and HIP
 failures injected into copies and kernel launches must come back as
 ATTN_EHIP without breaking the next call."""
 import os
@@ -60,6 +61,14 @@ def test_planted_fast_run_past_the_last_full_tile_is_reported(extent_exe):
     r = _run(extent_exe, "--plant-dkdv-fast-run")
     assert r.returncode == 1
     assert "dkdv fast run" in r.stderr and "failures: 0" not in r.stdout
+
+
+def test_planted_four_slot_forward_v_ring_is_reported(extent_exe):
+    # with the forward's deferred P V products, a V ring of four slots lets
+    # a wave load a tile into a slot another wave still reads
+    r = _run(extent_exe, "--plant-fwd-v-ring4")
+    assert r.returncode == 1
+    assert "fwd V ring" in r.stderr and "failures: 0" not in r.stdout
 
 
 def test_injected_copy_and_launch_failures_surface_and_leave_no_state(extent_exe):
