@@ -165,6 +165,25 @@ def test_wide_launch_run_to_run_deterministic(D):
             assert torch.equal(x, y), f"{n} changes from run to run"
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_wide_and_narrow_launches_agree_non_causal(D):
+    # non-causal: every wave walks every tile, so the 8-wave shape's deferred
+    # P V products run on every pair.  head_chunk 16 launches 64 x 16 = 1024
+    # forward / dQ workgroups (8 waves), head_chunk 1 launches 64 (4 waves,
+    # checked against the oracle at small sizes in test_non_causal*): the two
+    # must give the same bits
+    from head_chunked_context_amd.inputs import attention_inputs
+    S, Hq, Hkv = 16384, 16, 4
+    d = attention_inputs(S, Hq, Hkv, D, 37, device=DEV)
+    out = {}
+    for hc in (Hq, 1):
+        print(f"non-causal wide/narrow S={S} Hq={Hq} D={D} hc={hc}", flush=True)
+        o, lse = gpu_fwd(d, hc, causal=False)
+        out[hc] = (o, lse) + tuple(gpu_bwd(d, o, lse, hc, causal=False))
+    for x, y, n in zip(out[Hq], out[1], ("o", "lse", "dq", "dk", "dv")):
+        assert torch.equal(x, y), f"{n} differs between the wide and narrow launches"
+
+
 def test_q_zero_closed_form():
     # q = 0: P is uniform over the visible keys, LSE_i = ln(i+1), O_i = mean(v_0..v_i)
     S, Hq, Hkv, D = 4096, 2, 1, 128
